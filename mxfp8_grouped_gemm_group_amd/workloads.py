@@ -1,0 +1,298 @@
+"""Seeded synthetic inputs for the fused MXFP8 grouped-matmul + finalize-routing op.
+
+This module only draws inputs.  It holds none of the operator's arithmetic, so
+both the GPU library's tests/benchmark and the CPU oracle can take their inputs
+from it.  The construction follows the test-tensor recipe of the page
+"基于 PyPTO 的 MoE 融合算子实践：grouped_matmul_finalize_routing 的 MXFP8 实现与精度验证"
+(§3.3 tensor construction: FP8 data cast from N(0,1), E8M0 scales, ceil(K/64)
+scale blocks of 2, ``row_index = arange(M) % batch``, bf16 shared input, FP32
+out; §4.3 ``make_group_list``: uniform groups whose remainder goes to the
+leading experts) and the shape table of its §4.1/§6.2.
+
+Random streams:
+  * small arrays (scale exponents, logits, routing, shared input, out init) come
+    from ``numpy.random.default_rng(seed)`` in a fixed draw order, so they are
+    identical on every machine;
+  * the large FP8 operands x1/x2 come from ``torch.randn`` with a
+    ``torch.Generator`` seeded from the same seed *on the target device* (so the
+    GPU can draw a 1 GB weight tensor in milliseconds).  The values therefore
+    depend on the device type; the oracle always receives host copies of the
+    very tensors the GPU path consumes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Dict, Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+FP8_DTYPES = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_KIND = {"e4m3fn": 0, "e5m2": 1}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One operator invocation's shapes and input distributions."""
+    name: str
+    batch: int
+    K: int
+    N: int
+    E: int
+    M: int
+    fp8: str = "e4m3fn"                 # "e4m3fn" | "e5m2"
+    transpose_x2: bool = False
+    group_list_type: int = 1             # 0 prefix sums, 1 counts
+    groups: Union[str, Tuple] = "uniform"  # "uniform" | ("zipf", s) | explicit counts
+    exp_range: Tuple[int, int] = (-3, 3)  # E8M0 exponents drawn uniformly in [lo, hi]
+    logit: str = "uniform"               # "uniform" | "softmax" | "none"
+    row_index: str = "mod"               # "mod" (arange % batch) | "perm"
+    shared_rows: Optional[int] = None    # None -> batch rows; 0 -> no shared input
+    shared_weight: float = 1.0
+    shared_offset: int = 0
+    out_init: str = "zeros"              # "zeros" | "normal"
+    exact: bool = False                  # integer-valued variant, exact in FP32
+    seed: int = 0
+    topk: int = 0                        # informational (M = batch * topk)
+
+    @property
+    def fp8_kind(self) -> int:
+        return FP8_KIND[self.fp8]
+
+    @property
+    def R(self) -> int:
+        return self.batch if self.shared_rows is None else self.shared_rows
+
+    def counts(self) -> np.ndarray:
+        """Tokens per expert (int64 [E]); deterministic in the seed."""
+        return _counts(self)
+
+    def flops(self) -> int:
+        """2*M_routed*K*N: one K x N contraction per routed token."""
+        return 2 * int(self.counts().sum()) * self.K * self.N
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes a single pass must move at least once (HBM roofline numerator).
+
+        x2 of non-empty experts, x1, both scale tensors, logit, row_index,
+        group_list, out read + write, shared input.
+        """
+        c = self.counts()
+        active = int((c > 0).sum())
+        M_r = int(c.sum())
+        K, N = self.K, self.N
+        kb32 = 2 * ((K + 63) // 64)
+        b = active * K * N + M_r * K + M_r * kb32 + N * kb32
+        b += (4 * M_r if self.logit != "none" else 0) + 8 * M_r + 8 * self.E
+        b += 8 * self.batch * N + 2 * self.R * N
+        return b
+
+
+# --------------------------------------------------------------------------
+# Named workloads.  c1..c5 are the five benchmark configurations (shape sets of
+# the page's §4.1/§6.2 plus larger routed-MoE shapes); the rest are parity
+# cases: the page's registered test configurations (batch 4 and 128, topk 8,
+# K 7168, N 4096, E 8), the ragged zero/odd/power-of-two counts pattern of the
+# companion LLaDA2.0 grouped-GEMM page's operator test, and small ragged cases
+# that span several tiles.
+# --------------------------------------------------------------------------
+WORKLOADS: Dict[str, Workload] = {}
+
+
+def _reg(w: Workload) -> Workload:
+    WORKLOADS[w.name] = w
+    return w
+
+
+C1 = _reg(Workload("c1", batch=64, topk=2, M=128, K=5120, N=4096, E=8, fp8="e4m3fn",
+                   groups="uniform", group_list_type=1, exp_range=(-3, 3), seed=1001))
+C2 = _reg(Workload("c2", batch=128, topk=2, M=256, K=6144, N=4096, E=16, fp8="e5m2",
+                   transpose_x2=True, groups="uniform", group_list_type=1, exp_range=(-4, 4),
+                   shared_weight=0.5, out_init="normal", seed=1002))
+C3 = _reg(Workload("c3", batch=256, topk=3, M=768, K=8192, N=4096, E=32, fp8="e4m3fn",
+                   groups="uniform", group_list_type=0, exp_range=(-3, 3), seed=1003))
+C4 = _reg(Workload("c4", batch=512, topk=6, M=3072, K=7168, N=4096, E=64, fp8="e4m3fn",
+                   groups=("zipf", 1.1), group_list_type=1, exp_range=(-6, 6),
+                   row_index="perm", shared_rows=256, shared_weight=0.75, shared_offset=128,
+                   seed=1004))
+C5 = _reg(Workload("c5", batch=2048, topk=8, M=16384, K=7168, N=4096, E=256, fp8="e5m2",
+                   transpose_x2=True, groups=("zipf", 1.2), group_list_type=1,
+                   exp_range=(-8, 8), logit="softmax", row_index="perm", seed=1005))
+
+P1_TC_A = _reg(Workload("p1_tc_a", batch=4, topk=8, M=32, K=7168, N=4096, E=8, seed=1011))
+P1_TC_B = _reg(Workload("p1_tc_b", batch=128, topk=8, M=1024, K=7168, N=4096, E=8, seed=1012))
+P2_RAGGED = _reg(Workload("p2_ragged", batch=16, M=63, K=7168, N=4096, E=8,
+                          groups=(0, 1, 2, 4, 8, 16, 32, 0), seed=1013))
+
+# Small cases the oracle finishes in well under a second; several n-tiles,
+# ragged tails in M, N and the number of K steps.
+SMALL_N = _reg(Workload("small_n", batch=37, M=300, K=1024, N=704, E=7, fp8="e4m3fn",
+                        groups=(0, 37, 1, 120, 0, 95, 47), group_list_type=1,
+                        exp_range=(-5, 5), row_index="perm", shared_rows=20,
+                        shared_weight=0.75, shared_offset=9, out_init="normal", seed=1021))
+SMALL_T = _reg(Workload("small_t", batch=64, M=200, K=640, N=576, E=5, fp8="e5m2",
+                        transpose_x2=True, groups=(33, 0, 64, 100, 3), group_list_type=0,
+                        exp_range=(-6, 6), shared_weight=0.5, out_init="normal", seed=1022))
+
+# Integer-valued variants: every partial sum is exactly representable in FP32,
+# so any summation order must reproduce the oracle bit for bit.
+for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T):
+    _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
+                 logit="exact" if _base.logit != "none" else "none"))
+
+
+# --------------------------------------------------------------------------
+# Drawing.
+# --------------------------------------------------------------------------
+def make_group_list(counts: np.ndarray, group_list_type: int) -> np.ndarray:
+    """counts -> group_list in the requested format (0: prefix sums, 1: counts)."""
+    counts = np.asarray(counts, np.int64)
+    return np.cumsum(counts) if group_list_type == 0 else counts.copy()
+
+
+def _counts(w: Workload) -> np.ndarray:
+    if isinstance(w.groups, tuple) and w.groups and w.groups[0] == "zipf":
+        return _zipf_counts(w.M, w.E, float(w.groups[1]), w.seed)
+    if isinstance(w.groups, tuple):
+        c = np.asarray(w.groups, np.int64)
+        assert c.shape == (w.E,) and int(c.sum()) <= w.M
+        return c
+    # Uniform; a remainder goes one each to the leading experts.
+    c = np.full(w.E, w.M // w.E, np.int64)
+    c[: w.M % w.E] += 1
+    return c
+
+
+def _zipf_counts(M: int, E: int, s: float, seed: int) -> np.ndarray:
+    """Skewed routing: a seeded permutation ranks the experts; the last E/16 of
+    it are forced empty; the others get floor(M * r^-s / H) tokens by rank r,
+    and the remainder goes one each to the lowest-id active experts."""
+    rng = np.random.default_rng(seed + 7)
+    perm = rng.permutation(E)
+    n_empty = E // 16
+    active = perm[: E - n_empty]
+    ranks = np.arange(1, active.size + 1, dtype=np.float64)
+    p = ranks ** (-s)
+    p /= p.sum()
+    c = np.zeros(E, np.int64)
+    c[active] = np.floor(M * p).astype(np.int64)
+    rem = M - int(c.sum())
+    for e in np.sort(active)[:rem]:
+        c[e] += 1
+    return c
+
+
+def _fp8_from_normal(shape, dtype, gen, device, exact: bool) -> torch.Tensor:
+    if exact:
+        v = torch.randint(-2, 3, shape, generator=gen, device=device, dtype=torch.int32)
+        return v.to(torch.float32).to(dtype)
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dtype)
+
+
+def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
+    """Draw one invocation's inputs.  Returns a dict keyed by argument name.
+
+    x1 / x2 are float8 tensors; scale / pertoken_scale are uint8 E8M0 codes;
+    shared_input is bfloat16; out is the FP32 initial value.
+    """
+    device = torch.device(device)
+    rng = np.random.default_rng(w.seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    dt = FP8_DTYPES[w.fp8]
+    M, K, N, E, B = w.M, w.K, w.N, w.E, w.batch
+    KB = (K + 63) // 64
+
+    x1 = _fp8_from_normal((M, K), dt, gen, device, w.exact)
+    x2_shape = (N, K) if w.transpose_x2 else (K, N)
+    x2 = torch.empty((E,) + x2_shape, dtype=dt, device=device)
+    for e in range(E):  # per expert, so large configs never hold an FP32 copy
+        x2[e] = _fp8_from_normal(x2_shape, dt, gen, device, w.exact)
+
+    lo, hi = (0, 1) if w.exact else w.exp_range
+    pts = (127 + rng.integers(lo, hi + 1, size=(M, KB, 2))).astype(np.uint8)
+    sc_shape = (N, KB, 2) if w.transpose_x2 else (KB, N, 2)
+    sc = (127 + rng.integers(lo, hi + 1, size=sc_shape)).astype(np.uint8)
+
+    counts = _counts(w)
+    group_list = make_group_list(counts, w.group_list_type)
+
+    if w.row_index == "mod":
+        row_index = np.arange(M, dtype=np.int64) % B
+    else:
+        reps = -(-M // B)
+        row_index = rng.permutation(np.tile(np.arange(B, dtype=np.int64), reps))[:M]
+
+    if w.logit == "none":
+        logit = None
+    elif w.logit == "exact":
+        logit = rng.choice(np.array([1.0, 0.5, 0.25], np.float32), size=M)
+    elif w.logit == "softmax":
+        # softmax over each output row's tokens (its top-k routing weights)
+        s = rng.standard_normal(M)
+        ex = np.exp(s - s.max())
+        den = np.bincount(row_index, weights=ex, minlength=B)
+        logit = (ex / den[row_index]).astype(np.float32)
+    else:
+        logit = rng.random(M, dtype=np.float32)
+
+    R = w.R
+    if R > 0:
+        if w.exact:
+            shared = torch.from_numpy(rng.integers(-4, 5, size=(R, N)).astype(np.float32))
+        else:
+            shared = torch.from_numpy(rng.standard_normal((R, N), dtype=np.float32))
+        shared = shared.to(torch.bfloat16).to(device)
+    else:
+        shared = None
+
+    if w.out_init == "normal":
+        if w.exact:
+            init = rng.integers(-4, 5, size=(B, N)).astype(np.float32)
+        else:
+            init = rng.standard_normal((B, N), dtype=np.float32)
+    else:
+        init = np.zeros((B, N), np.float32)
+
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return dict(
+        x1=x1, x2=x2, scale=t(sc), pertoken_scale=t(pts),
+        group_list=t(group_list), group_list_type=w.group_list_type,
+        logit=None if logit is None else t(logit), row_index=t(row_index),
+        shared_input=shared, shared_input_weight=float(w.shared_weight),
+        shared_input_offset=int(w.shared_offset) if R > 0 else 0,
+        out=t(init), transpose_x2=bool(w.transpose_x2), fp8_kind=w.fp8_kind,
+    )
+
+
+def as_numpy(inputs: dict) -> dict:
+    """Host numpy copies of an input dict in the oracle's raw-code form."""
+    def u8(x):
+        return x.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+    d = dict(inputs)
+    d["x1"] = u8(inputs["x1"])
+    d["x2"] = u8(inputs["x2"])
+    d["scale"] = u8(inputs["scale"])
+    d["pertoken_scale"] = u8(inputs["pertoken_scale"])
+    d["group_list"] = inputs["group_list"].cpu().numpy()
+    d["row_index"] = inputs["row_index"].cpu().numpy()
+    d["logit"] = None if inputs["logit"] is None else inputs["logit"].cpu().numpy()
+    sh = inputs["shared_input"]
+    d["shared_input"] = None if sh is None else sh.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    d["out_init"] = inputs["out"].cpu().numpy()
+    del d["out"]
+    return d
+
+
+def sample_rows(w: Workload, n: int, seed: int = 0) -> np.ndarray:
+    """A seeded sample of output rows plus the shared range's edge rows."""
+    rng = np.random.default_rng(10_000 + w.seed + seed)
+    rows = set(rng.choice(w.batch, size=min(n, w.batch), replace=False).tolist())
+    if w.R > 0:
+        for r in (w.shared_offset - 1, w.shared_offset, w.shared_offset + w.R - 1,
+                  w.shared_offset + w.R):
+            if 0 <= r < w.batch:
+                rows.add(r)
+    rows.update({0, w.batch - 1})
+    return np.array(sorted(rows), np.int64)

@@ -1,0 +1,324 @@
+/*
+ * CPU oracle for the fused MoE grouped-matmul + finalize-routing operator with
+ * MXFP8 inputs.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg call it; the GPU library never does, and the two
+ * share no code, header or table.
+ *
+ * Sources (the web pages this operator is defined on):
+ *   [P1] "基于 PyPTO 的 MoE 融合算子实践：grouped_matmul_finalize_routing 的
+ *        MXFP8 实现与精度验证" (czykbl.com/news/94077)
+ *   [P3] CANN API reference "aclnnGroupedMatmulFinalizeRoutingV3"
+ *        (hiascend.com, ops-transformer)
+ *
+ * What is computed, written out as its plain definition ([P1] §2.1, expanded
+ * form; [P3] "计算公式" formulas 1 and 2; [P1] §6.3 golden description):
+ *
+ *   out[row_index[t], n] += w_t * sum_k  dq1(t,k) * dq2(e(t),k,n)
+ *   out[off + r, n]      += shared_input_weight * shared_input[r, n]
+ *
+ * with dq = FP8 value * 2^(E8M0 byte - 127), one E8M0 scale per 32 consecutive
+ * K elements (the reading of the "[ceil(K/64), ..., 2]" scale layout: sub-block
+ * j of 64-block b covers k in [64b+32j, 64b+32j+32)), w_t = logit[t] (1 when
+ * logit is absent), and e(t) the expert whose group_list range holds t.
+ *
+ * Everything is evaluated in double precision.  FP8 x FP8 x 2^k products are
+ * exact in double, so the only difference from an exact result is the double
+ * summation error (about K * 2^-53 relative), which is negligible against the
+ * FP32 tolerance the GPU path is held to.
+ *
+ * Alongside out, the oracle returns mag = |out_init| + sum |w_t * term| +
+ * |shared term| per element: the sum of the magnitudes of every term that
+ * enters that element.  The GPU tolerance is expressed against it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Error codes returned by oracle_gmm_finalize_routing. */
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+#define ORACLE_BAD_GROUP_LIST (-2)
+#define ORACLE_BAD_ROW_INDEX (-3)
+#define ORACLE_BAD_SHARED_RANGE (-4)
+#define ORACLE_NO_MEMORY (-5)
+
+/* ---------------------------------------------------------------------------
+ * Bit-level decoders.  The pages name the formats (FP8 E4M3FN / E5M2 data,
+ * E8M0FNU scales, bf16 shared input: [P1] §2.1, §3.1) without restating them;
+ * these follow the standard definitions of those encodings.
+ * ------------------------------------------------------------------------- */
+
+/* FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+ * exponent 15 with mantissa 7 is NaN; exponent 0 is subnormal. */
+double oracle_decode_e4m3fn(uint8_t b)
+{
+    int s = (b >> 7) & 1;
+    int e = (b >> 3) & 15;
+    int m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* FP8 E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits; IEEE-style
+ * infinities and NaNs at exponent 31; exponent 0 is subnormal. */
+double oracle_decode_e5m2(uint8_t b)
+{
+    int s = (b >> 7) & 1;
+    int e = (b >> 2) & 31;
+    int m = b & 3;
+    double v;
+    if (e == 31)
+        v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)m / 4.0, -14);
+    else
+        v = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return s ? -v : v;
+}
+
+/* E8M0 (unsigned, exponent only, bias 127): 2^(b-127); 0xFF is NaN. */
+double oracle_decode_e8m0(uint8_t b)
+{
+    if (b == 255)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 mantissa bits. */
+double oracle_decode_bf16(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 7) & 255;
+    int m = h & 127;
+    double v;
+    if (e == 255)
+        v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)m / 128.0, -126);
+    else
+        v = ldexp(1.0 + (double)m / 128.0, e - 127);
+    return s ? -v : v;
+}
+
+/* ---------------------------------------------------------------------------
+ * Expert token ranges from group_list ([P1] §4.3, "group_list 的两种格式").
+ *   type 0 (prefix sums): expert i owns [group_list[i-1], group_list[i]),
+ *                         with group_list[-1] read as 0;
+ *   type 1 (counts):      expert i owns [sum(group_list[:i]),
+ *                                        sum(group_list[:i]) + group_list[i]).
+ * A negative count, a decreasing prefix or a range ending past M is rejected.
+ * Rows past the last range belong to no expert and contribute nothing.
+ * ------------------------------------------------------------------------- */
+int oracle_expert_ranges(const int64_t *group_list, int64_t E, int type,
+                         int64_t M, int64_t *start, int64_t *end)
+{
+    int64_t prev = 0;
+    for (int64_t i = 0; i < E; ++i) {
+        if (type == 0) {
+            start[i] = prev;
+            end[i] = group_list[i];
+        } else if (type == 1) {
+            start[i] = prev;
+            end[i] = prev + group_list[i];
+        } else {
+            return ORACLE_BAD_ARG;
+        }
+        if (end[i] < start[i] || end[i] > M)
+            return ORACLE_BAD_GROUP_LIST;
+        prev = end[i];
+    }
+    return ORACLE_OK;
+}
+
+/* Value of every FP8 code of the chosen kind, and of every E8M0 code, built
+ * once per call by the decoders above (a cache of them, nothing more). */
+static void decode_tables(int fp8_kind, double fp8v[256], double e8m0v[256])
+{
+    for (int c = 0; c < 256; ++c) {
+        fp8v[c] = fp8_kind == 0 ? oracle_decode_e4m3fn((uint8_t)c)
+                                : oracle_decode_e5m2((uint8_t)c);
+        e8m0v[c] = oracle_decode_e8m0((uint8_t)c);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * The operator.
+ *
+ * Layouts (row-major, contiguous) — [P1] §3.1 input table, [P3] Atlas 350
+ * parameter notes:
+ *   x1              [M, K]                    FP8 codes
+ *   x2              [E, K, N]  (transpose_x2 = 0) or [E, N, K] (= 1), FP8 codes
+ *   scale           [KB, N, 2] (transpose_x2 = 0) or [N, KB, 2] (= 1), E8M0,
+ *                   KB = ceil(K/64); with scale_per_expert a leading [E] axis
+ *   pertoken_scale  [M, KB, 2]                E8M0
+ *   group_list      [E] int64, read per group_list_type
+ *   logit           [M] float32, or NULL (weight 1)       ([P1] §5.1 has_logit)
+ *   row_index       [M] int64, each in [0, batch)          ([P1] §4.2)
+ *   shared_input    [R, N] bf16 bits, or NULL             ([P1] §5.1 has_shared_input)
+ *   out_init        [batch, N] float32, the initial value of out ([P1] §3.1)
+ *
+ * The scale of element k of row t of x1 is pertoken_scale[t, k/64, (k/32)%2];
+ * the scale of element (k, n) of expert e's weight is scale[k/64, n, (k/32)%2]
+ * (or scale[n, k/64, (k/32)%2] when transposed).  The pair axis splits each
+ * 64-block of K into its two 32-element halves in K order ([P1] §2.1 says one
+ * scale per block, §4.2 says each 64-block holds 2 scales, §6.3 says the golden
+ * expands each scale over 32 K elements; this is the reading all three allow).
+ *
+ * Only the output rows listed in rows[0..n_rows) are computed (all rows when
+ * rows is NULL, in which case n_rows must equal batch).  For each listed row b:
+ *   res[b] = out_init[b] + sum over tokens t with row_index[t] == b, t in some
+ *            expert's range, in ascending t, of w_t * (matmul row t)
+ *            + shared term if off <= b < off + R.
+ * Results go to res_out[i*N + n] and mag_out[i*N + n] (double).
+ * ------------------------------------------------------------------------- */
+int oracle_gmm_finalize_routing(
+    const uint8_t *x1, const uint8_t *x2, const uint8_t *scale,
+    int scale_per_expert, const uint8_t *pertoken_scale,
+    const int64_t *group_list, int group_list_type, const float *logit,
+    const int64_t *row_index, const uint16_t *shared_input,
+    double shared_input_weight, int64_t shared_input_offset,
+    int64_t shared_rows, const float *out_init, int transpose_x2,
+    int fp8_kind, int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+    const int64_t *rows, int64_t n_rows, double *res_out, double *mag_out)
+{
+    if (M < 0 || K <= 0 || N < 0 || E <= 0 || batch < 0 || n_rows < 0)
+        return ORACLE_BAD_ARG;
+    if (fp8_kind != 0 && fp8_kind != 1)
+        return ORACLE_BAD_ARG;
+    if (rows == NULL && n_rows != batch)
+        return ORACLE_BAD_ARG;
+    if (shared_input != NULL &&
+        (shared_input_offset < 0 || shared_rows < 0 ||
+         shared_input_offset + shared_rows > batch))
+        return ORACLE_BAD_SHARED_RANGE;
+
+    const int64_t KB = (K + 63) / 64;
+    double fp8v[256], e8m0v[256];
+    decode_tables(fp8_kind, fp8v, e8m0v);
+
+    int64_t *start = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t *end = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t *expert_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double *absacc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    int rc = ORACLE_OK;
+    if (!start || !end || !expert_of || !acc || !absacc) {
+        rc = ORACLE_NO_MEMORY;
+        goto done;
+    }
+
+    rc = oracle_expert_ranges(group_list, E, group_list_type, M, start, end);
+    if (rc != ORACLE_OK)
+        goto done;
+
+    /* Token -> expert; tokens in no range keep -1 and are never read. */
+    for (int64_t t = 0; t < M; ++t)
+        expert_of[t] = -1;
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t t = start[e]; t < end[e]; ++t)
+            expert_of[t] = e;
+
+    /* row_index must lie in [0, batch) for every routed token ([P1] §4.2). */
+    for (int64_t t = 0; t < M; ++t)
+        if (expert_of[t] >= 0 && (row_index[t] < 0 || row_index[t] >= batch)) {
+            rc = ORACLE_BAD_ROW_INDEX;
+            goto done;
+        }
+
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t b = rows ? rows[i] : i;
+        if (b < 0 || b >= batch) {
+            rc = ORACLE_BAD_ARG;
+            goto done;
+        }
+        double *res = res_out + i * N;
+        double *mag = mag_out + i * N;
+
+        /* out starts from its initial value ([P1] §3.1: out is the initial value). */
+        for (int64_t n = 0; n < N; ++n) {
+            res[n] = (double)out_init[b * N + n];
+            mag[n] = fabs(res[n]);
+        }
+
+        /* Routed experts: every token scattered to row b, ascending t
+         * ([P1] §2.2 stages 1-3; [P3] formula 2). */
+        for (int64_t t = 0; t < M; ++t) {
+            const int64_t e = expert_of[t];
+            if (e < 0 || row_index[t] != b)
+                continue;
+            const double w = logit ? (double)logit[t] : 1.0;
+
+            for (int64_t n = 0; n < N; ++n) {
+                acc[n] = 0.0;
+                absacc[n] = 0.0;
+            }
+
+            /* Stage 1: the scaled matmul row, summed over k in ascending order
+             * for each n.  The loop nest is ordered for the memory layout only;
+             * each element's sum is the same sequence either way. */
+            const uint8_t *ps_row = pertoken_scale + t * KB * 2;
+            const uint8_t *sc = scale + (scale_per_expert ? e * KB * N * 2 : 0);
+            if (!transpose_x2) {
+                const uint8_t *w2 = x2 + e * K * N; /* w2[k*N + n] */
+                for (int64_t k = 0; k < K; ++k) {
+                    const double a = fp8v[x1[t * K + k]] *
+                                     e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double bw = fp8v[w2[k * N + n]] *
+                                          e8m0v[sc[((k / 64) * N + n) * 2 + (k / 32) % 2]];
+                        const double term = a * bw;
+                        acc[n] += term;
+                        absacc[n] += fabs(term);
+                    }
+                }
+            } else {
+                const uint8_t *w2 = x2 + e * N * K; /* w2[n*K + k] */
+                for (int64_t n = 0; n < N; ++n) {
+                    for (int64_t k = 0; k < K; ++k) {
+                        const double a = fp8v[x1[t * K + k]] *
+                                         e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
+                        const double bw = fp8v[w2[n * K + k]] *
+                                          e8m0v[sc[(n * KB + k / 64) * 2 + (k / 32) % 2]];
+                        const double term = a * bw;
+                        acc[n] += term;
+                        absacc[n] += fabs(term);
+                    }
+                }
+            }
+
+            /* Stages 2-3: weight by logit, add into row b. */
+            for (int64_t n = 0; n < N; ++n) {
+                res[n] += w * acc[n];
+                mag[n] += fabs(w) * absacc[n];
+            }
+        }
+
+        /* Stage 4: shared expert into rows [off, off + R) ([P1] §2.1, §5.3;
+         * [P3] formula 3). */
+        if (shared_input && b >= shared_input_offset &&
+            b < shared_input_offset + shared_rows) {
+            const int64_t r = b - shared_input_offset;
+            for (int64_t n = 0; n < N; ++n) {
+                const double v = shared_input_weight *
+                                 oracle_decode_bf16(shared_input[r * N + n]);
+                res[n] += v;
+                mag[n] += fabs(v);
+            }
+        }
+    }
+
+done:
+    free(start);
+    free(end);
+    free(expert_of);
+    free(acc);
+    free(absacc);
+    return rc;
+}

@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* decoders: every code against torch's independent float8/bfloat16 casts, plus
+  the closed-form extremes of each format;
+* contraction + routing: an independent float64 formulation built from library
+  primitives (torch decoding, ``np.repeat`` of the scales over 32 K elements as
+  the golden description in §6.3 of the grouped_matmul_finalize_routing MXFP8
+  page does, ``numpy.matmul``, ``np.add.at``) on tiny brute-force inputs;
+* a textbook special case (one expert, unit scales, unit logits, identity
+  routing) that is a plain matrix product;
+* exact integer arithmetic (int64 einsum) on the integer-valued variant;
+* analytic one-hot cases that pin the scale-layout reading;
+* invariants: logit = 0, empty experts, group_list formats, transposition,
+  shared input absent, scale-exponent linearity.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.tiny_inputs import tiny_case, decode_np, numpy_reference
+
+
+# ----------------------------------------------------------------------------
+# Decoders
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,tdt", [("e4m3fn", torch.float8_e4m3fn),
+                                      ("e5m2", torch.float8_e5m2),
+                                      ("e8m0", torch.float8_e8m0fnu)])
+def test_decode_all_codes_match_torch(kind, tdt):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(tdt).to(torch.float64).numpy()
+    got = np.array([oracle.decode(kind, int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_decode_bf16_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.decode("bf16", int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_decode_closed_forms():
+    d = oracle.decode
+    # E4M3FN: max finite 448 = 1.75 * 2^8 at 0x7E, NaN at 0x7F/0xFF, no inf,
+    # smallest subnormal 2^-9, smallest normal 2^-6, one = 0x38.
+    assert d("e4m3fn", 0x7E) == 448.0 and d("e4m3fn", 0xFE) == -448.0
+    assert math.isnan(d("e4m3fn", 0x7F)) and math.isnan(d("e4m3fn", 0xFF))
+    assert d("e4m3fn", 0x01) == 2.0 ** -9 and d("e4m3fn", 0x08) == 2.0 ** -6
+    assert d("e4m3fn", 0x38) == 1.0 and d("e4m3fn", 0x80) == 0.0
+    # E5M2: max finite 57344 = 1.75 * 2^15 at 0x7B, +inf 0x7C, NaN 0x7D..0x7F,
+    # smallest subnormal 2^-16, one = 0x3C.
+    assert d("e5m2", 0x7B) == 57344.0 and d("e5m2", 0x7C) == math.inf
+    assert d("e5m2", 0xFC) == -math.inf
+    assert all(math.isnan(d("e5m2", c)) for c in (0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF))
+    assert d("e5m2", 0x01) == 2.0 ** -16 and d("e5m2", 0x3C) == 1.0
+    # E8M0: 2^(b-127), 0xFF NaN.
+    assert d("e8m0", 127) == 1.0 and d("e8m0", 0) == 2.0 ** -127
+    assert d("e8m0", 254) == 2.0 ** 127 and math.isnan(d("e8m0", 255))
+    # bf16: one = 0x3F80, -2 = 0xC000.
+    assert d("bf16", 0x3F80) == 1.0 and d("bf16", 0xC000) == -2.0
+
+
+# ----------------------------------------------------------------------------
+# group_list
+# ----------------------------------------------------------------------------
+def test_expert_ranges_formats():
+    counts = np.array([3, 0, 2, 5, 0], np.int64)
+    s1, e1 = oracle.expert_ranges(counts, 1, 10)
+    s0, e0 = oracle.expert_ranges(np.cumsum(counts), 0, 10)
+    assert s1.tolist() == [0, 3, 3, 5, 10] and e1.tolist() == [3, 3, 5, 10, 10]
+    assert np.array_equal(s0, s1) and np.array_equal(e0, e1)
+
+
+@pytest.mark.parametrize("g,t,M", [([2, -1, 3], 1, 10), ([2, 1, 3], 0, 10),
+                                   ([4, 4, 4], 1, 11), ([3, 12], 0, 11)])
+def test_expert_ranges_reject_invalid(g, t, M):
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.expert_ranges(np.array(g, np.int64), t, M)
+    assert ei.value.code == -2
+
+
+# ----------------------------------------------------------------------------
+# Contraction and routing
+# ----------------------------------------------------------------------------
+def _run(c, **over):
+    a = dict(c)
+    a.update(over)
+    return oracle.gmm_finalize_routing(
+        a["x1"], a["x2"], a["scale"], a["pertoken_scale"], a["group_list"],
+        a["group_list_type"], a["logit"], a["row_index"], a["shared_input"],
+        a["shared_input_weight"], a["shared_input_offset"], a["out_init"],
+        a["transpose_x2"], a["fp8_kind"], rows=a.get("rows"))
+
+
+CASES = [dict(seed=s, E=E, M=M, K=K, N=N, transpose=tr, kind=kd, gtype=gt)
+         for s, (E, M, K, N, tr, kd, gt) in enumerate([
+             (1, 3, 32, 2, False, 0, 1), (2, 5, 64, 3, True, 1, 0),
+             (3, 8, 96, 5, False, 1, 1), (3, 7, 128, 4, True, 0, 0),
+             (2, 6, 160, 5, False, 0, 0), (3, 8, 128, 5, True, 1, 1)])]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c['seed']}")
+def test_tiny_matches_independent_numpy(case):
+    c = tiny_case(**case)
+    got, mag = _run(c)
+    ref = numpy_reference(c)
+    assert np.all(np.abs(got - ref) <= 1e-13 * mag + 1e-300)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_textbook_plain_matmul(transpose):
+    """One expert, unit scales, unit logits, identity routing, zero init, no
+    shared input: out is exactly the decoded FP8 product x1 @ x2[0]."""
+    c = tiny_case(seed=42, E=1, M=6, K=128, N=5, transpose=transpose, kind=0, gtype=1,
+                  groups=[6], batch=6, routing="identity", unit_scales=True,
+                  logit="ones", shared=False)
+    got, _ = _run(c, out_init=np.zeros_like(c["out_init"]))
+    a = decode_np(c["x1"], 0)
+    b = decode_np(c["x2"][0], 0)
+    if transpose:
+        b = b.T
+    # Products span < 40 bits and 128 terms add < 8 more: exact in float64 in
+    # any summation order, so the comparison is exact.
+    assert np.array_equal(got, a @ b)
+
+
+def test_exact_integer_arithmetic():
+    """Integer FP8 values in [-2, 2], exponents {0, 1}, logits {1, 1/2, 1/4}:
+    compare against int64 arithmetic."""
+    for seed in range(3):
+        c = tiny_case(seed=100 + seed, E=3, M=8, K=256, N=5, transpose=bool(seed % 2),
+                      kind=seed % 2, gtype=seed % 2, exact=True)
+        got, _ = _run(c)
+        kind = c["fp8_kind"]
+        a = decode_np(c["x1"], kind).astype(np.int64)
+        b = decode_np(c["x2"], kind).astype(np.int64)
+        if c["transpose_x2"]:
+            b = np.transpose(b, (0, 2, 1))
+        M, K = a.shape
+        pe = (c["pertoken_scale"].astype(np.int64) - 127).reshape(M, -1)[:, np.arange(K) // 32]
+        if c["transpose_x2"]:
+            se = (c["scale"].astype(np.int64) - 127).reshape(b.shape[2], -1)[:, np.arange(K) // 32].T
+        else:
+            s3 = c["scale"].astype(np.int64) - 127  # [KB, N, 2]
+            se = np.moveaxis(s3, 2, 1).reshape(-1, s3.shape[1])[np.arange(K) // 32]
+        a_s = a << pe                     # exact integers
+        b_s = b << se[None]
+        g = c["group_list"]
+        counts = np.diff(np.concatenate([[0], g])) if c["group_list_type"] == 0 else g
+        end = np.cumsum(counts)
+        start = end - counts
+        out = c["out_init"].astype(np.float64).copy()
+        for e in range(len(start)):
+            for t in range(start[e], end[e]):
+                row = np.einsum("k,kn->n", a_s[t], b_s[e])  # int64
+                out[c["row_index"][t]] += float(c["logit"][t]) * row.astype(np.float64)
+        sh = decode_np(c["shared_input"], "bf16")
+        off = c["shared_input_offset"]
+        out[off:off + sh.shape[0]] += c["shared_input_weight"] * sh
+        assert np.array_equal(got, out)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_one_hot_pins_scale_layout(transpose):
+    """A single non-zero in x1 at (t, k) and in x2 at (e, k, n): the only
+    changed output element is (row_index[t], n) and its change is
+    logit[t] * x1 * x2 * 2^(pertoken_scale[t, k//64, (k//32)%2] - 127)
+    * 2^(scale[k//64, n, (k//32)%2] - 127) (scale[n, k//64, ...] if transposed)."""
+    rng = np.random.default_rng(7)
+    for _ in range(12):
+        c = tiny_case(seed=int(rng.integers(1 << 30)), E=2, M=5, K=192, N=4,
+                      transpose=transpose, kind=0, gtype=1, groups=[2, 3], batch=3)
+        t = int(rng.integers(5))
+        k = int(rng.integers(192))
+        n = int(rng.integers(4))
+        e = 0 if t < 2 else 1
+        x1 = np.zeros_like(c["x1"])
+        x2 = np.zeros_like(c["x2"])
+        x1[t, k] = 0x38            # 1.0
+        if transpose:
+            x2[e, n, k] = 0x40     # 2.0
+        else:
+            x2[e, k, n] = 0x40
+        got, _ = _run(c, x1=x1, x2=x2, shared_input=None)
+        pe = int(c["pertoken_scale"][t, k // 64, (k // 32) % 2]) - 127
+        se = int((c["scale"][n, k // 64, (k // 32) % 2] if transpose
+                  else c["scale"][k // 64, n, (k // 32) % 2])) - 127
+        want = c["out_init"].astype(np.float64).copy()
+        want[c["row_index"][t], n] += float(c["logit"][t]) * 2.0 * 2.0 ** (pe + se)
+        assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------
+# Invariants
+# ----------------------------------------------------------------------------
+def test_logit_zero_leaves_init_plus_shared():
+    c = tiny_case(seed=5, E=3, M=8, K=128, N=5, transpose=False, kind=0, gtype=1)
+    got, _ = _run(c, logit=np.zeros_like(c["logit"]))
+    want = c["out_init"].astype(np.float64).copy()
+    sh = decode_np(c["shared_input"], "bf16")
+    off = c["shared_input_offset"]
+    want[off:off + sh.shape[0]] += c["shared_input_weight"] * sh
+    assert np.array_equal(got, want)
+
+
+def test_empty_expert_contributes_nothing():
+    c = tiny_case(seed=6, E=3, M=6, K=128, N=4, transpose=True, kind=1, gtype=1,
+                  groups=[2, 0, 4])
+    base, _ = _run(c)
+    x2 = c["x2"].copy()
+    x2[1] = np.random.default_rng(0).integers(0, 0x7B, size=x2[1].shape, dtype=np.uint8)
+    got, _ = _run(c, x2=x2)
+    assert np.array_equal(base, got)
+
+
+def test_tokens_past_last_group_contribute_nothing():
+    c = tiny_case(seed=8, E=2, M=8, K=64, N=3, transpose=False, kind=0, gtype=1,
+                  groups=[2, 3])
+    base, _ = _run(c)
+    x1 = c["x1"].copy()
+    x1[5:] = 0x38
+    ri = c["row_index"].copy()
+    ri[5:] = 10 ** 6   # never read
+    got, _ = _run(c, x1=x1, row_index=ri)
+    assert np.array_equal(base, got)
+
+
+def test_group_list_type_equivalence():
+    c = tiny_case(seed=9, E=3, M=8, K=96, N=4, transpose=False, kind=0, gtype=1,
+                  groups=[3, 0, 4])
+    a, _ = _run(c)
+    b, _ = _run(c, group_list=np.cumsum(c["group_list"]), group_list_type=0)
+    assert np.array_equal(a, b)
+
+
+def test_transpose_equivalence():
+    c = tiny_case(seed=10, E=2, M=6, K=160, N=5, transpose=False, kind=1, gtype=1)
+    a, _ = _run(c)
+    x2t = np.ascontiguousarray(np.transpose(c["x2"], (0, 2, 1)))
+    st = np.ascontiguousarray(np.transpose(c["scale"], (1, 0, 2)))   # [KB,N,2] -> [N,KB,2]
+    b, _ = _run(c, x2=x2t, scale=st, transpose_x2=True)
+    assert np.array_equal(a, b)
+
+
+def test_shared_absent_equals_zero_weight():
+    c = tiny_case(seed=11, E=2, M=6, K=64, N=3, transpose=False, kind=0, gtype=1)
+    a, _ = _run(c, shared_input=None)
+    b, _ = _run(c, shared_input_weight=0.0)
+    assert np.array_equal(a, b)
+
+
+def test_logit_absent_equals_unit_logit():
+    c = tiny_case(seed=12, E=2, M=6, K=64, N=3, transpose=True, kind=0, gtype=0)
+    a, _ = _run(c, logit=None)
+    b, _ = _run(c, logit=np.ones_like(c["logit"]))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("which", ["pertoken", "weight"])
+def test_scale_exponent_linearity(which):
+    """Raising one E8M0 exponent by 1 adds exactly that 32-element sub-block's
+    contribution once more; the sub-block's contribution is measured by
+    zeroing x1 outside it (integer data, so everything is exact)."""
+    rng = np.random.default_rng(13)
+    for trial in range(8):
+        tr = bool(trial % 2)
+        c = tiny_case(seed=200 + trial, E=2, M=6, K=256, N=4, transpose=tr, kind=0,
+                      gtype=1, groups=[3, 3], batch=6, routing="identity", exact=True,
+                      shared=False)
+        base, _ = _run(c)
+        kb = int(rng.integers(8))            # 32-element sub-block
+        b, j = kb // 2, kb % 2
+        mask = np.zeros_like(c["x1"])
+        mask[:, 32 * kb:32 * kb + 32] = 1
+        x1_sub = np.where(mask == 1, c["x1"], 0).astype(np.uint8)
+        init0 = np.zeros_like(c["out_init"])
+        if which == "pertoken":
+            t = int(rng.integers(6))
+            pts = c["pertoken_scale"].copy()
+            pts[t, b, j] += 1
+            bumped, _ = _run(c, pertoken_scale=pts)
+            contrib, _ = _run(c, x1=x1_sub, out_init=init0)
+            want = base.copy()
+            r = c["row_index"][t]
+            want[r] += contrib[r]
+        else:
+            n = int(rng.integers(4))
+            sc = c["scale"].copy()
+            if tr:
+                sc[n, b, j] += 1
+            else:
+                sc[b, n, j] += 1
+            bumped, _ = _run(c, scale=sc)
+            contrib, _ = _run(c, x1=x1_sub, out_init=init0)
+            want = base.copy()
+            want[:, n] += contrib[:, n]
+        assert np.array_equal(bumped, want)
+
+
+def test_row_selection_matches_full():
+    c = tiny_case(seed=14, E=3, M=8, K=64, N=4, transpose=True, kind=1, gtype=0, batch=5)
+    full, fmag = _run(c)
+    rows = np.array([4, 1, 3], np.int64)
+    part, pmag = _run(c, rows=rows)
+    assert np.array_equal(part, full[rows]) and np.array_equal(pmag, fmag[rows])
+
+
+def test_duplicate_rows_accumulate():
+    c = tiny_case(seed=15, E=1, M=4, K=64, N=3, transpose=False, kind=0, gtype=1,
+                  groups=[4], batch=2, shared=False)
+    ri = np.array([1, 1, 1, 1], np.int64)
+    got, _ = _run(c, row_index=ri)
+    # row 1 collects all four tokens; row 0 keeps its initial value
+    parts = []
+    for t in range(4):
+        lg = np.zeros_like(c["logit"])
+        lg[t] = c["logit"][t]
+        p, _ = _run(c, row_index=ri, logit=lg, out_init=np.zeros_like(c["out_init"]))
+        parts.append(p[1])
+    assert np.array_equal(got[0], c["out_init"][0].astype(np.float64))
+    assert np.allclose(got[1], c["out_init"][1] + sum(parts), rtol=1e-15, atol=0)
+
+
+def test_errors():
+    c = tiny_case(seed=16, E=2, M=4, K=64, N=3, transpose=False, kind=0, gtype=1,
+                  groups=[2, 2], batch=2)
+    with pytest.raises(oracle.OracleError) as ei:
+        _run(c, row_index=np.array([0, 1, 2, 0], np.int64))
+    assert ei.value.code == -3
+    with pytest.raises(oracle.OracleError) as ei:
+        _run(c, shared_input_offset=1)
+    assert ei.value.code == -4
+    with pytest.raises(oracle.OracleError) as ei:
+        _run(c, group_list=np.array([3, 2], np.int64))
+    assert ei.value.code == -2
+
+
+def test_tolerance_helper():
+    ok, r = oracle.within_tolerance([1.0, 2.0], np.array([1.0, 2.0 + 1e-4]), np.array([1.0, 1.0]))
+    assert not ok and r > 1
+    ok, r = oracle.within_tolerance([1.0], np.array([1.0 + 1e-5]), np.array([1.0]))
+    assert ok and r < 1
+
+
+# ----------------------------------------------------------------------------
+# Hand-derived worked example (tests/golden/worked_example_1.json)
+# ----------------------------------------------------------------------------
+def _load_worked_example(kind, transpose):
+    import json
+    import os
+    d = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "worked_example_1.json")))
+    f8 = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}[kind]
+    enc = lambda v: torch.tensor(v, dtype=torch.float32).to(f8).view(torch.uint8).numpy()
+    x2 = enc(d["x2_values_EKN"])
+    sc = (127 + np.array(d["scale_exponents_KB_N_2"])).astype(np.uint8)
+    if transpose:
+        x2 = np.ascontiguousarray(np.transpose(x2, (0, 2, 1)))
+        sc = np.ascontiguousarray(np.transpose(sc, (1, 0, 2)))
+    sh = torch.tensor(d["shared_input"], dtype=torch.float32).to(torch.bfloat16)
+    c = dict(x1=enc(d["x1_values"]), x2=x2, scale=sc,
+             pertoken_scale=(127 + np.array(d["pertoken_scale_exponents_M_KB_2"])).astype(np.uint8),
+             group_list=np.array(d["group_list"], np.int64), group_list_type=d["group_list_type"],
+             logit=np.array(d["logit"], np.float32), row_index=np.array(d["row_index"], np.int64),
+             shared_input=sh.view(torch.int16).numpy().view(np.uint16),
+             shared_input_weight=d["shared_input_weight"],
+             shared_input_offset=d["shared_input_offset"],
+             out_init=np.array(d["out_init"], np.float32), transpose_x2=transpose, fp8_kind=kind)
+    return c, np.array(d["expected_out"], np.float64)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_worked_example(kind, transpose):
+    c, want = _load_worked_example(kind, transpose)
+    got, _ = _run(c)
+    assert np.array_equal(got, want)

@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MXFP8 grouped-matmul + finalize-routing operator.
+
+One step = one full call of the operator (grouped block-scaled FP8 matmul,
+logit weighting, scatter-add into out, shared-expert axpy) over the headline
+workload (M=768 routed tokens, K=8192, N=4096, E=32 experts of 24 tokens,
+batch 256), inputs resident in HBM.  Prints ONE JSON line.
+
+value      = effective TFLOP/s = 2*M*K*N / (time per step)
+roofline   = the fused kernel against the HBM roofline (its algorithmic bytes
+             per launch / its mean launch time, timed with events on the launch
+             stream), the binding roof for every configuration here
+cpu_baseline = the CPU oracle on a bounded sample of output rows of the same
+             workload (single-threaded C, double precision)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MXFP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the oracle on a growing seeded sample of output rows."""
+    import numpy as np
+    import oracle
+    from mxfp8_grouped_gemm_group_amd.workloads import as_numpy
+
+    h = as_numpy(inp)
+    ri = h["row_index"]
+    total_tokens = int(w.counts().sum())
+    routed = ri[:total_tokens]
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(w.batch)
+    n, spent, rows_done, tok_done = 1, 0.0, 0, 0
+    while True:
+        rows = order[rows_done:rows_done + n]
+        if rows.size == 0:
+            break
+        t0 = time.perf_counter()
+        oracle.gmm_finalize_routing(
+            h["x1"], h["x2"], h["scale"], h["pertoken_scale"], h["group_list"],
+            h["group_list_type"], h["logit"], h["row_index"], h["shared_input"],
+            h["shared_input_weight"], h["shared_input_offset"], h["out_init"],
+            h["transpose_x2"], h["fp8_kind"], rows=rows)
+        spent += time.perf_counter() - t0
+        rows_done += rows.size
+        tok_done += int(np.isin(routed, rows).sum())
+        if spent >= budget_s:
+            break
+        n = max(1, int(rows_done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
+    flops = 2.0 * tok_done * w.K * w.N
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} of {w.batch} output rows ({tok_done} routed tokens, all "
+                      f"{w.N} columns) of workload {w.name}; {spent:.1f} s single-threaded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this operator is "
+              "built and measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mxfp8_grouped_gemm_group_amd as gfr
+    from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_inputs
+
+    gfr.load_library()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, dev)
+    # Rotate weight copies so the 256 MB last-level cache never holds the
+    # next step's weights (cold HBM every step).
+    x2_bytes = inp["x2"].numel()
+    n_sets = max(1, -(-(1 << 30) // x2_bytes)) if x2_bytes < (1 << 29) else 1
+    x2_sets = [inp["x2"]] + [inp["x2"].clone() for _ in range(n_sets - 1)]
+    out = inp["out"].clone()
+    ws = None
+    if args.deterministic:
+        ws = torch.empty(max(1, gfr.workspace_size(w.M, w.K, w.N, w.E, w.batch, True)),
+                         dtype=torch.uint8, device=dev)
+
+    def step(i):
+        gfr.gmm_finalize_routing(
+            inp["x1"], x2_sets[i % n_sets], inp["scale"], inp["pertoken_scale"],
+            inp["group_list"], inp["group_list_type"], inp["logit"], inp["row_index"],
+            inp["shared_input"], inp["shared_input_weight"], inp["shared_input_offset"], out,
+            inp["transpose_x2"], deterministic=args.deterministic, workspace=ws,
+            split_k=args.split_k)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+
+    flops = w.flops()
+    alg_bytes = w.algorithmic_bytes()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tfile) and not args.deterministic:
+        traffic = json.load(open(tfile)).get("bytes_per_launch")
+
+    line = {
+        "metric": "effective TFLOP/s (2*M*K*N/t) + % of binding roofline, M=768 K=8192 N=4096 E=32",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8 (fp8 x fp8 x e8m0 -> f32)",
+        "data": "synthetic (seeded; FP8 from N(0,1), E8M0 exponents uniform)",
+        "config": {
+            "workload": f"{w.name}: M={w.M} K={w.K} N={w.N} E={w.E} batch={w.batch} "
+                        f"fp8={w.fp8} transpose_x2={w.transpose_x2} "
+                        f"group_list_type={w.group_list_type} shared_rows={w.R}",
+            "mode": "deterministic" if args.deterministic else "atomic",
+            "split_k": args.split_k,
+            "weight_copies_rotated": n_sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "fused_kernel (gfr grouped MXFP8 GEMM + finalize routing)",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mean_launch_ms": round(mean_launch_ms, 5),
+            "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

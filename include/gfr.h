@@ -1,0 +1,158 @@
+/*
+ * gfr.h — C ABI of the MI355X (gfx950) fused MXFP8 grouped-matmul +
+ * finalize-routing library (libgfr.so).
+ *
+ * The operation is the MoE "grouped matmul, then finalize routing" combine
+ * defined on two pages:
+ *   [P1] "基于 PyPTO 的 MoE 融合算子实践：grouped_matmul_finalize_routing 的
+ *        MXFP8 实现与精度验证" — §2.1 formula and expanded form, §2.2 the four
+ *        stages, §3.1 input/output table, §4.2 constraints, §4.3 group_list
+ *        formats, §5.3 kernel stages, §5.4 host wrapper (out is in/out);
+ *   [P3] CANN "aclnnGroupedMatmulFinalizeRoutingV3" — formulas 1-4, Atlas 350
+ *        MX parameter notes (shapes, empty-tensor rules), two-phase
+ *        workspace-size/execute call, determinism note.
+ *
+ * For every expert e, with token rows [start_e, end_e) taken from group_list:
+ *
+ *   out[row_index[t], n] += logit[t] * sum_k dq(x1[t, k]) * dq(x2[e, k, n])
+ *   out[off + r, n]      += shared_input_weight * shared_input[r, n]
+ *
+ * where dq(v) = FP8 value * 2^(E8M0 - 127) with one E8M0 scale per 32
+ * consecutive K elements: the scale tensors have a trailing (ceil(K/64), 2)
+ * pair of axes, and element j of the pair for 64-block b covers
+ * k in [64b + 32j, 64b + 32j + 32).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major storage
+ *    owned by the caller; the library never allocates, frees or retains them.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is the
+ *    null stream).  Nothing is synchronised and no device memory is read on the
+ *    host: group_list is consumed on the device.
+ *  - Arguments are validated on the host before anything is launched; on a
+ *    nonzero return nothing was enqueued and `out` is untouched.
+ *  - Data errors only visible on the device (see GFR_DEV_*) never cause an
+ *    out-of-bounds access: the offending work is skipped and, if a status word
+ *    is supplied through gfr_options, a bit is OR-ed into it.
+ *  - In the default mode `out` is updated with FP32 atomics, so the bitwise
+ *    result may vary between runs ([P3] determinism note); set
+ *    gfr_options.deterministic for a fixed summation order.
+ */
+#ifndef GFR_H
+#define GFR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum gfr_status {
+    GFR_OK = 0,
+    GFR_ERR_NULL_ARG = 1,        /* a required pointer is NULL */
+    GFR_ERR_BAD_SHAPE = 2,       /* negative or inconsistent sizes */
+    GFR_ERR_BAD_OFFSET = 3,      /* shared_input_offset < 0 or off + rows > batch */
+    GFR_ERR_UNSUPPORTED = 4,     /* valid per the pages but not implemented here */
+    GFR_ERR_BAD_ALIGNMENT = 5,   /* x1 / x2 / scale not 16-byte aligned */
+    GFR_ERR_WORKSPACE_TOO_SMALL = 6,
+    GFR_ERR_BAD_ARG = 7,         /* unknown enum value (fp8_kind, group_list_type) */
+    GFR_ERR_HIP = 8              /* a HIP runtime call failed */
+};
+
+/* FP8 element formats of x1 and x2 ([P1] §3.1: FP8 E4M3FN or E5M2). */
+enum gfr_fp8_kind { GFR_FP8_E4M3FN = 0, GFR_FP8_E5M2 = 1 };
+
+/* group_list formats ([P1] §4.3): 0 = prefix sums, expert i owns
+ * [group_list[i-1], group_list[i]) with group_list[-1] = 0; 1 = counts, expert
+ * i owns [sum(group_list[:i]), sum(group_list[:i]) + group_list[i]). */
+enum gfr_group_list_type { GFR_GROUP_LIST_CUMSUM = 0, GFR_GROUP_LIST_COUNT = 1 };
+
+/* Bits OR-ed into gfr_options.status_dev by the device. */
+#define GFR_DEV_BAD_GROUP_LIST 0x1 /* negative count, decreasing prefix, or total > M:
+                                      ranges are clamped to [0, M) */
+#define GFR_DEV_BAD_ROW_INDEX 0x2  /* row_index outside [0, batch): token skipped */
+
+/* Limits of this implementation. */
+#define GFR_MAX_EXPERTS 1024       /* [P3] Atlas 350 notes: e <= 1024 */
+
+typedef struct gfr_options {
+    /* 0: scatter-add with FP32 atomics (default).  1: deterministic — the
+     * matmul writes logit-weighted rows to the workspace, then each output row
+     * is reduced in a fixed order: initial value, tokens in ascending t, then
+     * the shared term.  Needs gfr_workspace_size() bytes of workspace. */
+    int deterministic;
+    /* Device workspace (may be NULL when 0 bytes are required). */
+    void *workspace;
+    size_t workspace_bytes;
+    /* Optional device int32 word; GFR_DEV_* bits are OR-ed into it. */
+    int32_t *status_dev;
+    /* K-split factor for the atomic mode; 0 = chosen on the device from the
+     * routed work size.  Ignored (1) in deterministic mode. */
+    int split_k;
+} gfr_options;
+
+/*
+ * gmm_finalize_routing — the fused operator ([P1] §2.1–2.2; [P3] formulas).
+ *
+ *  x1              [M, K] FP8 (fp8_kind), routed tokens sorted by expert.
+ *  x2              [E, K, N] FP8, or [E, N, K] when transpose_x2 != 0.
+ *  scale           E8M0 bytes, [ceil(K/64), N, 2], or [N, ceil(K/64), 2] when
+ *                  transpose_x2 != 0; shared by all experts ([P1] §3.1).
+ *  pertoken_scale  E8M0 bytes, [M, ceil(K/64), 2].
+ *  group_list      int64 [E], format per group_list_type.
+ *  logit           float32 [M], or NULL for weight 1 ([P1] §5.1 has_logit).
+ *  row_index       int64 [M], destination row of each token, in [0, batch).
+ *  shared_input    bfloat16 [shared_rows, N], or NULL (no shared expert).
+ *  shared_input_weight, shared_input_offset: shared rows land in
+ *                  out[offset, offset + shared_rows); offset >= 0 and
+ *                  offset + shared_rows <= batch.
+ *  out             float32 [batch, N]; read as the initial value and updated
+ *                  in place ([P1] §3.1, §5.4).
+ *  transpose_x2    0 or 1 (scale layout follows it, [P3] Atlas 350 notes).
+ *  fp8_kind        gfr_fp8_kind of both x1 and x2.
+ *  M, K, N, E, batch, shared_rows: sizes.  M = 0 leaves only the shared term;
+ *                  N = 0 or batch = 0 is a no-op ([P3] empty-tensor notes).
+ *  stream          hipStream_t.
+ *
+ * Implementation limits (GFR_ERR_UNSUPPORTED): K % 128 != 0, N % 16 != 0,
+ * E outside [1, 1024], M or batch >= 2^31.  x1, x2 and scale must be 16-byte
+ * aligned (GFR_ERR_BAD_ALIGNMENT).  Atomic mode needs no workspace.
+ * Returns a gfr_status.
+ */
+int gmm_finalize_routing(const void *x1, const void *x2, const uint8_t *scale,
+                         const uint8_t *pertoken_scale, const int64_t *group_list,
+                         int group_list_type, const float *logit,
+                         const int64_t *row_index, const uint16_t *shared_input,
+                         float shared_input_weight, int64_t shared_input_offset,
+                         float *out, int transpose_x2, int fp8_kind,
+                         int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                         int64_t shared_rows, void *stream);
+
+/* gmm_finalize_routing with options (NULL opts = defaults: atomic mode, no
+ * workspace, no status word).  Returns GFR_ERR_WORKSPACE_TOO_SMALL when the
+ * deterministic mode is asked for without enough workspace. */
+int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale,
+                            const uint8_t *pertoken_scale, const int64_t *group_list,
+                            int group_list_type, const float *logit,
+                            const int64_t *row_index, const uint16_t *shared_input,
+                            float shared_input_weight, int64_t shared_input_offset,
+                            float *out, int transpose_x2, int fp8_kind,
+                            int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                            int64_t shared_rows, void *stream,
+                            const gfr_options *opts);
+
+/* Workspace bytes a call with these sizes and options needs — the first phase
+ * of the two-phase call of [P3] ("GetWorkspaceSize", then execute).  Pure host
+ * arithmetic: no device call.  Returns a gfr_status. */
+int gfr_workspace_size(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                       const gfr_options *opts, size_t *bytes);
+
+/* Static, NUL-terminated description of a gfr_status. */
+const char *gfr_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GFR_H */

@@ -1,0 +1,153 @@
+"""ctypes binding of libgfr.so (include/gfr.h).
+
+Argument marshalling only: shapes and dtypes of torch tensors are read here,
+device pointers and sizes go to the C ABI, and every step of the operator runs
+in the library's HIP kernels.  torch provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgfr.so")
+
+GFR_OK = 0
+DEV_BAD_GROUP_LIST = 0x1
+DEV_BAD_ROW_INDEX = 0x2
+
+_FP8_KIND = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
+_E8M0 = (torch.uint8, torch.float8_e8m0fnu)
+
+
+class GfrError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gfr error {code}: {msg}")
+        self.code = code
+
+
+class GfrOptions(ctypes.Structure):
+    _fields_ = [("deterministic", ctypes.c_int), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p),
+                ("split_k", ctypes.c_int)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_MAIN_ARGS = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [
+    ctypes.c_float, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [
+    ctypes.c_int64] * 6 + [ctypes.c_void_p]
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libgfr.so; raises if it has not been built (no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "mxfp8_grouped_gemm_group_amd.build_lib.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.gmm_finalize_routing.argtypes = _MAIN_ARGS
+        lib.gmm_finalize_routing.restype = ctypes.c_int
+        lib.gmm_finalize_routing_ex.argtypes = _MAIN_ARGS + [ctypes.POINTER(GfrOptions)]
+        lib.gmm_finalize_routing_ex.restype = ctypes.c_int
+        lib.gfr_workspace_size.argtypes = [ctypes.c_int64] * 5 + [
+            ctypes.POINTER(GfrOptions), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gfr_workspace_size.restype = ctypes.c_int
+        lib.gfr_status_string.argtypes = [ctypes.c_int]
+        lib.gfr_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return load_library().gfr_status_string(code).decode()
+
+
+def workspace_size(M: int, K: int, N: int, E: int, batch: int, deterministic: bool = False) -> int:
+    opts = GfrOptions(int(deterministic), None, 0, None, 0)
+    n = ctypes.c_size_t(0)
+    rc = load_library().gfr_workspace_size(M, K, N, E, batch, ctypes.byref(opts), ctypes.byref(n))
+    if rc:
+        raise GfrError(rc, status_string(rc))
+    return n.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_type, logit,
+                         row_index, shared_input, shared_input_weight, shared_input_offset,
+                         out, transpose_x2=False, *, deterministic=False, workspace=None,
+                         status=None, split_k=0, stream=None):
+    """out += routed expert rows + shared term, in place; returns out.
+
+    x1 [M,K] / x2 [E,K,N] (or [E,N,K] when transpose_x2) are float8_e4m3fn or
+    float8_e5m2; scale / pertoken_scale hold E8M0 codes (uint8 or
+    float8_e8m0fnu); group_list int64 [E]; logit float32 [M] or None;
+    row_index int64 [M]; shared_input bfloat16 [R,N] or None; out float32
+    [batch,N].  ``status`` (int32 CUDA tensor, 1 element) receives device-side
+    data-error bits.  ``workspace`` (uint8 CUDA tensor) is allocated here when
+    the deterministic mode needs one and none is given.
+    """
+    lib = load_library()
+    _need(x1.dtype in _FP8_KIND and x2.dtype == x1.dtype, "x1/x2 must share an FP8 dtype")
+    _need(x1.dim() == 2 and x2.dim() == 3, "x1 must be 2-D and x2 3-D")
+    M, K = x1.shape
+    E = x2.shape[0]
+    if transpose_x2:
+        N = x2.shape[1]
+        _need(x2.shape[2] == K, "x2 [E,N,K] does not match K")
+    else:
+        N = x2.shape[2]
+        _need(x2.shape[1] == K, "x2 [E,K,N] does not match K")
+    KB = (K + 63) // 64
+    _need(scale.dtype in _E8M0 and pertoken_scale.dtype in _E8M0, "scales must be E8M0 bytes")
+    _need(tuple(scale.shape) == ((N, KB, 2) if transpose_x2 else (KB, N, 2)), "bad scale shape")
+    _need(tuple(pertoken_scale.shape) == (M, KB, 2), "bad pertoken_scale shape")
+    _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
+    _need(row_index.dtype == torch.int64 and tuple(row_index.shape) == (M,), "bad row_index")
+    if logit is not None:
+        _need(logit.dtype == torch.float32 and tuple(logit.shape) == (M,), "bad logit")
+    _need(out.dtype == torch.float32 and out.dim() == 2 and out.shape[1] == N, "bad out")
+    batch = out.shape[0]
+    R = 0
+    if shared_input is not None:
+        _need(shared_input.dtype == torch.bfloat16 and shared_input.dim() == 2
+              and shared_input.shape[1] == N, "bad shared_input")
+        R = shared_input.shape[0]
+    tensors = [x1, x2, scale, pertoken_scale, group_list, row_index, out, logit, shared_input,
+               workspace, status]
+    dev = out.device
+    for t in tensors:
+        if t is not None:
+            _need(t.is_cuda and t.device == dev, "all tensors must be on out's CUDA device")
+            _need(t.is_contiguous(), "all tensors must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ws_bytes = 0
+    if deterministic:
+        need = workspace_size(M, K, N, E, batch, True)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    opts = GfrOptions(int(bool(deterministic)), _ptr(workspace), ws_bytes, _ptr(status),
+                      int(split_k))
+    with torch.cuda.device(dev):
+        rc = lib.gmm_finalize_routing_ex(
+            _ptr(x1), _ptr(x2), _ptr(scale), _ptr(pertoken_scale), _ptr(group_list),
+            int(group_list_type), _ptr(logit), _ptr(row_index), _ptr(shared_input),
+            float(shared_input_weight), int(shared_input_offset), _ptr(out),
+            int(bool(transpose_x2)), _FP8_KIND[x1.dtype], M, K, N, E, batch, R,
+            ctypes.c_void_p(stream), ctypes.byref(opts))
+    if rc:
+        raise GfrError(rc, status_string(rc))
+    return out

@@ -1,0 +1,64 @@
+// Internal interface between the host API (gfr_api.cpp) and the kernels
+// (gfr_kernels.hip).  Not installed; the public ABI is include/gfr.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gfr {
+
+// Tile shape of one routed work item: 32 token rows x 128 output columns,
+// consumed in K steps of 64 (one 32x32x64 block-scaled MFMA per 32 columns).
+constexpr int kTileM = 32;
+constexpr int kTileN = 128;
+constexpr int kStepK = 64;
+constexpr int kWaveSize = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
+constexpr int kMaxExperts = 1024;
+// Shared-expert work item: 64 lanes x 4 x 8 bf16 elements.
+constexpr int kSharedChunk = kWaveSize * 32;
+
+// Everything a launch needs; device pointers, plain sizes.
+struct FusedParams {
+    const uint8_t *x1;
+    const uint8_t *x2;
+    const uint8_t *scale;
+    const uint8_t *pts;
+    const int64_t *group_list;
+    const float *logit;        // may be null (weight 1)
+    const int64_t *row_index;
+    const uint16_t *shared;    // may be null
+    float shared_w;
+    int32_t shared_off;
+    int32_t shared_rows;
+    float *out;
+    float *wbuf;               // deterministic mode: weighted rows [M, N]; else null
+    int32_t *status;           // may be null
+    int32_t *det_total;        // deterministic mode: routed-token total written here
+    int32_t M, K, N, E, batch;
+    int32_t group_list_type;
+    int32_t split_k;           // 0: chosen on the device
+};
+
+// Deterministic-mode workspace layout (all offsets 256-byte aligned):
+//   wbuf          float [M, N]     weighted matmul rows
+//   counts        int32 [batch]    tokens per output row (cleared each call)
+//   cursor        int32 [batch]    fill positions
+//   offsets       int32 [batch+1]  exclusive prefix of counts
+//   tokens        int32 [M]        tokens grouped by output row
+//   total_tokens  int32            routed tokens (sum of group counts)
+struct DetLayout {
+    size_t wbuf, counts, cursor, offsets, tokens, total_tokens, total;
+};
+DetLayout det_layout(int64_t M, int64_t N, int64_t batch);
+
+// Launchers; return hipSuccess or the launch error.
+hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
+                        hipStream_t stream);
+hipError_t launch_deterministic_prep(const FusedParams &p, void *workspace,
+                                     hipStream_t stream);
+hipError_t launch_deterministic_reduce(const FusedParams &p, void *workspace,
+                                       hipStream_t stream);
+
+}  // namespace gfr

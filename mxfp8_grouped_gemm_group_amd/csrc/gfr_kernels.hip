@@ -1,0 +1,648 @@
+// gfx950 kernels of the fused MXFP8 grouped-matmul + finalize-routing operator.
+//
+// Operation (page "grouped_matmul_finalize_routing 的 MXFP8 实现与精度验证",
+// §2.1 formula, §2.2 four stages; CANN "aclnnGroupedMatmulFinalizeRoutingV3",
+// formulas 1-4):
+//   out[row_index[t], n] += logit[t] * sum_k dq(x1[t,k]) dq(x2[e(t),k,n])
+//   out[off + r, n]      += shared_w * shared_input[r, n]
+//
+// One persistent launch does all of it:
+//   * prologue — every workgroup turns group_list into per-expert token ranges
+//     and a prefix of work items in LDS (no host round trip; ragged and empty
+//     experts cost nothing);
+//   * routed items — (expert, 32-token m-tile, 128-column n-tile, K split),
+//     one per wave.  x2 and x1 go global -> VGPR with a 3-deep software
+//     pipeline; the [K, N] weight layout is byte-transposed in registers
+//     (v_perm) into the K-contiguous operand the MFMA wants; the contraction is
+//     v_mfma_scale_f32_32x32x64_f8f6f4 with the E8M0 scales fed per lane (one
+//     scale per 32 K elements of one row / column);
+//   * epilogue — acc * logit, then FP32 atomic add into out[row_index[t], n]
+//     (or, in deterministic mode, a plain store of the weighted row);
+//   * shared items — the bf16 shared-expert axpy, atomically, same launch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gfr.h"
+#include "gfr_internal.h"
+
+namespace gfr {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ uint2 ld8(const uint8_t *p) {
+    return *reinterpret_cast<const uint2 *>(p);
+}
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// In-register 4x4 byte transpose: on entry w_r holds bytes (r, 0..3) of a
+// 4x4 byte block, on exit w_c holds bytes (0..3, c).
+__device__ __forceinline__ void transpose4x4(uint32_t &w0, uint32_t &w1, uint32_t &w2,
+                                             uint32_t &w3) {
+    // v_perm_b32(a, b, sel): selector byte 0-3 picks a byte of b, 4-7 of a.
+    const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
+    const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
+    const uint32_t t2 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
+    const uint32_t t3 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // w2.2 w3.2 w2.3 w3.3
+    w0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);                 // w0.0 w1.0 w2.0 w3.0
+    w1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);                 // w0.1 w1.1 w2.1 w3.1
+    w2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);                 // w0.2 ...
+    w3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);                 // w0.3 ...
+}
+
+__device__ __forceinline__ void flag(int32_t *status, int32_t bit) {
+    if (status) atomicOr(status, bit);
+}
+
+// Exclusive block-wide prefix sum (Hillis-Steele in LDS).
+template <class T>
+__device__ T block_exclusive_scan(T v, T *s_scan, T &total) {
+    const int tid = threadIdx.x;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kBlockThreads; off <<= 1) {
+        const T add = tid >= off ? s_scan[tid - off] : T(0);
+        __syncthreads();
+        s_scan[tid] += add;
+        __syncthreads();
+    }
+    const T incl = s_scan[tid];
+    total = s_scan[kBlockThreads - 1];
+    __syncthreads();
+    return incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Work list (group_list -> expert ranges -> item prefix), built in LDS by
+// every workgroup.  group_list formats per the page's §4.3: type 0 = prefix
+// sums, type 1 = counts.  Invalid lists are clamped into [0, M) and flagged.
+// ---------------------------------------------------------------------------
+struct WorkList {
+    int *start;   // [E]   first token of expert e
+    int *cnt;     // [E]   tokens of expert e
+    int *pref;    // [E+1] prefix of per-expert item counts (one K split)
+    int routed_tokens;  // sum of counts
+    int items;          // pref[E]
+};
+
+constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
+
+__device__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
+                                int64_t *s_scan) {
+    const int tid = threadIdx.x;
+    int c[kPerThread];
+    int64_t csum = 0;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int e = tid * kPerThread + i;
+        int64_t v = 0;
+        if (e < p.E && p.M > 0) {  // with M = 0 group_list may be absent
+            const int64_t g = p.group_list[e];
+            if (p.group_list_type == GFR_GROUP_LIST_COUNT) {
+                v = g;
+            } else {
+                v = g - (e > 0 ? p.group_list[e - 1] : 0);
+            }
+            if (v < 0) { bad = true; v = 0; }
+            if (v > p.M) { bad = true; v = p.M; }
+        }
+        c[i] = static_cast<int>(v);
+        csum += c[i];
+    }
+    // 64-bit: with invalid lists the raw sum can exceed M many times over.
+    int64_t total_tokens = 0;
+    int64_t run = block_exclusive_scan<int64_t>(csum, s_scan, total_tokens);
+    int64_t isum = 0;
+    int items[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int e = tid * kPerThread + i;
+        int cnt = c[i];
+        if (run + cnt > p.M) { bad = true; cnt = run < p.M ? static_cast<int>(p.M - run) : 0; }
+        if (e < p.E) {
+            wl.start[e] = static_cast<int>(run < p.M ? run : p.M);
+            wl.cnt[e] = cnt;
+        }
+        run += c[i];
+        items[i] = ((cnt + kTileM - 1) / kTileM) * n_tiles;
+        isum += items[i];
+    }
+    // Item totals stay below 2^31: the host bounds (M/32 + E) * ceil(N/128).
+    int64_t total_items = 0;
+    int64_t ipre = block_exclusive_scan<int64_t>(isum, s_scan, total_items);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int e = tid * kPerThread + i;
+        if (e < p.E) wl.pref[e] = static_cast<int>(ipre);
+        ipre += items[i];
+    }
+    if (tid == 0) wl.pref[p.E] = static_cast<int>(total_items);
+    wl.routed_tokens = static_cast<int>(total_tokens < p.M ? total_tokens : p.M);
+    wl.items = static_cast<int>(total_items);
+    if (bad && blockIdx.x == 0) flag(p.status, GFR_DEV_BAD_GROUP_LIST);
+    __syncthreads();
+}
+
+// Largest e in [0, E) with pref[e] <= q (pref non-decreasing, pref[0] = 0).
+__device__ __forceinline__ int find_expert(const int *pref, int E, int q) {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] <= q) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Routed item: 32 tokens [m0, m0 + mcount) of expert e, columns
+// [n0, n0 + 128), K steps [ks0, ks1) of 64.
+//
+// Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 for one 64-wide K step
+// (lane l, c = l % 32, g = l / 32), as measured on gfx950 with one-hot data
+// and a distinct scale per lane:
+//   A / B: row (column) c; bytes 0..15 hold K [16g, 16g + 16) and bytes
+//          16..31 hold K [32 + 16g, 48 + 16g) of the step, i.e. a lane carries
+//          half of each of the step's two 32-element scale blocks;
+//   scales: the E8M0 of 32-block b of row (column) c comes from lane c + 32b,
+//          so lane (c, g) supplies block g.
+//   D: 16 floats; element r is row 8(r/4) + 4g + r%4, column c.
+// Column c of MFMA j maps to output column n0 + 4c + j for the [K, N] layout
+// (each lane loads 4 adjacent columns and transposes them in registers) and
+// n0 + 32j + c for the [N, K] layout.
+// ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes); the wave-uniform base and
+// row offsets live in SGPRs, each lane keeps one 32-bit offset.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+struct StepKN {           // one K step, [K, N] weight layout
+    // Operand byte i of the lane (K row 16g + i + 16*(i >= 16) of the step,
+    // 4 adjacent columns) is loaded into slot 8*(i%4) + i/4, so the in-place
+    // 4x4 byte transposes of slots {q, 8+q, 16+q, 24+q} leave column j's 32
+    // operand bytes in slots 8j .. 8j+7: the MFMA operand, contiguous.
+    uint32_t b[32];
+    v4i alo, ahi;         // x1 row: K [16g, +16) and K [32 + 16g, +16) of the step
+    uint32_t sa;          // x1 scale byte
+    v2i sb;               // weight scales: 4 columns x 2 halves
+};
+
+struct StepNK {           // one K step, [N, K] weight layout
+    v4i b[4][2];          // 4 MFMA column tiles x (K [16g, +16), K [32 + 16g, +16))
+    v4i alo, ahi;
+    uint32_t sa;
+    uint32_t sb[4];
+};
+
+// D += A * B with per-lane E8M0 scales; OPSEL_B picks the byte of sb.
+template <int FMT, int OPSEL_B>
+__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f acc, uint32_t sa, uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, FMT, FMT, 0, sa,
+                                                            OPSEL_B, sb);
+}
+
+__device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Epilogue: weight each row by its logit and scatter-add (or store) it.
+__device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)[4],
+                                         int m0, int mcount, int n0, bool kn_layout,
+                                         bool store_rows) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (row >= mcount) continue;
+        const int t = m0 + row;
+        const int64_t dst = p.row_index[t];
+        const float w = p.logit ? p.logit[t] : 1.0f;
+        if (dst < 0 || dst >= p.batch) {
+            flag(p.status, GFR_DEV_BAD_ROW_INDEX);
+            continue;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = kn_layout ? n0 + 4 * c + j : n0 + 32 * j + c;
+            if (col >= p.N) continue;
+            const float v = acc[j][r] * w;
+            if (store_rows) {
+                p.wbuf[static_cast<int64_t>(t) * p.N + col] = v;
+            } else {
+                unsafeAtomicAdd(p.out + dst * p.N + col, v);
+            }
+        }
+    }
+}
+
+// Software pipeline over K steps with D buffers: the loads of step s + D - 1
+// are issued before step s is consumed.
+template <int D, class Buf, class Load, class Comp>
+__device__ __forceinline__ void pipeline(int s0, int s1, Buf (&buf)[D], Load load, Comp comp) {
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (s0 + d < s1) load(buf[d], s0 + d);
+    for (int s = s0; s < s1; s += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (s + d < s1) {
+                if (s + d + D - 1 < s1) load(buf[(d + D - 1) % D], s + d + D - 1);
+                comp(buf[d]);
+            }
+        }
+    }
+}
+
+constexpr int kDepth = 2;
+
+template <int FMT>
+__device__ void routed_item_kn(const FusedParams &p, int e, int m0, int mcount, int n0,
+                               int ks0, int ks1, bool store_rows) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+    const int K = p.K, N = p.N, KS = p.K / 32;
+    // x1 rows of this tile; padding rows read row 0 and are zeroed before use
+    const bool arow_ok = c < mcount;
+    const int arow = arow_ok ? c : 0;
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
+    const int va = arow * K + 16 * g;
+    const int vsa = arow * KS + g;
+    // 4 adjacent weight columns of this lane (clamped when past N)
+    const int col = n0 + 4 * c;
+    const int colc = col < N ? col : n0;
+    const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * K * N, static_cast<int64_t>(K) * N);
+    const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(K / 64) * N * 2);
+    const int vb = 16 * g * N + colc;
+    const int vsb = colc * 2;
+
+    v16f acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = v16f{};
+
+    StepKN buf[kDepth];
+    auto load = [&](StepKN &s, int ks) {
+        const int k0 = ks * kStepK;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            s.b[8 * (i & 3) + (i >> 2)] =
+                __builtin_amdgcn_raw_buffer_load_b32(rb, vb, (k0 + i + 16 * (i >> 4)) * N, 0);
+        s.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
+        s.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
+        s.sa = __builtin_amdgcn_raw_buffer_load_b8(rsa, vsa, k0 / 32, 0);
+        s.sb = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb, ks * 2 * N, 0);
+    };
+    auto comp = [&](StepKN &s) {
+        const v8i a = arow_ok ? cat(s.alo, s.ahi) : v8i{};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            transpose4x4(s.b[q], s.b[8 + q], s.b[16 + q], s.b[24 + q]);
+        v8i bt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bt[j][q] = s.b[8 * j + q];
+        const uint32_t s01 = static_cast<uint32_t>(s.sb.x) >> (8 * g);  // byte 0: col 0, byte 2: col 1
+        const uint32_t s23 = static_cast<uint32_t>(s.sb.y) >> (8 * g);  // byte 0: col 2, byte 2: col 3
+        acc[0] = mfma<FMT, 0>(a, bt[0], acc[0], s.sa, s01);
+        acc[1] = mfma<FMT, 2>(a, bt[1], acc[1], s.sa, s01);
+        acc[2] = mfma<FMT, 0>(a, bt[2], acc[2], s.sa, s23);
+        acc[3] = mfma<FMT, 2>(a, bt[3], acc[3], s.sa, s23);
+    };
+    pipeline<kDepth>(ks0, ks1, buf, load, comp);
+    epilogue(p, acc, m0, mcount, n0, true, store_rows);
+}
+
+template <int FMT>
+__device__ void routed_item_nk(const FusedParams &p, int e, int m0, int mcount, int n0,
+                               int ks0, int ks1, bool store_rows) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+    const int K = p.K, N = p.N, KS = p.K / 32;
+    const bool arow_ok = c < mcount;
+    const int arow = arow_ok ? c : 0;
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
+    const int va = arow * K + 16 * g;
+    const int vsa = arow * KS + g;
+    const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * N * K, static_cast<int64_t>(K) * N);
+    const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(KS) * N);
+    int vb[4], vsb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + 32 * j + c;
+        const int colc = col < N ? col : n0;
+        vb[j] = colc * K + 16 * g;
+        vsb[j] = colc * KS + g;
+    }
+
+    v16f acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = v16f{};
+
+    StepNK buf[kDepth];
+    auto load = [&](StepNK &s, int ks) {
+        const int k0 = ks * kStepK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s.b[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb[j], k0, 0);
+            s.b[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb[j], k0 + 32, 0);
+            s.sb[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb, vsb[j], k0 / 32, 0);
+        }
+        s.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
+        s.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
+        s.sa = __builtin_amdgcn_raw_buffer_load_b8(rsa, vsa, k0 / 32, 0);
+    };
+    auto comp = [&](StepNK &s) {
+        const v8i a = arow_ok ? cat(s.alo, s.ahi) : v8i{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[j] = mfma<FMT, 0>(a, cat(s.b[j][0], s.b[j][1]), acc[j], s.sa, s.sb[j]);
+    };
+    pipeline<kDepth>(ks0, ks1, buf, load, comp);
+    epilogue(p, acc, m0, mcount, n0, false, store_rows);
+}
+
+// Shared-expert item: kSharedChunk consecutive elements of shared_input.
+__device__ void shared_item(const FusedParams &p, int64_t item) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int64_t total = static_cast<int64_t>(p.shared_rows) * p.N;
+#pragma unroll
+    for (int i = 0; i < kSharedChunk / (kWaveSize * 8); ++i) {
+        const int64_t e0 = item * kSharedChunk + (i * kWaveSize + lane) * 8;
+        if (e0 >= total) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(p.shared + e0);
+        const int64_t r = e0 / p.N;
+        const int64_t col = e0 - r * p.N;
+        float *o = p.out + (p.shared_off + r) * p.N + col;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            unsafeAtomicAdd(o + 2 * u, p.shared_w * __uint_as_float(w[u] << 16));
+            unsafeAtomicAdd(o + 2 * u + 1, p.shared_w * __uint_as_float(w[u] & 0xffff0000u));
+        }
+    }
+}
+
+template <int FMT, bool TRANS>
+__global__ __launch_bounds__(kBlockThreads, 2) void fused_kernel(FusedParams p) {
+    __shared__ int s_start[kMaxExperts];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_pref[kMaxExperts + 1];
+    __shared__ int64_t s_scan[kBlockThreads];
+
+    const int n_tiles = (p.N + kTileN - 1) / kTileN;
+    WorkList wl{s_start, s_cnt, s_pref, 0, 0};
+    build_work_list(p, n_tiles, wl, s_scan);
+    if (p.det_total && blockIdx.x == 0 && threadIdx.x == 0) *p.det_total = wl.routed_tokens;
+
+    const bool store_rows = p.wbuf != nullptr;
+    const int k_steps = p.K / kStepK;
+    int S = p.split_k;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    if (store_rows) {
+        S = 1;
+    } else if (S <= 0) {
+        // Enough K splits to give every wave a routed item, keeping >= 8 K steps each.
+        S = wl.items > 0 ? static_cast<int>(waves / wl.items) : 1;
+        S = S < k_steps / 8 ? S : k_steps / 8;
+        S = S > 1 ? S : 1;
+    }
+    S = S < k_steps ? S : k_steps;
+    const int64_t routed = static_cast<int64_t>(wl.items) * S;
+    const int64_t shared_items =
+        (p.shared && !store_rows)
+            ? (static_cast<int64_t>(p.shared_rows) * p.N + kSharedChunk - 1) / kSharedChunk
+            : 0;
+    const int64_t total = routed + shared_items;
+
+    const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    for (int64_t it = wave_id; it < total; it += waves) {
+        if (it < routed) {
+            const int q = static_cast<int>(it / S);
+            const int e = find_expert(s_pref, p.E, q);
+            const int mt_count = (s_cnt[e] + kTileM - 1) / kTileM;
+            const int64_t local = it - static_cast<int64_t>(s_pref[e]) * S;
+            const int mt = static_cast<int>(local % mt_count);
+            const int64_t rest = local / mt_count;
+            const int s = static_cast<int>(rest % S);
+            const int nt = static_cast<int>(rest / S);
+            const int m0 = s_start[e] + mt * kTileM;
+            const int mcount = min(kTileM, s_cnt[e] - mt * kTileM);
+            const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
+            const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
+            if (TRANS)
+                routed_item_nk<FMT>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows);
+            else
+                routed_item_kn<FMT>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows);
+        } else {
+            shared_item(p, it - routed);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic mode: CSR of row_index, then a fixed-order reduction
+//   out[b] = ((init + W[t_1]) + W[t_2]) + ... + shared,  t_1 < t_2 < ...
+// ---------------------------------------------------------------------------
+__global__ void det_count_kernel(FusedParams p, int *counts) {
+    const int T = *p.det_total;
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+        const int64_t b = p.row_index[t];
+        if (b >= 0 && b < p.batch) atomicAdd(counts + b, 1);
+    }
+}
+
+__global__ void det_scan_kernel(FusedParams p, const int *counts, int *offsets, int *cursor) {
+    __shared__ int64_t s_scan[kBlockThreads];
+    __shared__ int64_t s_carry;
+    if (threadIdx.x == 0) s_carry = 0;
+    __syncthreads();
+    for (int base = 0; base < p.batch; base += kBlockThreads) {
+        const int b = base + threadIdx.x;
+        const int64_t v = b < p.batch ? counts[b] : 0;
+        int64_t tot = 0;
+        const int64_t ex = block_exclusive_scan<int64_t>(v, s_scan, tot);
+        if (b < p.batch) {
+            offsets[b] = static_cast<int>(s_carry + ex);
+            cursor[b] = static_cast<int>(s_carry + ex);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) s_carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) offsets[p.batch] = static_cast<int>(s_carry);
+}
+
+__global__ void det_fill_kernel(FusedParams p, int *cursor, int *tokens) {
+    const int T = *p.det_total;
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+        const int64_t b = p.row_index[t];
+        if (b >= 0 && b < p.batch) tokens[atomicAdd(cursor + b, 1)] = t;
+    }
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+    return v;
+}
+
+constexpr int kDetSortCap = 512;  // tokens per output row ordered in LDS
+
+// One wave per output row.  The row's tokens (filled in arbitrary order) are
+// put in ascending t — by rank (count of smaller tokens; tokens are distinct)
+// into LDS when the row has at most kDetSortCap of them, otherwise by repeated
+// wave-wide minimum searches — and reduced in that order:
+//   out[b] = ((init + W[t_1]) + W[t_2]) + ... + shared term.
+__global__ __launch_bounds__(kBlockThreads) void det_reduce_kernel(FusedParams p,
+                                                                   const int *offsets,
+                                                                   const int *tokens) {
+    __shared__ int s_sorted[kWavesPerBlock][kDetSortCap];
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wv = threadIdx.x >> 6;
+    int *sorted = s_sorted[wv];
+    const int wave = blockIdx.x * kWavesPerBlock + wv;
+    const int waves = gridDim.x * kWavesPerBlock;
+    for (int b = wave; b < p.batch; b += waves) {
+        const int o0 = offsets[b], L = offsets[b + 1] - o0;
+        const bool in_lds = L <= kDetSortCap;
+        if (in_lds) {
+            for (int i = lane; i < L; i += kWaveSize) {
+                const int ti = tokens[o0 + i];
+                int rank = 0;
+                for (int j = 0; j < L; ++j) rank += tokens[o0 + j] < ti;
+                sorted[rank] = ti;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const bool has_shared = p.shared && b >= p.shared_off && b < p.shared_off + p.shared_rows;
+        for (int col0 = 0; col0 < p.N; col0 += kWaveSize) {
+            const int col = col0 + lane;
+            const bool ok = col < p.N;
+            float acc = ok ? p.out[static_cast<int64_t>(b) * p.N + col] : 0.0f;
+            int prev = -1;
+            for (int i = 0; i < L; ++i) {
+                int t;
+                if (in_lds) {
+                    t = sorted[i];
+                } else {
+                    int m = 0x7fffffff;
+                    for (int j = lane; j < L; j += kWaveSize) {
+                        const int tj = tokens[o0 + j];
+                        if (tj > prev && tj < m) m = tj;
+                    }
+                    t = wave_min(m);
+                    prev = t;
+                }
+                if (ok) acc += p.wbuf[static_cast<int64_t>(t) * p.N + col];
+            }
+            if (ok && has_shared) {
+                const uint16_t h = p.shared[static_cast<int64_t>(b - p.shared_off) * p.N + col];
+                acc += p.shared_w * __uint_as_float(static_cast<uint32_t>(h) << 16);
+            }
+            if (ok) p.out[static_cast<int64_t>(b) * p.N + col] = acc;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+}
+
+__global__ void fill_zero_kernel(int *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int FMT, bool TRANS>
+hipError_t launch_fused_t(const FusedParams &p, hipStream_t stream) {
+    const int grid = device_cu_count() * 2;
+    hipLaunchKernelGGL((fused_kernel<FMT, TRANS>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    DetLayout d{};
+    d.wbuf = 0;
+    d.counts = up(static_cast<size_t>(M) * N * sizeof(float));
+    d.cursor = d.counts + up(static_cast<size_t>(batch) * sizeof(int));
+    d.offsets = d.cursor + up(static_cast<size_t>(batch) * sizeof(int));
+    d.tokens = d.offsets + up((static_cast<size_t>(batch) + 1) * sizeof(int));
+    d.total_tokens = d.tokens + up(static_cast<size_t>(M) * sizeof(int));
+    d.total = d.total_tokens + 256;
+    return d;
+}
+
+hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
+                        hipStream_t stream) {
+    if (fp8_kind == GFR_FP8_E4M3FN)
+        return transpose_x2 ? launch_fused_t<0, true>(p, stream) : launch_fused_t<0, false>(p, stream);
+    return transpose_x2 ? launch_fused_t<1, true>(p, stream) : launch_fused_t<1, false>(p, stream);
+}
+
+// Workspace regions: see DetLayout.  The counts are cleared by a fill kernel
+// (not a memset node) so the sequence stays safe under graph capture.
+hipError_t launch_deterministic_prep(const FusedParams &p, void *workspace,
+                                     hipStream_t stream) {
+    const DetLayout d = det_layout(p.M, p.N, p.batch);
+    int *counts = reinterpret_cast<int *>(static_cast<char *>(workspace) + d.counts);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(device_cu_count()), dim3(kBlockThreads), 0,
+                       stream, counts, p.batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_deterministic_reduce(const FusedParams &p, void *workspace,
+                                       hipStream_t stream) {
+    const DetLayout d = det_layout(p.M, p.N, p.batch);
+    char *ws = static_cast<char *>(workspace);
+    int *counts = reinterpret_cast<int *>(ws + d.counts);
+    int *cursor = reinterpret_cast<int *>(ws + d.cursor);
+    int *offsets = reinterpret_cast<int *>(ws + d.offsets);
+    int *tokens = reinterpret_cast<int *>(ws + d.tokens);
+    const int cu = device_cu_count();
+    hipLaunchKernelGGL(det_count_kernel, dim3(cu), dim3(kBlockThreads), 0, stream, p, counts);
+    hipLaunchKernelGGL(det_scan_kernel, dim3(1), dim3(kBlockThreads), 0, stream, p, counts,
+                       offsets, cursor);
+    hipLaunchKernelGGL(det_fill_kernel, dim3(cu), dim3(kBlockThreads), 0, stream, p, cursor,
+                       tokens);
+    hipLaunchKernelGGL(det_reduce_kernel, dim3(cu * 2), dim3(kBlockThreads), 0, stream, p,
+                       offsets, tokens);
+    return hipGetLastError();
+}
+
+}  // namespace gfr

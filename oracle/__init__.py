@@ -76,6 +76,9 @@ def _lib() -> ctypes.CDLL:
             i64, i64, i64, i64, i64,  # M K N E batch
             p, i64, p, p]             # rows n_rows res mag
         lib.oracle_gmm_finalize_routing.restype = ctypes.c_int
+        lib.oracle_mx_group_slack.argtypes = [
+            p, p, p, i32, p, p, i32, p, p, i32, i32, i64, i64, i64, i64, i64, p, i64, p]
+        lib.oracle_mx_group_slack.restype = ctypes.c_int
         _lib_handle = lib
     return _lib_handle
 
@@ -160,6 +163,39 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
     if rc:
         raise OracleError(rc)
     return res, mag
+
+
+def mx_group_slack(x1, x2, scale, pertoken_scale, group_list, group_list_type, logit,
+                   row_index, transpose_x2, fp8_kind, batch, rows=None):
+    """Per-element bound on the extra error of a dot-product unit that sums
+    runs of 8 consecutive K products aligned to the largest one and truncated
+    13 bits below it (see oracle_mx_group_slack in gfr_oracle.c).  Not part
+    of the operator: a tolerance term.  Returns float64 [len(rows), N]."""
+    x1 = _u8(x1)
+    x2 = _u8(x2)
+    scale = _u8(scale)
+    pts = _u8(pertoken_scale)
+    g = np.ascontiguousarray(group_list, dtype=np.int64)
+    ri = np.ascontiguousarray(row_index, dtype=np.int64)
+    M, K = x1.shape
+    E = x2.shape[0]
+    N = x2.shape[1] if transpose_x2 else x2.shape[2]
+    lg = None if logit is None else np.ascontiguousarray(logit, dtype=np.float32)
+    if rows is None:
+        rows_arr, n_rows = None, batch
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows_arr.shape[0]
+    out = np.zeros((n_rows, N), np.float64)
+    rc = _lib().oracle_mx_group_slack(
+        x1.ctypes.data, x2.ctypes.data, scale.ctypes.data, 1 if scale.ndim == 4 else 0,
+        pts.ctypes.data, g.ctypes.data, int(group_list_type),
+        None if lg is None else lg.ctypes.data, ri.ctypes.data, int(bool(transpose_x2)),
+        int(fp8_kind), M, K, N, E, batch,
+        None if rows_arr is None else rows_arr.ctypes.data, n_rows, out.ctypes.data)
+    if rc:
+        raise OracleError(rc)
+    return out
 
 
 def within_tolerance(got, ref, mag, rel=2e-5, abs_=1e-6):

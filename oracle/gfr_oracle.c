@@ -322,3 +322,94 @@ done:
     free(absacc);
     return rc;
 }
+
+/* ---------------------------------------------------------------------------
+ * Tolerance support, not part of the operator: a per-element bound on the
+ * extra error of a block-scaled dot-product unit that sums each run of 8
+ * consecutive K products (k in [8i, 8i + 8)) after aligning them to the
+ * largest one's binary exponent E and truncating below 2^(E - 13).  Each
+ * product can then lose less than min(|term|, 2^(E - 13)).  Returned, for the
+ * selected rows, is
+ *   slack[b, n] = sum over tokens t routed to b of |w_t| *
+ *                 sum over groups G of sum_{k in G} min(|term_k|, 2^(E_G - 13)).
+ * Arguments as for oracle_gmm_finalize_routing.
+ * ------------------------------------------------------------------------- */
+int oracle_mx_group_slack(
+    const uint8_t *x1, const uint8_t *x2, const uint8_t *scale,
+    int scale_per_expert, const uint8_t *pertoken_scale,
+    const int64_t *group_list, int group_list_type, const float *logit,
+    const int64_t *row_index, int transpose_x2, int fp8_kind,
+    int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+    const int64_t *rows, int64_t n_rows, double *slack_out)
+{
+    if (M < 0 || K <= 0 || N < 0 || E <= 0 || batch < 0 || n_rows < 0 ||
+        (fp8_kind != 0 && fp8_kind != 1) || (rows == NULL && n_rows != batch))
+        return ORACLE_BAD_ARG;
+    const int64_t KB = (K + 63) / 64;
+    double fp8v[256], e8m0v[256];
+    decode_tables(fp8_kind, fp8v, e8m0v);
+    int64_t *start = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t *end = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t *expert_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    double term[8];
+    int rc = ORACLE_OK;
+    if (!start || !end || !expert_of) {
+        rc = ORACLE_NO_MEMORY;
+        goto done;
+    }
+    rc = oracle_expert_ranges(group_list, E, group_list_type, M, start, end);
+    if (rc != ORACLE_OK)
+        goto done;
+    for (int64_t t = 0; t < M; ++t)
+        expert_of[t] = -1;
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t t = start[e]; t < end[e]; ++t)
+            expert_of[t] = e;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t b = rows ? rows[i] : i;
+        double *sl = slack_out + i * N;
+        for (int64_t n = 0; n < N; ++n)
+            sl[n] = 0.0;
+        for (int64_t t = 0; t < M; ++t) {
+            const int64_t e = expert_of[t];
+            if (e < 0 || row_index[t] != b)
+                continue;
+            const double w = fabs(logit ? (double)logit[t] : 1.0);
+            const uint8_t *ps_row = pertoken_scale + t * KB * 2;
+            const uint8_t *sc = scale + (scale_per_expert ? e * KB * N * 2 : 0);
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int64_t g0 = 0; g0 < K; g0 += 8) {
+                    double mx = 0.0;
+                    int cnt = 0;
+                    for (int64_t k = g0; k < g0 + 8 && k < K; ++k) {
+                        const double a = fp8v[x1[t * K + k]] *
+                                         e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
+                        const double bw = transpose_x2
+                            ? fp8v[x2[e * N * K + n * K + k]] *
+                                  e8m0v[sc[(n * KB + k / 64) * 2 + (k / 32) % 2]]
+                            : fp8v[x2[e * K * N + k * N + n]] *
+                                  e8m0v[sc[((k / 64) * N + n) * 2 + (k / 32) % 2]];
+                        term[cnt] = fabs(a * bw);
+                        if (term[cnt] > mx)
+                            mx = term[cnt];
+                        ++cnt;
+                    }
+                    if (mx == 0.0)
+                        continue;
+                    int ex;
+                    frexp(mx, &ex);                      /* mx in [2^(ex-1), 2^ex) */
+                    const double q = ldexp(1.0, ex - 1 - 13); /* 2^(E - 13) */
+                    for (int c = 0; c < cnt; ++c)
+                        acc += term[c] < q ? term[c] : q;
+                }
+                sl[n] += w * acc;
+            }
+        }
+    }
+done:
+    free(start);
+    free(end);
+    free(expert_of);
+    return rc;
+}

@@ -1,0 +1,87 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before any device call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_grouped_gemm_group_amd as gfr
+from mxfp8_grouped_gemm_group_amd._binding import GfrOptions
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = gfr.load_library()
+    names = _declared_functions()
+    assert {"gmm_finalize_routing", "gmm_finalize_routing_ex", "gfr_workspace_size",
+            "gfr_status_string"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(0, 9):
+        assert gfr.status_string(code)
+    assert gfr.status_string(0) == "ok"
+    assert gfr.status_string(999) == "unknown status"
+
+
+def test_workspace_size():
+    assert gfr.workspace_size(768, 8192, 4096, 32, 256, False) == 0
+    need = gfr.workspace_size(768, 8192, 4096, 32, 256, True)
+    assert need >= 768 * 4096 * 4 + 4 * (2 * 256 + 257 + 768)
+
+
+def _call(**over):
+    """Call gmm_finalize_routing_ex with fake non-null pointers and overrides;
+    only argument combinations that fail host validation are used, so nothing
+    is ever launched and no pointer is dereferenced."""
+    lib = gfr.load_library()
+    fake = 0x10000
+    a = dict(x1=fake, x2=fake, scale=fake, pts=fake, group_list=fake, gtype=1, logit=fake,
+             row_index=fake, shared=fake, sw=1.0, soff=0, out=fake, trans=0, kind=0,
+             M=768, K=8192, N=4096, E=32, batch=256, R=256, stream=None, opts=None)
+    a.update(over)
+    return lib.gmm_finalize_routing_ex(
+        a["x1"], a["x2"], a["scale"], a["pts"], a["group_list"], a["gtype"], a["logit"],
+        a["row_index"], a["shared"], a["sw"], a["soff"], a["out"], a["trans"], a["kind"],
+        a["M"], a["K"], a["N"], a["E"], a["batch"], a["R"], a["stream"], a["opts"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x1=None), 1), (dict(x2=None), 1), (dict(scale=None), 1), (dict(pts=None), 1),
+    (dict(group_list=None), 1), (dict(row_index=None), 1), (dict(out=None), 1),
+    (dict(M=-1), 2), (dict(K=0), 2), (dict(E=0), 2), (dict(batch=-3), 2),
+    (dict(soff=-1), 3), (dict(soff=1), 3), (dict(R=257), 3),
+    (dict(K=8000), 4), (dict(N=4100), 4), (dict(E=1025), 4), (dict(M=1 << 31), 4),
+    (dict(x1=0x10004), 5), (dict(x2=0x10008), 5), (dict(scale=0x10001), 5),
+    (dict(shared=0x10002), 5),
+    (dict(kind=2), 7), (dict(gtype=2), 7), (dict(trans=3), 7),
+])
+def test_host_validation(over, code):
+    assert _call(**over) == code
+
+
+def test_deterministic_needs_workspace():
+    opts = GfrOptions(1, None, 0, None, 0)
+    assert _call(opts=ctypes.byref(opts)) == 6
+    opts = GfrOptions(1, 0x10000, 100, None, 0)
+    assert _call(opts=ctypes.byref(opts)) == 6
+
+
+def test_empty_output_is_a_noop():
+    # N = 0 or batch = 0: valid per the empty-tensor rules, returns before any launch
+    assert _call(N=0) == 0
+    assert _call(batch=0, R=0, shared=None) == 0

@@ -383,3 +383,25 @@ def test_worked_example(kind, transpose):
     c, want = _load_worked_example(kind, transpose)
     got, _ = _run(c)
     assert np.array_equal(got, want)
+
+
+def test_mx_group_slack_analytic():
+    """Group-truncation slack: groups are 8 consecutive K; each term adds
+    min(|term|, 2^(E-13)) with E the exponent of the group's largest term."""
+    one, sub = 0x38, 0x01          # E4M3 1.0 and 2^-9
+    K, N = 16, 1
+    x1 = np.full((1, K), one, np.uint8)
+    x1[0, 1] = sub
+    x2 = np.zeros((1, K, N), np.uint8)
+    x2[0, 0:3, 0] = [one, sub, 0x30]      # group 0 terms: 1, 2^-18, 0.5 (x1[1] = 2^-9)
+    x2[0, 8:11, 0] = [sub, sub, sub]      # group 1 terms: 2^-9 each
+    pts = np.full((1, 1, 2), 127, np.uint8)
+    sc = np.full((1, N, 2), 127, np.uint8)
+    lg = np.array([0.5], np.float32)
+    got = oracle.mx_group_slack(x1, x2, sc, pts, np.array([1]), 1, lg, np.array([0]),
+                                False, 0, 1)
+    # group 0: E = 0, q = 2^-13; terms 1, 2^-9 * 2^-9 = 2^-18, 0.5
+    want_g0 = 2.0 ** -13 + 2.0 ** -18 + 2.0 ** -13
+    want_g1 = 3 * 2.0 ** -22            # E = -9, q = 2^-22, each term 2^-9 > q
+    assert got.shape == (1, 1)
+    assert got[0, 0] == 0.5 * (want_g0 + want_g1)

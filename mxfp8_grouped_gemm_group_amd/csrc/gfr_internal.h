@@ -16,8 +16,6 @@ constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
 constexpr int kMaxExperts = 1024;
-// Shared-expert work item: 64 lanes x 4 x 8 bf16 elements.
-constexpr int kSharedChunk = kWaveSize * 32;
 
 // Everything a launch needs; device pointers, plain sizes.
 struct FusedParams {

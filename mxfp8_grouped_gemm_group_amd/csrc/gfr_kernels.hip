@@ -22,6 +22,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "gfr.h"
 #include "gfr_internal.h"
 
@@ -183,6 +186,7 @@ __device__ __forceinline__ int find_expert(const int *pref, int E, int q) {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Raw buffer resource over [base, base + bytes); the wave-uniform base and
 // row offsets live in SGPRs, each lane keeps one 32-bit offset.
@@ -191,23 +195,74 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
 
-struct StepKN {           // one K step, [K, N] weight layout
-    // Operand byte i of the lane (K row 16g + i + 16*(i >= 16) of the step,
-    // 4 adjacent columns) is loaded into slot 8*(i%4) + i/4, so the in-place
-    // 4x4 byte transposes of slots {q, 8+q, 16+q, 24+q} leave column j's 32
-    // operand bytes in slots 8j .. 8j+7: the MFMA operand, contiguous.
-    uint32_t b[32];
-    v4i alo, ahi;         // x1 row: K [16g, +16) and K [32 + 16g, +16) of the step
-    uint32_t sa;          // x1 scale byte
-    v2i sb;               // weight scales: 4 columns x 2 halves
-};
+// s_waitcnt vmcnt(N) (other counters untouched), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
 
-struct StepNK {           // one K step, [N, K] weight layout
-    v4i b[4][2];          // 4 MFMA column tiles x (K [16g, +16), K [32 + 16g, +16))
-    v4i alo, ahi;
-    uint32_t sa;
-    uint32_t sb[4];
-};
+// LDS reads of the weight tile.  They are issued as inline asm because the
+// compiler's wait insertion cannot tell which direct-to-LDS load wrote which
+// slot and would otherwise drain every outstanding load before the read; the
+// explicit vmcnt wait before them orders the data.  Each asm block ends with
+// s_waitcnt lgkmcnt(0), so no consumer can be scheduled before the data is in
+// its registers.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
+}
+
+// 16 dwords at addr + O0 + 128 * i, i = 0..15 (one K row each of the [K, N]
+// tile).
+template <int O0>
+__device__ __forceinline__ void lds_read_16rows(uint32_t addr, uint32_t (&v)[16]) {
+    asm volatile(
+        "ds_read_b32 %0, %16 offset:%17\n\t"
+        "ds_read_b32 %1, %16 offset:%17+128\n\t"
+        "ds_read_b32 %2, %16 offset:%17+256\n\t"
+        "ds_read_b32 %3, %16 offset:%17+384\n\t"
+        "ds_read_b32 %4, %16 offset:%17+512\n\t"
+        "ds_read_b32 %5, %16 offset:%17+640\n\t"
+        "ds_read_b32 %6, %16 offset:%17+768\n\t"
+        "ds_read_b32 %7, %16 offset:%17+896\n\t"
+        "ds_read_b32 %8, %16 offset:%17+1024\n\t"
+        "ds_read_b32 %9, %16 offset:%17+1152\n\t"
+        "ds_read_b32 %10, %16 offset:%17+1280\n\t"
+        "ds_read_b32 %11, %16 offset:%17+1408\n\t"
+        "ds_read_b32 %12, %16 offset:%17+1536\n\t"
+        "ds_read_b32 %13, %16 offset:%17+1664\n\t"
+        "ds_read_b32 %14, %16 offset:%17+1792\n\t"
+        "ds_read_b32 %15, %16 offset:%17+1920\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+        : "v"(addr), "i"(O0)
+        : "memory");
+}
+
+// Four 16-byte reads at lo + 2048 j and four at hi + 2048 j, j = 0..3 (the
+// [N, K] tile's 32-column MFMA groups).
+__device__ __forceinline__ void lds_read_nk(uint32_t lo, uint32_t hi, v4i (&a)[4], v4i (&b)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:2048\n\t"
+        "ds_read_b128 %2, %8 offset:4096\n\t"
+        "ds_read_b128 %3, %8 offset:6144\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:2048\n\t"
+        "ds_read_b128 %6, %9 offset:4096\n\t"
+        "ds_read_b128 %7, %9 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(lo), "v"(hi)
+        : "memory");
+}
+
 
 // D += A * B with per-lane E8M0 scales; OPSEL_B picks the byte of sb.
 template <int FMT, int OPSEL_B>
@@ -220,12 +275,44 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Per-wave LDS ring: kStages slots of one K step of the 64 x 128 weight tile.
+constexpr int kStages = 4;
+constexpr int kSlotBytes = kStepK * kTileN;            // 8 KB
+constexpr int kRingBytes = kStages * kSlotBytes;       // 32 KB per wave
+constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
+static_assert(kRingBytes >= kTileM * kTileN * 4, "epilogue staging reuses the ring");
+
+// Registers that travel with one K step (the weight tile itself is in LDS).
+// Scales are loaded as the aligned dword that holds them and the byte is
+// selected when the step is consumed: a byte load would be zero-extended where
+// the compiler chooses, which can force an early wait on the load.
+struct StepRegs {
+    v4i alo, ahi;         // x1 row: K [16g, +16) and K [32 + 16g, +16) of the step
+    uint32_t sa;          // dword holding the x1 scale of 32-block 2ks + g
+    uint32_t sb[4];       // [K,N]: sb[0..1] = 8 bytes, 4 cols x 2 halves;
+                          // [N,K]: dword holding the scale of column j's block
+};
+
 // Epilogue: weight each row by its logit and scatter-add (or store) it.
+// acc element (j, r) of lane (c, g) is row 8(r/4) + 4g + r%4 and output column
+// n0 + col_of(c, j).  For the [K,N] layout the accumulator is first staged
+// through the wave's LDS ring so that each atomic covers 32 adjacent columns.
 __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)[4],
                                          int m0, int mcount, int n0, bool kn_layout,
-                                         bool store_rows) {
+                                         bool store_rows, char *ring) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
+    float *stage = reinterpret_cast<float *>(ring);     // [32 rows][128 cols]
+    if (kn_layout) {
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+            float4 v = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+            *reinterpret_cast<float4 *>(stage + row * kTileN + 4 * c) = v;  // cols 4c..4c+3
+        }
+        wait_lgkmcnt0();
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * g + (r & 3);
@@ -239,41 +326,35 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int col = kn_layout ? n0 + 4 * c + j : n0 + 32 * j + c;
+            const int col = n0 + 32 * j + c;
             if (col >= p.N) continue;
-            const float v = acc[j][r] * w;
-            if (store_rows) {
+            const float a = kn_layout ? stage[row * kTileN + 32 * j + c] : acc[j][r];
+            const float v = a * w;
+            if (store_rows)
                 p.wbuf[static_cast<int64_t>(t) * p.N + col] = v;
-            } else {
+            else
                 unsafeAtomicAdd(p.out + dst * p.N + col, v);
-            }
         }
     }
 }
 
-// Software pipeline over K steps with D buffers: the loads of step s + D - 1
-// are issued before step s is consumed.
-template <int D, class Buf, class Load, class Comp>
-__device__ __forceinline__ void pipeline(int s0, int s1, Buf (&buf)[D], Load load, Comp comp) {
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-        if (s0 + d < s1) load(buf[d], s0 + d);
-    for (int s = s0; s < s1; s += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            if (s + d < s1) {
-                if (s + d + D - 1 < s1) load(buf[(d + D - 1) % D], s + d + D - 1);
-                comp(buf[d]);
-            }
-        }
-    }
-}
-
-constexpr int kDepth = 2;
-
-template <int FMT>
-__device__ void routed_item_kn(const FusedParams &p, int e, int m0, int mcount, int n0,
-                               int ks0, int ks1, bool store_rows) {
+// ---------------------------------------------------------------------------
+// Routed item mainloop.  Per K step the wave
+//   * issues 8 direct-to-LDS 16-byte loads of the 64 x 128 weight tile into
+//     its ring slot, plus register loads of its x1 bytes and the scales;
+//   * waits (vmcnt) until the slot of the step it is about to use has landed,
+//     kStages - 1 steps are kept in flight;
+//   * reads its MFMA operands from LDS and runs 4 MFMAs (32 rows x 128 cols).
+// [K, N]: the slot is row-major [64 K rows][128 cols]; lane (c, g) reads the
+//   dword (4 columns) of each of its 32 K rows and byte-transposes in
+//   registers; slot byte i of the operand is placed as described at StepKN.
+// [N, K]: the slot is [128 cols][64 K bytes] with the four 16-byte chunks of
+//   a column XOR-swizzled by (col >> 1) & 3 so that 16-byte LDS reads of 32
+//   lanes do not collide on banks.
+// ---------------------------------------------------------------------------
+template <int FMT, bool KN>
+__device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
+                            int ks0, int ks1, bool store_rows, char *ring) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
@@ -283,129 +364,188 @@ __device__ void routed_item_kn(const FusedParams &p, int e, int m0, int mcount, 
     const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
     const int va = arow * K + 16 * g;
-    const int vsa = arow * KS + g;
-    // 4 adjacent weight columns of this lane (clamped when past N)
-    const int col = n0 + 4 * c;
-    const int colc = col < N ? col : n0;
+    const int vsa = arow * KS;     // + (2 ks) & ~3: KS is a multiple of 4
     const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * K * N, static_cast<int64_t>(K) * N);
-    const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(K / 64) * N * 2);
-    const int vb = 16 * g * N + colc;
-    const int vsb = colc * 2;
-
-    v16f acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = v16f{};
-
-    StepKN buf[kDepth];
-    auto load = [&](StepKN &s, int ks) {
-        const int k0 = ks * kStepK;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            s.b[8 * (i & 3) + (i >> 2)] =
-                __builtin_amdgcn_raw_buffer_load_b32(rb, vb, (k0 + i + 16 * (i >> 4)) * N, 0);
-        s.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
-        s.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
-        s.sa = __builtin_amdgcn_raw_buffer_load_b8(rsa, vsa, k0 / 32, 0);
-        s.sb = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb, ks * 2 * N, 0);
-    };
-    auto comp = [&](StepKN &s) {
-        const v8i a = arow_ok ? cat(s.alo, s.ahi) : v8i{};
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            transpose4x4(s.b[q], s.b[8 + q], s.b[16 + q], s.b[24 + q]);
-        v8i bt[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) bt[j][q] = s.b[8 * j + q];
-        const uint32_t s01 = static_cast<uint32_t>(s.sb.x) >> (8 * g);  // byte 0: col 0, byte 2: col 1
-        const uint32_t s23 = static_cast<uint32_t>(s.sb.y) >> (8 * g);  // byte 0: col 2, byte 2: col 3
-        acc[0] = mfma<FMT, 0>(a, bt[0], acc[0], s.sa, s01);
-        acc[1] = mfma<FMT, 2>(a, bt[1], acc[1], s.sa, s01);
-        acc[2] = mfma<FMT, 0>(a, bt[2], acc[2], s.sa, s23);
-        acc[3] = mfma<FMT, 2>(a, bt[3], acc[3], s.sa, s23);
-    };
-    pipeline<kDepth>(ks0, ks1, buf, load, comp);
-    epilogue(p, acc, m0, mcount, n0, true, store_rows);
-}
-
-template <int FMT>
-__device__ void routed_item_nk(const FusedParams &p, int e, int m0, int mcount, int n0,
-                               int ks0, int ks1, bool store_rows) {
-    const int lane = threadIdx.x & (kWaveSize - 1);
-    const int c = lane & 31, g = lane >> 5;
-    const int K = p.K, N = p.N, KS = p.K / 32;
-    const bool arow_ok = c < mcount;
-    const int arow = arow_ok ? c : 0;
-    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
-    const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
-    const int va = arow * K + 16 * g;
-    const int vsa = arow * KS + g;
-    const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * N * K, static_cast<int64_t>(K) * N);
     const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(KS) * N);
-    int vb[4], vsb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = n0 + 32 * j + c;
-        const int colc = col < N ? col : n0;
-        vb[j] = colc * K + 16 * g;
-        vsb[j] = colc * KS + g;
-    }
 
-    v16f acc[4];
+    // Weight-tile load offsets (lane part) and weight-scale offsets.  Columns
+    // past N (last partial n-tile) re-read column n0; their results are never
+    // written.
+    int vb[KN ? 1 : kBLoadsPerStep];
+    int vsb[4];
+    if (KN) {
+        // load u, lane l: K row 8u + l/8 (row offset in soffset), 16-byte chunk
+        // l%8 of the 128 columns
+        const int chunk_col = n0 + 16 * (lane & 7);
+        vb[0] = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
+        const int col = n0 + 4 * c;                 // the lane's 4 operand columns
+        vsb[0] = (col < N ? col : n0) * 2;
+        vsb[1] = vsb[2] = vsb[3] = 0;
+    } else {
+        // load u, lane l: column 16u + l/4; physical chunk l%4 of the slot holds
+        // logical chunk (l%4) ^ ((l/4 >> 1) & 3) of that column
+        const int q = (lane & 3) ^ (((lane >> 2) >> 1) & 3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = v16f{};
-
-    StepNK buf[kDepth];
-    auto load = [&](StepNK &s, int ks) {
-        const int k0 = ks * kStepK;
+        for (int u = 0; u < kBLoadsPerStep; ++u) {
+            const int col = n0 + 16 * u + (lane >> 2);
+            vb[u] = (col < N ? col : n0) * K + 16 * q;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            s.b[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb[j], k0, 0);
-            s.b[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb[j], k0 + 32, 0);
-            s.sb[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb, vsb[j], k0 / 32, 0);
+            const int cj = n0 + 32 * j + c;
+            vsb[j] = (cj < N ? cj : n0) * KS;
         }
-        s.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
-        s.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
-        s.sa = __builtin_amdgcn_raw_buffer_load_b8(rsa, vsa, k0 / 32, 0);
-    };
-    auto comp = [&](StepNK &s) {
-        const v8i a = arow_ok ? cat(s.alo, s.ahi) : v8i{};
+    }
+
+    v16f acc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[j] = mfma<FMT, 0>(a, cat(s.b[j][0], s.b[j][1]), acc[j], s.sa, s.sb[j]);
+    for (int j = 0; j < 4; ++j) acc[j] = v16f{};
+    StepRegs regs[kStages];
+
+    auto issue = [&](int ks, int slot) {
+        const int k0 = ks * kStepK;
+        __builtin_amdgcn_sched_barrier(0);
+        StepRegs &r = regs[slot];
+        r.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
+        r.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
+        r.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, (2 * ks) & ~3, 0);
+        if (KN) {
+            const v2i sb = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[0], ks * 2 * N, 0);
+            r.sb[0] = sb.x;
+            r.sb[1] = sb.y;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], (2 * ks) & ~3, 0);
+        }
+        // (the instruction's immediate offset would move both addresses, so
+        // each 1 KB destination gets its own LDS pointer)
+#pragma unroll
+        for (int u = 0; u < kBLoadsPerStep; ++u) {
+            lds_void_t *dst = (lds_void_t *)(ring + slot * kSlotBytes + u * 1024);
+            if (KN)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[0], (k0 + 8 * u) * N, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[u], k0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
-    pipeline<kDepth>(ks0, ks1, buf, load, comp);
-    epilogue(p, acc, m0, mcount, n0, false, store_rows);
+
+    auto compute = [&](int slot, bool live, int ks) {
+        StepRegs &r = regs[slot];
+        // padding rows and padding steps (re-reads past the last K step)
+        // multiply a zero operand
+        const v8i a = (arow_ok && live) ? cat(r.alo, r.ahi) : v8i{};
+        // byte (2 ks + g) & 3 of the scale dwords
+        const int sh = 8 * (2 * (ks & 1) + g);
+        const uint32_t sa = r.sa >> sh;
+        const char *sl = ring + slot * kSlotBytes;
+        if (KN) {
+            // operand byte i of lane (c, g) = K row 16g + i + 16*(i >= 16) of the step;
+            // loaded into b[8*(i%4) + i/4] so the transposes leave column j in b[8j..8j+7]
+            uint32_t b[32];
+            {
+                const uint32_t base = lds_addr(sl + (16 * g) * kTileN + 4 * c);
+                uint32_t r0[16], r1[16];
+                lds_read_16rows<0>(base, r0);                 // operand bytes 0..15
+                lds_read_16rows<32 * kTileN>(base, r1);       // operand bytes 16..31
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    b[8 * (i & 3) + (i >> 2)] = r0[i];
+                    b[8 * (i & 3) + ((i + 16) >> 2)] = r1[i];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) transpose4x4(b[q], b[8 + q], b[16 + q], b[24 + q]);
+            const uint32_t s01 = r.sb[0] >> (8 * g);   // byte 0: col 0, byte 2: col 1
+            const uint32_t s23 = r.sb[1] >> (8 * g);   // byte 0: col 2, byte 2: col 3
+            v8i bt[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) bt[j][q] = b[8 * j + q];
+            acc[0] = mfma<FMT, 0>(a, bt[0], acc[0], sa, s01);
+            acc[1] = mfma<FMT, 2>(a, bt[1], acc[1], sa, s01);
+            acc[2] = mfma<FMT, 0>(a, bt[2], acc[2], sa, s23);
+            acc[3] = mfma<FMT, 2>(a, bt[3], acc[3], sa, s23);
+        } else {
+            const int f = (c >> 1) & 3;
+            v4i lo[4], hi[4];
+            lds_read_nk(lds_addr(sl + c * 64 + 16 * (g ^ f)),
+                        lds_addr(sl + c * 64 + 16 * ((2 + g) ^ f)), lo, hi);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = mfma<FMT, 0>(a, cat(lo[j], hi[j]), acc[j], sa, r.sb[j] >> sh);
+        }
+    };
+
+    // Vector-memory instructions per step, in issue order: x1 (2), x1 scale
+    // (1), weight scales (1 or 4), weight tile (8).  Every iteration issues
+    // the same groups (past the last step the last step is re-read; those are
+    // L2 hits and are never consumed), so the wait for step ks's tile is a
+    // constant: only the kStages - 1 later groups may still be pending.
+    constexpr int kOpsPerStep = 3 + (KN ? 1 : 4) + kBLoadsPerStep;
+    static_assert((kStages - 1) * kOpsPerStep < 64, "vmcnt range");
+    const int n_steps = ks1 - ks0;
+    auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
+
+#pragma unroll
+    for (int d = 0; d < kStages - 1; ++d) issue(step_of(d), d);
+    for (int i0 = 0; i0 < n_steps; i0 += kStages) {
+#pragma unroll
+        for (int d = 0; d < kStages; ++d) {
+            // refill the slot consumed by the previous step
+            issue(step_of(i0 + d + kStages - 1), (d + kStages - 1) % kStages);
+            wait_vmcnt<(kStages - 1) * kOpsPerStep>();
+            __builtin_amdgcn_sched_barrier(0);
+            compute(d, i0 + d < n_steps, step_of(i0 + d));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // Drain the trailing re-reads before the ring is reused.
+    wait_vmcnt<0>();
+    epilogue(p, acc, m0, mcount, n0, KN, store_rows, ring);
 }
 
-// Shared-expert item: kSharedChunk consecutive elements of shared_input.
-__device__ void shared_item(const FusedParams &p, int64_t item) {
+// Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
+// contiguous slice of the R*N elements per wave, so every wave carries the
+// same small share (done before its routed work; the atomics are issued
+// without waiting and drain while the weights stream).  Lane l handles
+// elements 64i + l of the slice: every load and atomic covers 64 adjacent
+// elements.
+__device__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int64_t total = static_cast<int64_t>(p.shared_rows) * p.N;
+    int64_t per = (total + waves - 1) / waves;
+    per = (per + kWaveSize - 1) / kWaveSize * kWaveSize;
+    const int64_t begin = wave * per;
+    const int64_t end = begin + per < total ? begin + per : total;
+    float *o = p.out + static_cast<int64_t>(p.shared_off) * p.N;
+    constexpr int kBatch = 16;   // loads in flight per lane before their atomics
+    for (int64_t b = begin; b < end; b += kBatch * kWaveSize) {
+        uint16_t h[kBatch];
 #pragma unroll
-    for (int i = 0; i < kSharedChunk / (kWaveSize * 8); ++i) {
-        const int64_t e0 = item * kSharedChunk + (i * kWaveSize + lane) * 8;
-        if (e0 >= total) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(p.shared + e0);
-        const int64_t r = e0 / p.N;
-        const int64_t col = e0 - r * p.N;
-        float *o = p.out + (p.shared_off + r) * p.N + col;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t e = b + i * kWaveSize + lane;
+            h[i] = e < end ? p.shared[e] : 0;
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            unsafeAtomicAdd(o + 2 * u, p.shared_w * __uint_as_float(w[u] << 16));
-            unsafeAtomicAdd(o + 2 * u + 1, p.shared_w * __uint_as_float(w[u] & 0xffff0000u));
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t e = b + i * kWaveSize + lane;
+            if (e < end)
+                unsafeAtomicAdd(o + e, p.shared_w * __uint_as_float(static_cast<uint32_t>(h[i]) << 16));
         }
     }
 }
 
+// One block per CU (the four weight rings fill most of the 160 KB of LDS).
 template <int FMT, bool TRANS>
-__global__ __launch_bounds__(kBlockThreads, 2) void fused_kernel(FusedParams p) {
+__global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) {
     __shared__ int s_start[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_pref[kMaxExperts + 1];
     __shared__ int64_t s_scan[kBlockThreads];
+    __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock][kRingBytes];
 
     const int n_tiles = (p.N + kTileN - 1) / kTileN;
     WorkList wl{s_start, s_cnt, s_pref, 0, 0};
@@ -419,40 +559,48 @@ __global__ __launch_bounds__(kBlockThreads, 2) void fused_kernel(FusedParams p) 
     if (store_rows) {
         S = 1;
     } else if (S <= 0) {
-        // Enough K splits to give every wave a routed item, keeping >= 8 K steps each.
+        // Enough K splits to give every wave a routed item (long K runs per
+        // wave stream best, and every split adds a set of atomics), keeping
+        // >= 8 K steps each.
         S = wl.items > 0 ? static_cast<int>(waves / wl.items) : 1;
         S = S < k_steps / 8 ? S : k_steps / 8;
         S = S > 1 ? S : 1;
     }
     S = S < k_steps ? S : k_steps;
     const int64_t routed = static_cast<int64_t>(wl.items) * S;
-    const int64_t shared_items =
-        (p.shared && !store_rows)
-            ? (static_cast<int64_t>(p.shared_rows) * p.N + kSharedChunk - 1) / kSharedChunk
-            : 0;
-    const int64_t total = routed + shared_items;
 
-    const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    for (int64_t it = wave_id; it < total; it += waves) {
-        if (it < routed) {
+    // Everything that selects a work item is wave-uniform; readfirstlane makes
+    // that visible to the compiler so buffer descriptors and row offsets live
+    // in SGPRs (otherwise each buffer load becomes a waterfall loop).
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Workgroups are dealt to the 8 XCDs round-robin; number the waves so that
+    // consecutive items (the n-tiles and m-tiles of one expert, which share x1
+    // rows and scales) run on the same XCD and share its L2.
+    const int64_t wave_id =
+        (gridDim.x % 8 == 0)
+            ? ((static_cast<int64_t>(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) *
+                   kWavesPerBlock + wave_in_block)
+            : static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+    if (p.shared && !store_rows) shared_slice(p, wave_id, waves);
+    for (int64_t it = wave_id; it < routed; it += waves) {
+        {
             const int q = static_cast<int>(it / S);
-            const int e = find_expert(s_pref, p.E, q);
-            const int mt_count = (s_cnt[e] + kTileM - 1) / kTileM;
-            const int64_t local = it - static_cast<int64_t>(s_pref[e]) * S;
+            const int e = __builtin_amdgcn_readfirstlane(find_expert(s_pref, p.E, q));
+            const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
+            const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
+            const int e_pref = __builtin_amdgcn_readfirstlane(s_pref[e]);
+            const int mt_count = (e_cnt + kTileM - 1) / kTileM;
+            const int64_t local = it - static_cast<int64_t>(e_pref) * S;
             const int mt = static_cast<int>(local % mt_count);
             const int64_t rest = local / mt_count;
             const int s = static_cast<int>(rest % S);
             const int nt = static_cast<int>(rest / S);
-            const int m0 = s_start[e] + mt * kTileM;
-            const int mcount = min(kTileM, s_cnt[e] - mt * kTileM);
+            const int m0 = e_start + mt * kTileM;
+            const int mcount = min(kTileM, e_cnt - mt * kTileM);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            if (TRANS)
-                routed_item_nk<FMT>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows);
-            else
-                routed_item_kn<FMT>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows);
-        } else {
-            shared_item(p, it - routed);
+            routed_item<FMT, !TRANS>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows,
+                                     s_ring[wave_in_block]);
         }
     }
 }
@@ -588,7 +736,7 @@ int device_cu_count() {
 
 template <int FMT, bool TRANS>
 hipError_t launch_fused_t(const FusedParams &p, hipStream_t stream) {
-    const int grid = device_cu_count() * 2;
+    const int grid = device_cu_count();
     hipLaunchKernelGGL((fused_kernel<FMT, TRANS>), dim3(grid), dim3(kBlockThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -92,10 +92,18 @@ __device__ T block_exclusive_scan(T v, T *s_scan, T &total) {
 struct WorkList {
     int *start;   // [E]   first token of expert e
     int *cnt;     // [E]   tokens of expert e
-    int *pref;    // [E+1] prefix of per-expert item counts (one K split)
+    int *spref;   // [E+1] prefix of per-expert wave items (one K split)
+    int *lpref;   // [E+1] prefix of per-expert cooperative block items
     int routed_tokens;  // sum of counts
-    int items;          // pref[E]
+    int sitems;         // spref[E]
+    int litems;         // lpref[E]
 };
+
+// Experts with at least this many tokens are processed by cooperative block
+// items: the four waves of a block share one weight-tile stream and each
+// applies it to its own 32 rows, so one streamed tile serves 128 rows.
+constexpr int kCoopMinRows = 64;
+constexpr int kCoopRows = kTileM * kWavesPerBlock;   // 128
 
 constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 
@@ -125,8 +133,10 @@ __device__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
     // 64-bit: with invalid lists the raw sum can exceed M many times over.
     int64_t total_tokens = 0;
     int64_t run = block_exclusive_scan<int64_t>(csum, s_scan, total_tokens);
+    // Both item counts in one 64-bit scan: wave items low, block items high
+    // (each total stays below 2^31: the host bounds (M/32 + E) * ceil(N/128)).
     int64_t isum = 0;
-    int items[kPerThread];
+    int64_t items[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
@@ -137,21 +147,29 @@ __device__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
             wl.cnt[e] = cnt;
         }
         run += c[i];
-        items[i] = ((cnt + kTileM - 1) / kTileM) * n_tiles;
+        const int64_t si = cnt >= kCoopMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
+        const int64_t li = cnt >= kCoopMinRows ? ((cnt + kCoopRows - 1) / kCoopRows) * n_tiles : 0;
+        items[i] = si | (li << 32);
         isum += items[i];
     }
-    // Item totals stay below 2^31: the host bounds (M/32 + E) * ceil(N/128).
     int64_t total_items = 0;
     int64_t ipre = block_exclusive_scan<int64_t>(isum, s_scan, total_items);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
-        if (e < p.E) wl.pref[e] = static_cast<int>(ipre);
+        if (e < p.E) {
+            wl.spref[e] = static_cast<int>(ipre & 0xffffffff);
+            wl.lpref[e] = static_cast<int>(ipre >> 32);
+        }
         ipre += items[i];
     }
-    if (tid == 0) wl.pref[p.E] = static_cast<int>(total_items);
+    if (tid == 0) {
+        wl.spref[p.E] = static_cast<int>(total_items & 0xffffffff);
+        wl.lpref[p.E] = static_cast<int>(total_items >> 32);
+    }
     wl.routed_tokens = static_cast<int>(total_tokens < p.M ? total_tokens : p.M);
-    wl.items = static_cast<int>(total_items);
+    wl.sitems = static_cast<int>(total_items & 0xffffffff);
+    wl.litems = static_cast<int>(total_items >> 32);
     if (bad && blockIdx.x == 0) flag(p.status, GFR_DEV_BAD_GROUP_LIST);
     __syncthreads();
 }
@@ -339,26 +357,58 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
 }
 
 // ---------------------------------------------------------------------------
-// Routed item mainloop.  Per K step the wave
-//   * issues 8 direct-to-LDS 16-byte loads of the 64 x 128 weight tile into
-//     its ring slot, plus register loads of its x1 bytes and the scales;
-//   * waits (vmcnt) until the slot of the step it is about to use has landed,
-//     kStages - 1 steps are kept in flight;
-//   * reads its MFMA operands from LDS and runs 4 MFMAs (32 rows x 128 cols).
+// Routed item mainloop.  Per K step
+//   * the 64 x 128 weight tile is moved global -> LDS with 8 direct-to-LDS
+//     16-byte loads into a ring slot, and each wave loads its x1 bytes and the
+//     scales into registers;
+//   * a wave waits (vmcnt) until the slot it is about to use has landed, with
+//     the later steps' loads still in flight;
+//   * it reads its MFMA operands from LDS and runs 4 MFMAs (32 rows x 128 cols).
+// Two modes:
+//   wave (COOP = false): one wave owns the item, its own ring (kStages slots)
+//     and all 8 tile loads per step;
+//   cooperative (COOP = true): the four waves of a block share one ring
+//     (kCoopStagesKN / kCoopStagesNK slots); wave w issues tile loads 2w and 2w+1 of each step
+//     and applies the tile to its own 32 rows (rows 32w.. of a 128-row
+//     group); one s_barrier per step publishes the tile and retires the slot
+//     that is refilled next.
 // [K, N]: the slot is row-major [64 K rows][128 cols]; lane (c, g) reads the
 //   dword (4 columns) of each of its 32 K rows and byte-transposes in
-//   registers; slot byte i of the operand is placed as described at StepKN.
+//   registers; operand byte i is K row 16g + i + 16*(i >= 16) of the step.
 // [N, K]: the slot is [128 cols][64 K bytes] with the four 16-byte chunks of
 //   a column XOR-swizzled by (col >> 1) & 3 so that 16-byte LDS reads of 32
 //   lanes do not collide on banks.
 // ---------------------------------------------------------------------------
-template <int FMT, bool KN>
+constexpr int kCoopStagesKN = 8;   // vmcnt range caps these: (D - 2) * ops < 64
+constexpr int kCoopStagesNK = 8;
+static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
+                  kCoopStagesNK * kSlotBytes <= kWavesPerBlock * kRingBytes,
+              "cooperative ring fits the block's LDS");
+static_assert(kWavesPerBlock * kTileM * kTileN * 4 <= kWavesPerBlock * kRingBytes,
+              "per-wave epilogue staging fits the block's LDS");
+
+template <int FMT, bool KN, bool COOP>
 __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
-                            int ks0, int ks1, bool store_rows, char *ring) {
+                            int ks0, int ks1, bool store_rows, char *ring, char *stage,
+                            int w) {
+    constexpr int D = COOP ? (KN ? kCoopStagesKN : kCoopStagesNK) : kStages;
+    constexpr int kTileLoads = COOP ? kBLoadsPerStep / kWavesPerBlock : kBLoadsPerStep;
+    // The item is wave-uniform; say so, so that descriptors and offsets stay
+    // in SGPRs (a descriptor in VGPRs turns every buffer load into a loop).
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    mcount = __builtin_amdgcn_readfirstlane(mcount);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    ks0 = __builtin_amdgcn_readfirstlane(ks0);
+    ks1 = __builtin_amdgcn_readfirstlane(ks1);
+    w = __builtin_amdgcn_readfirstlane(w);
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
     // x1 rows of this tile; padding rows read row 0 and are zeroed before use
+    // (a cooperative wave past the expert's last row has mcount <= 0: its
+    // loads have an empty range and return zeros, its epilogue writes nothing)
+    if (mcount < 0) mcount = 0;
     const bool arow_ok = c < mcount;
     const int arow = arow_ok ? c : 0;
     const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
@@ -367,11 +417,12 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     const int vsa = arow * KS;     // + (2 ks) & ~3: KS is a multiple of 4
     const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * K * N, static_cast<int64_t>(K) * N);
     const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(KS) * N);
+    const int u0 = COOP ? w * kTileLoads : 0;   // first tile load this wave issues
 
     // Weight-tile load offsets (lane part) and weight-scale offsets.  Columns
     // past N (last partial n-tile) re-read column n0; their results are never
     // written.
-    int vb[KN ? 1 : kBLoadsPerStep];
+    int vb[KN ? 1 : kTileLoads];
     int vsb[4];
     if (KN) {
         // load u, lane l: K row 8u + l/8 (row offset in soffset), 16-byte chunk
@@ -386,9 +437,9 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         // logical chunk (l%4) ^ ((l/4 >> 1) & 3) of that column
         const int q = (lane & 3) ^ (((lane >> 2) >> 1) & 3);
 #pragma unroll
-        for (int u = 0; u < kBLoadsPerStep; ++u) {
-            const int col = n0 + 16 * u + (lane >> 2);
-            vb[u] = (col < N ? col : n0) * K + 16 * q;
+        for (int uu = 0; uu < kTileLoads; ++uu) {
+            const int col = n0 + 16 * (u0 + uu) + (lane >> 2);
+            vb[uu] = (col < N ? col : n0) * K + 16 * q;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -400,7 +451,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     v16f acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = v16f{};
-    StepRegs regs[kStages];
+    StepRegs regs[D];
 
     auto issue = [&](int ks, int slot) {
         const int k0 = ks * kStepK;
@@ -421,12 +472,13 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         // (the instruction's immediate offset would move both addresses, so
         // each 1 KB destination gets its own LDS pointer)
 #pragma unroll
-        for (int u = 0; u < kBLoadsPerStep; ++u) {
+        for (int uu = 0; uu < kTileLoads; ++uu) {
+            const int u = u0 + uu;
             lds_void_t *dst = (lds_void_t *)(ring + slot * kSlotBytes + u * 1024);
             if (KN)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[0], (k0 + 8 * u) * N, 0, 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[u], k0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[uu], k0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -442,7 +494,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         const char *sl = ring + slot * kSlotBytes;
         if (KN) {
             // operand byte i of lane (c, g) = K row 16g + i + 16*(i >= 16) of the step;
-            // loaded into b[8*(i%4) + i/4] so the transposes leave column j in b[8j..8j+7]
+            // placed in b[8*(i%4) + i/4] so the transposes leave column j in b[8j..8j+7]
             uint32_t b[32];
             {
                 const uint32_t base = lds_addr(sl + (16 * g) * kTileN + 4 * c);
@@ -480,31 +532,44 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     };
 
     // Vector-memory instructions per step, in issue order: x1 (2), x1 scale
-    // (1), weight scales (1 or 4), weight tile (8).  Every iteration issues
-    // the same groups (past the last step the last step is re-read; those are
-    // L2 hits and are never consumed), so the wait for step ks's tile is a
-    // constant: only the kStages - 1 later groups may still be pending.
-    constexpr int kOpsPerStep = 3 + (KN ? 1 : 4) + kBLoadsPerStep;
-    static_assert((kStages - 1) * kOpsPerStep < 64, "vmcnt range");
+    // (1), weight scales (1 or 4), weight tile (all 8, or this wave's 2).
+    // Every iteration issues the same groups (past the last step the last
+    // step is re-read; those are L2 hits and are never consumed), so the wait
+    // for step i is a constant count of later groups allowed to be pending:
+    //   wave mode:  issue(i + D - 1); wait (D - 1 later groups); compute(i)
+    //   coop mode:  wait (D - 2 later groups); s_barrier; issue(i + D - 1)
+    //               into the slot of step i - 1; compute(i)
+    constexpr int kOpsPerStep = 3 + (KN ? 1 : 4) + kTileLoads;
+    constexpr int kPending = (COOP ? D - 2 : D - 1) * kOpsPerStep;
+    static_assert(kPending < 64, "vmcnt range");
     const int n_steps = ks1 - ks0;
     auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
 
 #pragma unroll
-    for (int d = 0; d < kStages - 1; ++d) issue(step_of(d), d);
-    for (int i0 = 0; i0 < n_steps; i0 += kStages) {
+    for (int d = 0; d < D - 1; ++d) issue(step_of(d), d);
+    for (int i0 = 0; i0 < n_steps; i0 += D) {
 #pragma unroll
-        for (int d = 0; d < kStages; ++d) {
-            // refill the slot consumed by the previous step
-            issue(step_of(i0 + d + kStages - 1), (d + kStages - 1) % kStages);
-            wait_vmcnt<(kStages - 1) * kOpsPerStep>();
+        for (int d = 0; d < D; ++d) {
+            if (COOP) {
+                wait_vmcnt<kPending>();
+                __builtin_amdgcn_s_barrier();
+                issue(step_of(i0 + d + D - 1), (d + D - 1) % D);
+            } else {
+                // refill the slot consumed by the previous step
+                issue(step_of(i0 + d + D - 1), (d + D - 1) % D);
+                wait_vmcnt<kPending>();
+            }
             __builtin_amdgcn_sched_barrier(0);
             compute(d, i0 + d < n_steps, step_of(i0 + d));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // Drain the trailing re-reads before the ring is reused.
+    // Drain the trailing re-reads before the ring is reused (in cooperative
+    // mode the staging areas overlap the shared ring: every wave must be done
+    // reading it and every wave's trailing loads must have landed).
     wait_vmcnt<0>();
-    epilogue(p, acc, m0, mcount, n0, KN, store_rows, ring);
+    if (COOP && KN) __syncthreads();
+    epilogue(p, acc, m0, mcount, n0, KN, store_rows, stage);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
@@ -538,57 +603,88 @@ __device__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) 
     }
 }
 
-// One block per CU (the four weight rings fill most of the 160 KB of LDS).
+// One block per CU (the weight rings fill most of the 160 KB of LDS).
+//
+// Work is dealt in block units.  First come the cooperative units of the
+// large experts (expert, 128-row group, 128-column tile, K split); then the
+// wave items of the small experts (expert, 32-row tile, 128-column tile, K
+// split), four consecutive ones per unit, one per wave.  Blocks take units
+// round-robin, numbered so that consecutive units (which share weight bands,
+// x1 rows and scales) land on the same XCD and share its L2.
 template <int FMT, bool TRANS>
 __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) {
     __shared__ int s_start[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_pref[kMaxExperts + 1];
+    __shared__ int s_spref[kMaxExperts + 1];
+    __shared__ int s_lpref[kMaxExperts + 1];
     __shared__ int64_t s_scan[kBlockThreads];
-    __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock][kRingBytes];
+    __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock * kRingBytes];
 
     const int n_tiles = (p.N + kTileN - 1) / kTileN;
-    WorkList wl{s_start, s_cnt, s_pref, 0, 0};
+    WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
     build_work_list(p, n_tiles, wl, s_scan);
     if (p.det_total && blockIdx.x == 0 && threadIdx.x == 0) *p.det_total = wl.routed_tokens;
 
     const bool store_rows = p.wbuf != nullptr;
     const int k_steps = p.K / kStepK;
+    const int blocks = gridDim.x;
     int S = p.split_k;
-    const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    const int base_units = wl.litems + (wl.sitems + kWavesPerBlock - 1) / kWavesPerBlock;
     if (store_rows) {
         S = 1;
     } else if (S <= 0) {
-        // Enough K splits to give every wave a routed item (long K runs per
-        // wave stream best, and every split adds a set of atomics), keeping
-        // >= 8 K steps each.
-        S = wl.items > 0 ? static_cast<int>(waves / wl.items) : 1;
+        // Enough K splits to give every block a unit (long K runs stream
+        // best, and every split adds a set of atomics), keeping >= 8 K steps
+        // each.
+        S = base_units > 0 ? blocks / base_units : 1;
         S = S < k_steps / 8 ? S : k_steps / 8;
         S = S > 1 ? S : 1;
     }
     S = S < k_steps ? S : k_steps;
-    const int64_t routed = static_cast<int64_t>(wl.items) * S;
+    const int64_t coop_units = static_cast<int64_t>(wl.litems) * S;
+    const int64_t wave_items = static_cast<int64_t>(wl.sitems) * S;
+    const int64_t units = coop_units + (wave_items + kWavesPerBlock - 1) / kWavesPerBlock;
 
     // Everything that selects a work item is wave-uniform; readfirstlane makes
     // that visible to the compiler so buffer descriptors and row offsets live
     // in SGPRs (otherwise each buffer load becomes a waterfall loop).
-    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Workgroups are dealt to the 8 XCDs round-robin; number the waves so that
-    // consecutive items (the n-tiles and m-tiles of one expert, which share x1
-    // rows and scales) run on the same XCD and share its L2.
-    const int64_t wave_id =
-        (gridDim.x % 8 == 0)
-            ? ((static_cast<int64_t>(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) *
-                   kWavesPerBlock + wave_in_block)
-            : static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
-    if (p.shared && !store_rows) shared_slice(p, wave_id, waves);
-    for (int64_t it = wave_id; it < routed; it += waves) {
-        {
-            const int q = static_cast<int>(it / S);
-            const int e = __builtin_amdgcn_readfirstlane(find_expert(s_pref, p.E, q));
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Workgroups are dealt to the 8 XCDs round-robin.
+    const int64_t block_id =
+        (blocks % 8 == 0) ? static_cast<int64_t>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
+                          : blockIdx.x;
+    const int64_t waves = static_cast<int64_t>(blocks) * kWavesPerBlock;
+    if (p.shared && !store_rows) shared_slice(p, block_id * kWavesPerBlock + w, waves);
+
+    for (int64_t u = block_id; u < units; u += blocks) {
+        __syncthreads();   // the previous unit's waves are done with the LDS
+        if (u < coop_units) {
+            const int q = static_cast<int>(u / S);
+            const int e = __builtin_amdgcn_readfirstlane(find_expert(s_lpref, p.E, q));
             const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
-            const int e_pref = __builtin_amdgcn_readfirstlane(s_pref[e]);
+            const int e_pref = __builtin_amdgcn_readfirstlane(s_lpref[e]);
+            const int mg_count = (e_cnt + kCoopRows - 1) / kCoopRows;
+            const int64_t local = u - static_cast<int64_t>(e_pref) * S;
+            const int mg = static_cast<int>(local % mg_count);
+            const int64_t rest = local / mg_count;
+            const int s = static_cast<int>(rest % S);
+            const int nt = static_cast<int>(rest / S);
+            const int row0 = mg * kCoopRows + w * kTileM;   // this wave's rows
+            const int mcount = min(kTileM, e_cnt - row0);
+            const int m0 = e_start + (mcount > 0 ? row0 : 0);
+            const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
+            const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
+            routed_item<FMT, !TRANS, true>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows,
+                                           s_ring, s_ring + w * (kTileM * kTileN * 4), w);
+        } else {
+            const int64_t it = (u - coop_units) * kWavesPerBlock + w;
+            if (it >= wave_items) continue;
+            const int q = static_cast<int>(it / S);
+            const int e = __builtin_amdgcn_readfirstlane(find_expert(s_spref, p.E, q));
+            const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
+            const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
+            const int e_pref = __builtin_amdgcn_readfirstlane(s_spref[e]);
             const int mt_count = (e_cnt + kTileM - 1) / kTileM;
             const int64_t local = it - static_cast<int64_t>(e_pref) * S;
             const int mt = static_cast<int>(local % mt_count);
@@ -599,8 +695,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int mcount = min(kTileM, e_cnt - mt * kTileM);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            routed_item<FMT, !TRANS>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows,
-                                     s_ring[wave_in_block]);
+            char *own = s_ring + w * kRingBytes;
+            routed_item<FMT, !TRANS, false>(p, e, m0, mcount, nt * kTileN, ks0, ks1,
+                                            store_rows, own, own, w);
         }
     }
 }

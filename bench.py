@@ -37,7 +37,32 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the operator, run a plain 1 GiB device-to-device copy per "
+                         "step (the known-size reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(args):
+    """Plain copy of a known size: each step reads and writes exactly 1 GiB."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n,
+                      "steps": args.steps, "ms_per_copy": round(ms, 5),
+                      "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -81,8 +106,12 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this operator is "
               "built and measured on a single MI355X", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
     import torch
     import mxfp8_grouped_gemm_group_amd as gfr
+    from mxfp8_grouped_gemm_group_amd import traffic as traffic_mod
     from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_inputs
 
     gfr.load_library()
@@ -135,10 +164,11 @@ def main():
     alg_bytes = w.algorithmic_bytes()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    # HBM bytes per launch from rocprofv3 counters of this very kernel source
+    # (null when the kernel changed after the counters were taken)
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
-    if os.path.exists(tfile) and not args.deterministic:
-        traffic = json.load(open(tfile)).get("bytes_per_launch")
+    if not args.deterministic and args.split_k == 0:
+        traffic = traffic_mod.recorded_traffic(w.name)
 
     line = {
         "metric": "effective TFLOP/s (2*M*K*N/t) + % of binding roofline, M=768 K=8192 N=4096 E=32",

@@ -1,0 +1,117 @@
+"""HBM traffic of the fused kernel from rocprofv3 counters.
+
+rocprofv3's derived counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
+read for the fused kernel and for a plain device copy of known size (1 GiB read
++ 1 GiB written per dispatch, ``bench.py --copy-calibration``).  The copy gives
+the scale of each counter on this part (bytes the counter reports per byte
+actually moved); the kernel's counts are divided by it:
+
+    traffic = FETCH_SIZE(kernel) / (FETCH_SIZE(copy) / 1 GiB)
+            + WRITE_SIZE(kernel) / (WRITE_SIZE(copy) / 1 GiB)
+
+Collection (four counter runs, each its own process; see the profiles folder
+for the exact commands):
+
+    rocprofv3 --pmc FETCH_SIZE -d DIR/copy_fetch  -o p --output-format csv -- python bench.py --copy-calibration --steps 3 --warmup 1
+    rocprofv3 --pmc WRITE_SIZE -d DIR/copy_write  -o p --output-format csv -- python bench.py --copy-calibration --steps 3 --warmup 1
+    rocprofv3 --pmc FETCH_SIZE -d DIR/W_fetch     -o p --output-format csv -- python bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc WRITE_SIZE -d DIR/W_write     -o p --output-format csv -- python bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline
+    python -m mxfp8_grouped_gemm_group_amd.traffic DIR W
+
+The result goes to ``profiles/traffic_W.json`` together with a hash of the
+kernel source it was measured on; ``recorded_traffic`` returns None once the
+source has changed.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_PKG)
+_KERNEL_SRC = os.path.join(_PKG, "csrc", "gfr_kernels.hip")
+GIB = 1 << 30
+
+
+def kernel_hash() -> str:
+    with open(_KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _per_dispatch(run_dir: str, counter: str, name_part: str):
+    """Counter value (summed over its dimensions) of every dispatch whose kernel
+    name contains name_part, in dispatch order."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+                    continue
+                k = int(r["Dispatch_Id"])
+                per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def _steady(values):
+    """Mean over the dispatches after the first (the first one warms caches)."""
+    if not values:
+        raise ValueError("no matching dispatches")
+    v = values[1:] if len(values) > 1 else values
+    return sum(v) / len(v)
+
+
+def compute(run_dir: str, workload: str) -> dict:
+    copy_kernel = "copy"   # torch's device copy kernels carry "copy" in their names
+    f_copy = _steady(_per_dispatch(os.path.join(run_dir, "copy_fetch"), "FETCH_SIZE", copy_kernel))
+    w_copy = _steady(_per_dispatch(os.path.join(run_dir, "copy_write"), "WRITE_SIZE", copy_kernel))
+    f_k = _steady(_per_dispatch(os.path.join(run_dir, f"{workload}_fetch"), "FETCH_SIZE", "fused_kernel"))
+    w_k = _steady(_per_dispatch(os.path.join(run_dir, f"{workload}_write"), "WRITE_SIZE", "fused_kernel"))
+    f_scale = f_copy * 1024 / GIB      # counter bytes per real byte read
+    w_scale = w_copy * 1024 / GIB
+    read_b = f_k * 1024 / f_scale
+    write_b = w_k * 1024 / w_scale
+    return {
+        "workload": workload,
+        "kernel": "fused_kernel",
+        "kernel_source_sha256_16": kernel_hash(),
+        "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "kernel_fetch_kib": f_k, "kernel_write_kib": w_k,
+        "bytes_read": read_b, "bytes_written": write_b,
+        "bytes_per_launch": read_b + write_b,
+    }
+
+
+def recorded_traffic(workload: str) -> Optional[float]:
+    fn = os.path.join(_ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main(argv):
+    if len(argv) != 3:
+        print("usage: python -m mxfp8_grouped_gemm_group_amd.traffic RUN_DIR WORKLOAD", file=sys.stderr)
+        return 2
+    d = compute(argv[1], argv[2])
+    out = os.path.join(_ROOT, "profiles", f"traffic_{argv[2]}.json")
+    with open(out, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

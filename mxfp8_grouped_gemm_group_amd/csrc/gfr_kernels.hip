@@ -47,6 +47,18 @@ __device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
     return *reinterpret_cast<const uint32_t *>(p);
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Raw buffer resource over [base, base + bytes); the wave-uniform base and
+// row offsets live in SGPRs, each lane keeps one 32-bit offset.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
 // In-register 4x4 byte transpose: on entry w_r holds bytes (r, 0..3) of a
 // 4x4 byte block, on exit w_c holds bytes (0..3, c).
 __device__ __forceinline__ void transpose4x4(uint32_t &w0, uint32_t &w1, uint32_t &w2,
@@ -110,20 +122,29 @@ constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 __device__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
                                 int64_t *s_scan) {
     const int tid = threadIdx.x;
+    static_assert(kPerThread == 4, "one thread reads 4 consecutive group_list entries");
+    // All loads are issued before any is used (one memory latency, not one per
+    // entry); reads past the list (or of an absent list when M = 0) return 0.
+    const rsrc_t rg = make_rsrc(p.group_list, p.M > 0 ? static_cast<int64_t>(p.E) * 8 : 0);
+    const int e0 = tid * kPerThread;
+    const v4i g01 = __builtin_amdgcn_raw_buffer_load_b128(rg, e0 * 8, 0, 0);
+    const v4i g23 = __builtin_amdgcn_raw_buffer_load_b128(rg, e0 * 8 + 16, 0, 0);
+    const v2i gp = e0 > 0 ? __builtin_amdgcn_raw_buffer_load_b64(rg, e0 * 8 - 8, 0, 0) : v2i{0, 0};
+    auto i64 = [](int lo, int hi) {
+        return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                    static_cast<uint32_t>(lo));
+    };
+    const int64_t g[kPerThread + 1] = {i64(gp.x, gp.y), i64(g01.x, g01.y), i64(g01.z, g01.w),
+                                       i64(g23.x, g23.y), i64(g23.z, g23.w)};
     int c[kPerThread];
     int64_t csum = 0;
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-        const int e = tid * kPerThread + i;
+        const int e = e0 + i;
         int64_t v = 0;
-        if (e < p.E && p.M > 0) {  // with M = 0 group_list may be absent
-            const int64_t g = p.group_list[e];
-            if (p.group_list_type == GFR_GROUP_LIST_COUNT) {
-                v = g;
-            } else {
-                v = g - (e > 0 ? p.group_list[e - 1] : 0);
-            }
+        if (e < p.E && p.M > 0) {
+            v = p.group_list_type == GFR_GROUP_LIST_COUNT ? g[i + 1] : g[i + 1] - g[i];
             if (v < 0) { bad = true; v = 0; }
             if (v > p.M) { bad = true; v = p.M; }
         }
@@ -201,17 +222,6 @@ __device__ __forceinline__ int find_expert(const int *pref, int E, int q) {
 // (each lane loads 4 adjacent columns and transposes them in registers) and
 // n0 + 32j + c for the [N, K] layout.
 // ---------------------------------------------------------------------------
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Raw buffer resource over [base, base + bytes); the wave-uniform base and
-// row offsets live in SGPRs, each lane keeps one 32-bit offset.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
-}
 
 // s_waitcnt vmcnt(N) (other counters untouched), gfx9 encoding.
 template <int N>
@@ -311,15 +321,54 @@ struct StepRegs {
                           // [N,K]: dword holding the scale of column j's block
 };
 
+// Destination row and weight of the tile's 32 rows, loaded when the item
+// starts (their latency hides behind the weight stream): lane l < 32 holds row
+// l's, and the epilogue fetches them with a lane shuffle.  A row past the
+// expert's last token, or with row_index outside [0, batch) (flagged), gets
+// dst = -1 and is skipped.
+struct RowInfo {
+    v2i dst;      // row_index[t] as two dwords (low, high)
+    float w;
+    bool live;    // lane < 32 and the row is one of the expert's tokens
+};
+
+__device__ __forceinline__ RowInfo load_row_info(const FusedParams &p, int m0, int mcount) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    RowInfo ri{v2i{0, 0}, 0.0f, lane < kTileM && lane < mcount};
+    const int cnt = mcount < kTileM ? (mcount > 0 ? mcount : 0) : kTileM;
+    const rsrc_t rr = make_rsrc(p.row_index + m0, static_cast<int64_t>(cnt) * 8);
+    ri.dst = __builtin_amdgcn_raw_buffer_load_b64(rr, 8 * lane, 0, 0);
+    if (p.logit) {
+        const rsrc_t rl = make_rsrc(p.logit + m0, static_cast<int64_t>(cnt) * 4);
+        ri.w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lane, 0, 0));
+    } else {
+        ri.w = 1.0f;
+    }
+    return ri;
+}
+
+// Destination row of each lane's tile row (-1: skip), flagging bad indices.
+__device__ __forceinline__ int row_dst(const FusedParams &p, const RowInfo &ri) {
+    const int64_t d = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(ri.dst.y)) << 32) |
+                                           static_cast<uint32_t>(ri.dst.x));
+    if (!ri.live) return -1;
+    if (d < 0 || d >= p.batch) {
+        flag(p.status, GFR_DEV_BAD_ROW_INDEX);
+        return -1;
+    }
+    return static_cast<int>(d);
+}
+
 // Epilogue: weight each row by its logit and scatter-add (or store) it.
 // acc element (j, r) of lane (c, g) is row 8(r/4) + 4g + r%4 and output column
 // n0 + col_of(c, j).  For the [K,N] layout the accumulator is first staged
 // through the wave's LDS ring so that each atomic covers 32 adjacent columns.
 __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)[4],
-                                         int m0, int mcount, int n0, bool kn_layout,
-                                         bool store_rows, char *ring) {
+                                         int m0, int n0, bool kn_layout, bool store_rows,
+                                         char *ring, RowInfo ri) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
+    const int my_dst = row_dst(p, ri);
     float *stage = reinterpret_cast<float *>(ring);     // [32 rows][128 cols]
     if (kn_layout) {
         wait_lgkmcnt0();
@@ -334,14 +383,10 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row >= mcount) continue;
+        const int dst = __shfl(my_dst, row);
+        const float w = __shfl(ri.w, row);
+        if (dst < 0) continue;
         const int t = m0 + row;
-        const int64_t dst = p.row_index[t];
-        const float w = p.logit ? p.logit[t] : 1.0f;
-        if (dst < 0 || dst >= p.batch) {
-            flag(p.status, GFR_DEV_BAD_ROW_INDEX);
-            continue;
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int col = n0 + 32 * j + c;
@@ -351,7 +396,7 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
             if (store_rows)
                 p.wbuf[static_cast<int64_t>(t) * p.N + col] = v;
             else
-                unsafeAtomicAdd(p.out + dst * p.N + col, v);
+                unsafeAtomicAdd(p.out + static_cast<int64_t>(dst) * p.N + col, v);
         }
     }
 }
@@ -448,6 +493,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         }
     }
 
+    const RowInfo rinfo = load_row_info(p, m0, mcount);
     v16f acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = v16f{};
@@ -569,15 +615,13 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     // reading it and every wave's trailing loads must have landed).
     wait_vmcnt<0>();
     if (COOP && KN) __syncthreads();
-    epilogue(p, acc, m0, mcount, n0, KN, store_rows, stage);
+    epilogue(p, acc, m0, n0, KN, store_rows, stage, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
 // contiguous slice of the R*N elements per wave, so every wave carries the
-// same small share (done before its routed work; the atomics are issued
-// without waiting and drain while the weights stream).  Lane l handles
-// elements 64i + l of the slice: every load and atomic covers 64 adjacent
-// elements.
+// same small share (done after its routed work).  Lane l handles elements
+// 64i + l of the slice: every load and atomic covers 64 adjacent elements.
 __device__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int64_t total = static_cast<int64_t>(p.shared_rows) * p.N;
@@ -588,12 +632,13 @@ __device__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) 
     float *o = p.out + static_cast<int64_t>(p.shared_off) * p.N;
     constexpr int kBatch = 16;   // loads in flight per lane before their atomics
     for (int64_t b = begin; b < end; b += kBatch * kWaveSize) {
+        // a descriptor over the rest of the slice: loads past it return 0
+        const int64_t left = end - b;
+        const rsrc_t rs = make_rsrc(p.shared + b, 2 * (left < kBatch * kWaveSize ? left : kBatch * kWaveSize));
         uint16_t h[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int64_t e = b + i * kWaveSize + lane;
-            h[i] = e < end ? p.shared[e] : 0;
-        }
+        for (int i = 0; i < kBatch; ++i)
+            h[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * (i * kWaveSize + lane), 0, 0);
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int64_t e = b + i * kWaveSize + lane;
@@ -609,8 +654,7 @@ __device__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) 
 // large experts (expert, 128-row group, 128-column tile, K split); then the
 // wave items of the small experts (expert, 32-row tile, 128-column tile, K
 // split), four consecutive ones per unit, one per wave.  Blocks take units
-// round-robin, numbered so that consecutive units (which share weight bands,
-// x1 rows and scales) land on the same XCD and share its L2.
+// round-robin.
 template <int FMT, bool TRANS>
 __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) {
     __shared__ int s_start[kMaxExperts];
@@ -649,12 +693,12 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
     // that visible to the compiler so buffer descriptors and row offsets live
     // in SGPRs (otherwise each buffer load becomes a waterfall loop).
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Workgroups are dealt to the 8 XCDs round-robin.
-    const int64_t block_id =
-        (blocks % 8 == 0) ? static_cast<int64_t>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
-                          : blockIdx.x;
+    // Units go to workgroups in plain index order.  (Workgroups are dealt to
+    // the 8 XCDs round-robin; keeping neighbouring units on one XCD for L2
+    // sharing measured slower: the weight stream loses more than the few
+    // shared x1 / scale lines gain.)
+    const int64_t block_id = blockIdx.x;
     const int64_t waves = static_cast<int64_t>(blocks) * kWavesPerBlock;
-    if (p.shared && !store_rows) shared_slice(p, block_id * kWavesPerBlock + w, waves);
 
     for (int64_t u = block_id; u < units; u += blocks) {
         __syncthreads();   // the previous unit's waves are done with the LDS
@@ -700,6 +744,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
                                             store_rows, own, own, w);
         }
     }
+    // The shared-expert term last: at the start its loads would delay the
+    // first weight loads by a memory latency.
+    if (p.shared && !store_rows) shared_slice(p, block_id * kWavesPerBlock + w, waves);
 }
 
 // ---------------------------------------------------------------------------

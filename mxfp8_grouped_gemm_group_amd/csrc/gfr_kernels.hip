@@ -10,12 +10,13 @@
 //   * prologue — every workgroup turns group_list into per-expert token ranges
 //     and a prefix of work items in LDS (no host round trip; ragged and empty
 //     experts cost nothing);
-//   * routed items — (expert, 32-token m-tile, 128-column n-tile, K split),
-//     one per wave.  x2 and x1 go global -> VGPR with a 3-deep software
-//     pipeline; the [K, N] weight layout is byte-transposed in registers
-//     (v_perm) into the K-contiguous operand the MFMA wants; the contraction is
-//     v_mfma_scale_f32_32x32x64_f8f6f4 with the E8M0 scales fed per lane (one
-//     scale per 32 K elements of one row / column);
+//   * routed items — (expert, 32-token m-tile, 128-column n-tile, K split)
+//     per wave, or (expert, 128-token group, n-tile, K split) per workgroup
+//     for large experts.  Weight tiles stream global -> LDS ring with
+//     direct-to-LDS buffer loads, x1 and the scales go to VGPRs; the [K, N]
+//     layout is read out of LDS K-contiguous with transpose reads; the
+//     contraction is v_mfma_scale_f32_32x32x64_f8f6f4 with the E8M0 scales fed
+//     per lane (one scale per 32 K elements of one row / column);
 //   * epilogue — acc * logit, then FP32 atomic add into out[row_index[t], n]
 //     (or, in deterministic mode, a plain store of the weighted row);
 //   * shared items — the bf16 shared-expert axpy, atomically, same launch.
@@ -57,21 +58,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
     const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
-}
-
-// In-register 4x4 byte transpose: on entry w_r holds bytes (r, 0..3) of a
-// 4x4 byte block, on exit w_c holds bytes (0..3, c).
-__device__ __forceinline__ void transpose4x4(uint32_t &w0, uint32_t &w1, uint32_t &w2,
-                                             uint32_t &w3) {
-    // v_perm_b32(a, b, sel): selector byte 0-3 picks a byte of b, 4-7 of a.
-    const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
-    const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
-    const uint32_t t2 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
-    const uint32_t t3 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // w2.2 w3.2 w2.3 w3.3
-    w0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);                 // w0.0 w1.0 w2.0 w3.0
-    w1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);                 // w0.1 w1.1 w2.1 w3.1
-    w2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);                 // w0.2 ...
-    w3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);                 // w0.3 ...
 }
 
 __device__ __forceinline__ void flag(int32_t *status, int32_t bit) {
@@ -243,32 +229,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
 }
 
-// 16 dwords at addr + O0 + 128 * i, i = 0..15 (one K row each of the [K, N]
-// tile).
-template <int O0>
-__device__ __forceinline__ void lds_read_16rows(uint32_t addr, uint32_t (&v)[16]) {
+// The [K, N] tile's MFMA operand for one 32-column group: four
+// ds_read_b64_tr_b8 (gfx950 LDS transpose read).  Measured semantics: in each
+// group of 16 lanes, output lane 8h + j receives byte j of the 8-byte rows
+// addressed by lanes 2i + h, i = 0..7, as its bytes i.  So if lane 2i + h of
+// the group points at K row k0 + i, columns c0 + 8h .. c0 + 8h + 7, lane 8h + j
+// gets K rows k0 .. k0 + 7 of column c0 + 8h + j: 8 bytes of its operand.
+// The four reads at addr + Q0..Q3 give operand bytes 0-7, 8-15, 16-23, 24-31.
+// Inline asm for the same reason as above, ending in lgkmcnt(0).
+template <int Q0, int Q1, int Q2, int Q3>
+__device__ __forceinline__ void lds_read_tr_kn(uint32_t addr, v2i (&v)[4]) {
     asm volatile(
-        "ds_read_b32 %0, %16 offset:%17\n\t"
-        "ds_read_b32 %1, %16 offset:%17+128\n\t"
-        "ds_read_b32 %2, %16 offset:%17+256\n\t"
-        "ds_read_b32 %3, %16 offset:%17+384\n\t"
-        "ds_read_b32 %4, %16 offset:%17+512\n\t"
-        "ds_read_b32 %5, %16 offset:%17+640\n\t"
-        "ds_read_b32 %6, %16 offset:%17+768\n\t"
-        "ds_read_b32 %7, %16 offset:%17+896\n\t"
-        "ds_read_b32 %8, %16 offset:%17+1024\n\t"
-        "ds_read_b32 %9, %16 offset:%17+1152\n\t"
-        "ds_read_b32 %10, %16 offset:%17+1280\n\t"
-        "ds_read_b32 %11, %16 offset:%17+1408\n\t"
-        "ds_read_b32 %12, %16 offset:%17+1536\n\t"
-        "ds_read_b32 %13, %16 offset:%17+1664\n\t"
-        "ds_read_b32 %14, %16 offset:%17+1792\n\t"
-        "ds_read_b32 %15, %16 offset:%17+1920\n\t"
+        "ds_read_b64_tr_b8 %0, %4 offset:%5\n\t"
+        "ds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b8 %2, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b8 %3, %4 offset:%8\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
-          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-        : "v"(addr), "i"(O0)
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(addr), "i"(Q0), "i"(Q1), "i"(Q2), "i"(Q3)
         : "memory");
 }
 
@@ -308,7 +286,6 @@ constexpr int kStages = 4;
 constexpr int kSlotBytes = kStepK * kTileN;            // 8 KB
 constexpr int kRingBytes = kStages * kSlotBytes;       // 32 KB per wave
 constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
-static_assert(kRingBytes >= kTileM * kTileN * 4, "epilogue staging reuses the ring");
 
 // Registers that travel with one K step (the weight tile itself is in LDS).
 // Scales are loaded as the aligned dword that holds them and the byte is
@@ -317,8 +294,7 @@ static_assert(kRingBytes >= kTileM * kTileN * 4, "epilogue staging reuses the ri
 struct StepRegs {
     v4i alo, ahi;         // x1 row: K [16g, +16) and K [32 + 16g, +16) of the step
     uint32_t sa;          // dword holding the x1 scale of 32-block 2ks + g
-    uint32_t sb[4];       // [K,N]: sb[0..1] = 8 bytes, 4 cols x 2 halves;
-                          // [N,K]: dword holding the scale of column j's block
+    uint32_t sb[4];       // dword holding the scale byte of column group j
 };
 
 // Destination row and weight of the tile's 32 rows, loaded when the item
@@ -361,25 +337,12 @@ __device__ __forceinline__ int row_dst(const FusedParams &p, const RowInfo &ri) 
 
 // Epilogue: weight each row by its logit and scatter-add (or store) it.
 // acc element (j, r) of lane (c, g) is row 8(r/4) + 4g + r%4 and output column
-// n0 + col_of(c, j).  For the [K,N] layout the accumulator is first staged
-// through the wave's LDS ring so that each atomic covers 32 adjacent columns.
+// n0 + 32j + c, so each atomic instruction covers 32 adjacent columns.
 __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)[4],
-                                         int m0, int n0, bool kn_layout, bool store_rows,
-                                         char *ring, RowInfo ri) {
+                                         int m0, int n0, bool store_rows, RowInfo ri) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
     const int my_dst = row_dst(p, ri);
-    float *stage = reinterpret_cast<float *>(ring);     // [32 rows][128 cols]
-    if (kn_layout) {
-        wait_lgkmcnt0();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-            float4 v = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
-            *reinterpret_cast<float4 *>(stage + row * kTileN + 4 * c) = v;  // cols 4c..4c+3
-        }
-        wait_lgkmcnt0();
-    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * g + (r & 3);
@@ -391,8 +354,7 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
         for (int j = 0; j < 4; ++j) {
             const int col = n0 + 32 * j + c;
             if (col >= p.N) continue;
-            const float a = kn_layout ? stage[row * kTileN + 32 * j + c] : acc[j][r];
-            const float v = a * w;
+            const float v = acc[j][r] * w;
             if (store_rows)
                 p.wbuf[static_cast<int64_t>(t) * p.N + col] = v;
             else
@@ -417,9 +379,10 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
 //     and applies the tile to its own 32 rows (rows 32w.. of a 128-row
 //     group); one s_barrier per step publishes the tile and retires the slot
 //     that is refilled next.
-// [K, N]: the slot is row-major [64 K rows][128 cols]; lane (c, g) reads the
-//   dword (4 columns) of each of its 32 K rows and byte-transposes in
-//   registers; operand byte i is K row 16g + i + 16*(i >= 16) of the step.
+// [K, N]: the slot is row-major [64 K rows][128 B] with the eight 16-byte
+//   chunks of row r XOR-swizzled by (r >> 1) & 3 (the transpose reads of a
+//   16-lane group then hit distinct banks); the operand comes out of LDS
+//   already K-contiguous per column (ds_read_b64_tr_b8).
 // [N, K]: the slot is [128 cols][64 K bytes] with the four 16-byte chunks of
 //   a column XOR-swizzled by (col >> 1) & 3 so that 16-byte LDS reads of 32
 //   lanes do not collide on banks.
@@ -429,13 +392,10 @@ constexpr int kCoopStagesNK = 8;
 static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
                   kCoopStagesNK * kSlotBytes <= kWavesPerBlock * kRingBytes,
               "cooperative ring fits the block's LDS");
-static_assert(kWavesPerBlock * kTileM * kTileN * 4 <= kWavesPerBlock * kRingBytes,
-              "per-wave epilogue staging fits the block's LDS");
 
 template <int FMT, bool KN, bool COOP>
 __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
-                            int ks0, int ks1, bool store_rows, char *ring, char *stage,
-                            int w) {
+                            int ks0, int ks1, bool store_rows, char *ring, int w) {
     constexpr int D = COOP ? (KN ? kCoopStagesKN : kCoopStagesNK) : kStages;
     constexpr int kTileLoads = COOP ? kBLoadsPerStep / kWavesPerBlock : kBLoadsPerStep;
     // The item is wave-uniform; say so, so that descriptors and offsets stay
@@ -469,14 +429,28 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     // written.
     int vb[KN ? 1 : kTileLoads];
     int vsb[4];
+    uint32_t tr_addr[4] = {0, 0, 0, 0};   // [K,N]: per 32-column group, slot-relative
+    int sb_shift = 0;
     if (KN) {
-        // load u, lane l: K row 8u + l/8 (row offset in soffset), 16-byte chunk
-        // l%8 of the 128 columns
-        const int chunk_col = n0 + 16 * (lane & 7);
+        // load u, lane l: K row r = 8u + l/8 (row offset in soffset); it fills
+        // physical chunk l%8 of the slot row, which holds logical chunk
+        // (l%8) ^ ((r >> 1) & 3) = (l%8) ^ ((l >> 4) & 3)
+        const int chunk_col = n0 + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
         vb[0] = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
-        const int col = n0 + 4 * c;                 // the lane's 4 operand columns
-        vsb[0] = (col < N ? col : n0) * 2;
-        vsb[1] = vsb[2] = vsb[3] = 0;
+        // transpose reads: lane s of 16-lane group G reads K row
+        // 16g + (s >> 1) + (read's K offset), columns 32j + 16(G & 1) + 8(s & 1)
+        const int G = lane >> 4, sl = lane & 15, i = sl >> 1, h = sl & 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            tr_addr[j] = (16 * g + i) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((i >> 1) & 3)) + 8 * h;
+        // scale byte (ks, col, g) is byte 2 col + g of row ks of [K/64, N, 2];
+        // the aligned dword holds columns col & ~1 and col | 1
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + 32 * j + c;
+            vsb[j] = ((col < N ? col : n0) & ~1) * 2;
+        }
+        sb_shift = 8 * (2 * (c & 1) + g);
     } else {
         // load u, lane l: column 16u + l/4; physical chunk l%4 of the slot holds
         // logical chunk (l%4) ^ ((l/4 >> 1) & 3) of that column
@@ -506,15 +480,10 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         r.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
         r.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
         r.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, (2 * ks) & ~3, 0);
-        if (KN) {
-            const v2i sb = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[0], ks * 2 * N, 0);
-            r.sb[0] = sb.x;
-            r.sb[1] = sb.y;
-        } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                r.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], (2 * ks) & ~3, 0);
-        }
+        for (int j = 0; j < 4; ++j)
+            r.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
+                                                           KN ? ks * 2 * N : (2 * ks) & ~3, 0);
         // (the instruction's immediate offset would move both addresses, so
         // each 1 KB destination gets its own LDS pointer)
 #pragma unroll
@@ -539,33 +508,16 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         const uint32_t sa = r.sa >> sh;
         const char *sl = ring + slot * kSlotBytes;
         if (KN) {
-            // operand byte i of lane (c, g) = K row 16g + i + 16*(i >= 16) of the step;
-            // placed in b[8*(i%4) + i/4] so the transposes leave column j in b[8j..8j+7]
-            uint32_t b[32];
-            {
-                const uint32_t base = lds_addr(sl + (16 * g) * kTileN + 4 * c);
-                uint32_t r0[16], r1[16];
-                lds_read_16rows<0>(base, r0);                 // operand bytes 0..15
-                lds_read_16rows<32 * kTileN>(base, r1);       // operand bytes 16..31
+            const uint32_t base = lds_addr(sl);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    b[8 * (i & 3) + (i >> 2)] = r0[i];
-                    b[8 * (i & 3) + ((i + 16) >> 2)] = r1[i];
-                }
+            for (int j = 0; j < 4; ++j) {
+                // operand bytes 0-7, 8-15: K rows 16g + [0, 16); 16-23, 24-31:
+                // K rows 32 + 16g + [0, 16)
+                v2i t[4];
+                lds_read_tr_kn<0, 8 * kTileN, 32 * kTileN, 40 * kTileN>(base + tr_addr[j], t);
+                const v8i b = {t[0].x, t[0].y, t[1].x, t[1].y, t[2].x, t[2].y, t[3].x, t[3].y};
+                acc[j] = mfma<FMT, 0>(a, b, acc[j], sa, r.sb[j] >> sb_shift);
             }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) transpose4x4(b[q], b[8 + q], b[16 + q], b[24 + q]);
-            const uint32_t s01 = r.sb[0] >> (8 * g);   // byte 0: col 0, byte 2: col 1
-            const uint32_t s23 = r.sb[1] >> (8 * g);   // byte 0: col 2, byte 2: col 3
-            v8i bt[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 8; ++q) bt[j][q] = b[8 * j + q];
-            acc[0] = mfma<FMT, 0>(a, bt[0], acc[0], sa, s01);
-            acc[1] = mfma<FMT, 2>(a, bt[1], acc[1], sa, s01);
-            acc[2] = mfma<FMT, 0>(a, bt[2], acc[2], sa, s23);
-            acc[3] = mfma<FMT, 2>(a, bt[3], acc[3], sa, s23);
         } else {
             const int f = (c >> 1) & 3;
             v4i lo[4], hi[4];
@@ -578,14 +530,14 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     };
 
     // Vector-memory instructions per step, in issue order: x1 (2), x1 scale
-    // (1), weight scales (1 or 4), weight tile (all 8, or this wave's 2).
+    // (1), weight scales (4), weight tile (all 8, or this wave's 2).
     // Every iteration issues the same groups (past the last step the last
     // step is re-read; those are L2 hits and are never consumed), so the wait
     // for step i is a constant count of later groups allowed to be pending:
     //   wave mode:  issue(i + D - 1); wait (D - 1 later groups); compute(i)
     //   coop mode:  wait (D - 2 later groups); s_barrier; issue(i + D - 1)
     //               into the slot of step i - 1; compute(i)
-    constexpr int kOpsPerStep = 3 + (KN ? 1 : 4) + kTileLoads;
+    constexpr int kOpsPerStep = 3 + 4 + kTileLoads;
     constexpr int kPending = (COOP ? D - 2 : D - 1) * kOpsPerStep;
     static_assert(kPending < 64, "vmcnt range");
     const int n_steps = ks1 - ks0;
@@ -614,8 +566,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     // mode the staging areas overlap the shared ring: every wave must be done
     // reading it and every wave's trailing loads must have landed).
     wait_vmcnt<0>();
-    if (COOP && KN) __syncthreads();
-    epilogue(p, acc, m0, n0, KN, store_rows, stage, rinfo);
+    epilogue(p, acc, m0, n0, store_rows, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
@@ -720,7 +671,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             routed_item<FMT, !TRANS, true>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows,
-                                           s_ring, s_ring + w * (kTileM * kTileN * 4), w);
+                                           s_ring, w);
         } else {
             const int64_t it = (u - coop_units) * kWavesPerBlock + w;
             if (it >= wave_items) continue;
@@ -741,7 +692,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
             routed_item<FMT, !TRANS, false>(p, e, m0, mcount, nt * kTileN, ks0, ks1,
-                                            store_rows, own, own, w);
+                                            store_rows, own, w);
         }
     }
     // The shared-expert term last: at the start its loads would delay the

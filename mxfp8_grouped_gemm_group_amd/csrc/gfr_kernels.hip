@@ -219,40 +219,55 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// LDS reads of the weight tile.  They are issued as inline asm because the
-// compiler's wait insertion cannot tell which direct-to-LDS load wrote which
-// slot and would otherwise drain every outstanding load before the read; the
-// explicit vmcnt wait before them orders the data.  Each asm block ends with
-// s_waitcnt lgkmcnt(0), so no consumer can be scheduled before the data is in
-// its registers.
+// LDS reads of the weight tile.  They are inline asm because the compiler's
+// wait insertion cannot tell which direct-to-LDS load wrote which slot and
+// would otherwise drain every outstanding load before each read; the explicit
+// vmcnt wait before them orders the data.  The reads of a step are issued
+// without waiting; lds_wait() waits for them and, since it takes the
+// destination registers as in/out operands, nothing that uses them can be
+// scheduled before it.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
 }
 
-// The [K, N] tile's MFMA operand for one 32-column group: four
-// ds_read_b64_tr_b8 (gfx950 LDS transpose read).  Measured semantics: in each
-// group of 16 lanes, output lane 8h + j receives byte j of the 8-byte rows
-// addressed by lanes 2i + h, i = 0..7, as its bytes i.  So if lane 2i + h of
-// the group points at K row k0 + i, columns c0 + 8h .. c0 + 8h + 7, lane 8h + j
-// gets K rows k0 .. k0 + 7 of column c0 + 8h + j: 8 bytes of its operand.
-// The four reads at addr + Q0..Q3 give operand bytes 0-7, 8-15, 16-23, 24-31.
-// Inline asm for the same reason as above, ending in lgkmcnt(0).
-template <int Q0, int Q1, int Q2, int Q3>
-__device__ __forceinline__ void lds_read_tr_kn(uint32_t addr, v2i (&v)[4]) {
-    asm volatile(
-        "ds_read_b64_tr_b8 %0, %4 offset:%5\n\t"
-        "ds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b8 %2, %4 offset:%7\n\t"
-        "ds_read_b64_tr_b8 %3, %4 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-        : "v"(addr), "i"(Q0), "i"(Q1), "i"(Q2), "i"(Q3)
-        : "memory");
+// The [K, N] tile's MFMA operands of one step: ds_read_b64_tr_b8 (gfx950 LDS
+// transpose read).  Measured semantics: in each group of 16 lanes, output lane
+// 8h + j receives byte j of the 8-byte rows addressed by lanes 2i + h,
+// i = 0..7, as its bytes i.  So if lane 2i + h of the group points at K row
+// k0 + i, columns c0 + 8h .. c0 + 8h + 7, lane 8h + j gets K rows k0 .. k0 + 7
+// of column c0 + 8h + j: 8 bytes of its operand.  For 32-column group j the
+// reads at a[j] + {0, 8, 32, 40} rows give operand bytes 0-7, 8-15, 16-23,
+// 24-31 (t[4j + q]).
+#define GFR_TR4(J)                                              \
+    "ds_read_b64_tr_b8 %[t" #J "0], %[a" #J "]\n\t"             \
+    "ds_read_b64_tr_b8 %[t" #J "1], %[a" #J "] offset:1024\n\t" \
+    "ds_read_b64_tr_b8 %[t" #J "2], %[a" #J "] offset:4096\n\t" \
+    "ds_read_b64_tr_b8 %[t" #J "3], %[a" #J "] offset:5120\n\t"
+__device__ __forceinline__ void lds_issue_kn(const uint32_t (&a)[4], v2i (&t)[16]) {
+    static_assert(8 * kTileN == 1024 && 32 * kTileN == 4096 && 40 * kTileN == 5120,
+                  "row offsets of the four reads");
+    asm volatile(GFR_TR4(0) GFR_TR4(1) GFR_TR4(2) GFR_TR4(3)
+                 : [t00] "=&v"(t[0]), [t01] "=&v"(t[1]), [t02] "=&v"(t[2]), [t03] "=&v"(t[3]),
+                   [t10] "=&v"(t[4]), [t11] "=&v"(t[5]), [t12] "=&v"(t[6]), [t13] "=&v"(t[7]),
+                   [t20] "=&v"(t[8]), [t21] "=&v"(t[9]), [t22] "=&v"(t[10]), [t23] "=&v"(t[11]),
+                   [t30] "=&v"(t[12]), [t31] "=&v"(t[13]), [t32] "=&v"(t[14]), [t33] "=&v"(t[15])
+                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3])
+                 : "memory");
+}
+#undef GFR_TR4
+
+__device__ __forceinline__ void lds_wait(v2i (&t)[16]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                   "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]),
+                   "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+                 :
+                 : "memory");
 }
 
-// Four 16-byte reads at lo + 2048 j and four at hi + 2048 j, j = 0..3 (the
-// [N, K] tile's 32-column MFMA groups).
-__device__ __forceinline__ void lds_read_nk(uint32_t lo, uint32_t hi, v4i (&a)[4], v4i (&b)[4]) {
+// The [N, K] tile's operands of one step: four 16-byte reads at lo + 2048 j
+// (t[j]) and four at hi + 2048 j (t[4 + j]), j = the 32-column groups.
+__device__ __forceinline__ void lds_issue_nk(uint32_t lo, uint32_t hi, v4i (&t)[8]) {
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
         "ds_read_b128 %1, %8 offset:2048\n\t"
@@ -261,14 +276,20 @@ __device__ __forceinline__ void lds_read_nk(uint32_t lo, uint32_t hi, v4i (&a)[4
         "ds_read_b128 %4, %9\n\t"
         "ds_read_b128 %5, %9 offset:2048\n\t"
         "ds_read_b128 %6, %9 offset:4096\n\t"
-        "ds_read_b128 %7, %9 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        "ds_read_b128 %7, %9 offset:6144"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]),
+          "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
         : "v"(lo), "v"(hi)
         : "memory");
 }
 
+__device__ __forceinline__ void lds_wait(v4i (&t)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                   "+v"(t[6]), "+v"(t[7])
+                 :
+                 : "memory");
+}
 
 // D += A * B with per-lane E8M0 scales; OPSEL_B picks the byte of sb.
 template <int FMT, int OPSEL_B>
@@ -387,7 +408,7 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
 //   a column XOR-swizzled by (col >> 1) & 3 so that 16-byte LDS reads of 32
 //   lanes do not collide on banks.
 // ---------------------------------------------------------------------------
-constexpr int kCoopStagesKN = 8;   // vmcnt range caps these: (D - 2) * ops < 64
+constexpr int kCoopStagesKN = 8;   // vmcnt range caps these: (D - 1) * ops < 64
 constexpr int kCoopStagesNK = 8;
 static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
                   kCoopStagesNK * kSlotBytes <= kWavesPerBlock * kRingBytes,
@@ -498,7 +519,27 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto compute = [&](int slot, bool live, int ks) {
+    // B operands of one step in registers, double-buffered across steps.
+    using BTile = std::conditional_t<KN, v2i[16], v4i[8]>;
+    BTile bt[2];
+    uint32_t nk_lo = 0, nk_hi = 0;
+    if (!KN) {
+        const int f = (c >> 1) & 3;
+        nk_lo = c * 64 + 16 * (g ^ f);
+        nk_hi = c * 64 + 16 * ((2 + g) ^ f);
+    }
+    auto read_b = [&](int slot, BTile &b) {
+        const uint32_t base = lds_addr(ring + slot * kSlotBytes);
+        if constexpr (KN) {
+            const uint32_t a[4] = {base + tr_addr[0], base + tr_addr[1], base + tr_addr[2],
+                                   base + tr_addr[3]};
+            lds_issue_kn(a, b);
+        } else {
+            lds_issue_nk(base + nk_lo, base + nk_hi, b);
+        }
+    };
+
+    auto mma = [&](int slot, const BTile &b, bool live, int ks) {
         StepRegs &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
@@ -506,65 +547,61 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         // byte (2 ks + g) & 3 of the scale dwords
         const int sh = 8 * (2 * (ks & 1) + g);
         const uint32_t sa = r.sa >> sh;
-        const char *sl = ring + slot * kSlotBytes;
-        if (KN) {
-            const uint32_t base = lds_addr(sl);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // operand bytes 0-7, 8-15: K rows 16g + [0, 16); 16-23, 24-31:
-                // K rows 32 + 16g + [0, 16)
-                v2i t[4];
-                lds_read_tr_kn<0, 8 * kTileN, 32 * kTileN, 40 * kTileN>(base + tr_addr[j], t);
-                const v8i b = {t[0].x, t[0].y, t[1].x, t[1].y, t[2].x, t[2].y, t[3].x, t[3].y};
-                acc[j] = mfma<FMT, 0>(a, b, acc[j], sa, r.sb[j] >> sb_shift);
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (KN) {
+                const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
+                                b[4 * j + 2].x, b[4 * j + 2].y, b[4 * j + 3].x, b[4 * j + 3].y};
+                acc[j] = mfma<FMT, 0>(a, bj, acc[j], sa, r.sb[j] >> sb_shift);
+            } else {
+                acc[j] = mfma<FMT, 0>(a, cat(b[j], b[4 + j]), acc[j], sa, r.sb[j] >> sh);
             }
-        } else {
-            const int f = (c >> 1) & 3;
-            v4i lo[4], hi[4];
-            lds_read_nk(lds_addr(sl + c * 64 + 16 * (g ^ f)),
-                        lds_addr(sl + c * 64 + 16 * ((2 + g) ^ f)), lo, hi);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[j] = mfma<FMT, 0>(a, cat(lo[j], hi[j]), acc[j], sa, r.sb[j] >> sh);
         }
     };
 
     // Vector-memory instructions per step, in issue order: x1 (2), x1 scale
     // (1), weight scales (4), weight tile (all 8, or this wave's 2).
     // Every iteration issues the same groups (past the last step the last
-    // step is re-read; those are L2 hits and are never consumed), so the wait
-    // for step i is a constant count of later groups allowed to be pending:
-    //   wave mode:  issue(i + D - 1); wait (D - 1 later groups); compute(i)
-    //   coop mode:  wait (D - 2 later groups); s_barrier; issue(i + D - 1)
-    //               into the slot of step i - 1; compute(i)
+    // step is re-read; those are L2 hits and are never consumed), so each
+    // wait is a constant count of later groups allowed to be pending.  The
+    // ring has D slots and the prologue fills all of them; iteration i
+    //   waits until step i + 1 has landed (D - 2 later groups pending);
+    //   [cooperative: s_barrier, so every wave's share of step i + 1 is in
+    //   and every wave has finished reading step i's slot];
+    //   issues the LDS reads of step i + 1;
+    //   runs step i's MFMAs (operands read in the previous iteration);
+    //   refills step i's slot and registers with step i + D;
+    //   waits for the LDS reads of step i + 1.
     constexpr int kOpsPerStep = 3 + 4 + kTileLoads;
-    constexpr int kPending = (COOP ? D - 2 : D - 1) * kOpsPerStep;
-    static_assert(kPending < 64, "vmcnt range");
+    static_assert((D - 1) * kOpsPerStep < 64, "vmcnt range");
+    static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
     const int n_steps = ks1 - ks0;
     auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
 
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d) issue(step_of(d), d);
+    for (int d = 0; d < D; ++d) issue(step_of(d), d);
+    wait_vmcnt<(D - 1) * kOpsPerStep>();
+    if (COOP) __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(0, bt[0]);
+    lds_wait(bt[0]);
     for (int i0 = 0; i0 < n_steps; i0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (COOP) {
-                wait_vmcnt<kPending>();
-                __builtin_amdgcn_s_barrier();
-                issue(step_of(i0 + d + D - 1), (d + D - 1) % D);
-            } else {
-                // refill the slot consumed by the previous step
-                issue(step_of(i0 + d + D - 1), (d + D - 1) % D);
-                wait_vmcnt<kPending>();
-            }
+            const int i = i0 + d;
+            wait_vmcnt<(D - 2) * kOpsPerStep>();
+            if (COOP) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            compute(d, i0 + d < n_steps, step_of(i0 + d));
+            read_b((d + 1) % D, bt[(d + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(d, bt[d & 1], i < n_steps, step_of(i));
+            __builtin_amdgcn_sched_barrier(0);
+            issue(step_of(i + D), d);
+            lds_wait(bt[(d + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // Drain the trailing re-reads before the ring is reused (in cooperative
-    // mode the staging areas overlap the shared ring: every wave must be done
-    // reading it and every wave's trailing loads must have landed).
+    // Drain the trailing re-reads before the ring is reused.
     wait_vmcnt<0>();
     epilogue(p, acc, m0, n0, store_rows, rinfo);
 }
@@ -644,14 +681,28 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
     // that visible to the compiler so buffer descriptors and row offsets live
     // in SGPRs (otherwise each buffer load becomes a waterfall loop).
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Units go to workgroups in plain index order.  (Workgroups are dealt to
-    // the 8 XCDs round-robin; keeping neighbouring units on one XCD for L2
-    // sharing measured slower: the weight stream loses more than the few
-    // shared x1 / scale lines gain.)
-    const int64_t block_id = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round-robin.  Cooperative units are
+    // taken in an XCD-grouped order (consecutive units on one XCD): the row
+    // groups of one column tile then share its weights, and the column tiles
+    // of one row group its x1 rows, through that XCD's L2 (without it the
+    // large experts' weights are read from HBM once per row group).  Wave
+    // units are taken in plain order (measured faster for streaming: each XCD
+    // then reads many experts' weights at once).
+    const int64_t xcd_block =
+        (blocks % 8 == 0) ? static_cast<int64_t>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
+                          : blockIdx.x;
+    const int64_t wave_units = units - coop_units;
     const int64_t waves = static_cast<int64_t>(blocks) * kWavesPerBlock;
 
-    for (int64_t u = block_id; u < units; u += blocks) {
+    for (int64_t uu = 0;; ++uu) {
+        int64_t u = xcd_block + uu * blocks;        // cooperative phase
+        if (u >= coop_units) {
+            // wave phase: this block's k-th wave unit is blockIdx.x + k * blocks
+            const int64_t first_wave = uu - (coop_units - xcd_block + blocks - 1) / blocks;
+            const int64_t v = blockIdx.x + first_wave * blocks;
+            if (v >= wave_units) break;
+            u = coop_units + v;
+        }
         __syncthreads();   // the previous unit's waves are done with the LDS
         if (u < coop_units) {
             const int q = static_cast<int>(u / S);
@@ -697,7 +748,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
     }
     // The shared-expert term last: at the start its loads would delay the
     // first weight loads by a memory latency.
-    if (p.shared && !store_rows) shared_slice(p, block_id * kWavesPerBlock + w, waves);
+    if (p.shared && !store_rows) shared_slice(p, blockIdx.x * kWavesPerBlock + w, waves);
 }
 
 // ---------------------------------------------------------------------------

@@ -24,8 +24,9 @@ int check_sizes(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch) {
     // One expert's weight slice and the weight-scale tensor are addressed with
     // 32-bit buffer offsets.
     if (K * N > kMaxRows || M * K > int64_t{1} << 40) return GFR_ERR_UNSUPPORTED;
-    // Work-item count (one K split) must fit an int32.
-    const int64_t n_tiles = (N + gfr::kTileN - 1) / gfr::kTileN;
+    // Work-item count (one K split, the narrower of the two layouts' column
+    // tiles) must fit an int32.
+    const int64_t n_tiles = (N + gfr::kTileNNK - 1) / gfr::kTileNNK;
     if ((M / gfr::kTileM + E) * n_tiles > kMaxRows) return GFR_ERR_UNSUPPORTED;
     return GFR_OK;
 }

@@ -7,11 +7,16 @@
 
 namespace gfr {
 
-// Tile shape of one routed work item: 32 token rows x 128 output columns,
-// consumed in K steps of 64 (one 32x32x64 block-scaled MFMA per 32 columns).
+// Tile shape of one routed work item: 32 token rows x kTileN output columns,
+// consumed in K steps of kStepK (32x32x64 block-scaled MFMAs); one step of the
+// weight tile is 8 KB in either layout.  [K, N] weights: 128 columns x 64 K
+// (each 128-byte row segment of x2 read whole); [N, K] weights: 64 columns x
+// 128 K (each column's 128-byte K segment read whole).
 constexpr int kTileM = 32;
 constexpr int kTileN = 128;
 constexpr int kStepK = 64;
+constexpr int kTileNNK = 64;
+constexpr int kStepKNK = 128;
 constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;

@@ -265,21 +265,23 @@ __device__ __forceinline__ void lds_wait(v2i (&t)[16]) {
                  : "memory");
 }
 
-// The [N, K] tile's operands of one step: four 16-byte reads at lo + 2048 j
-// (t[j]) and four at hi + 2048 j (t[4 + j]), j = the 32-column groups.
-__device__ __forceinline__ void lds_issue_nk(uint32_t lo, uint32_t hi, v4i (&t)[8]) {
+// The [N, K] tile's operands of one step: 16-byte reads at a[sh] (column
+// group 0, t[2 sh]) and a[sh] + 4096 (column group 1, t[2 sh + 1]), issued
+// without waiting.
+__device__ __forceinline__ void lds_issue_nk(const uint32_t (&a)[4], v4i (&t)[8]) {
+    static_assert(32 * kStepKNK == 4096, "column group stride");
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:2048\n\t"
-        "ds_read_b128 %2, %8 offset:4096\n\t"
-        "ds_read_b128 %3, %8 offset:6144\n\t"
-        "ds_read_b128 %4, %9\n\t"
-        "ds_read_b128 %5, %9 offset:2048\n\t"
-        "ds_read_b128 %6, %9 offset:4096\n\t"
-        "ds_read_b128 %7, %9 offset:6144"
+        "ds_read_b128 %1, %8 offset:4096\n\t"
+        "ds_read_b128 %2, %9\n\t"
+        "ds_read_b128 %3, %9 offset:4096\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %10 offset:4096\n\t"
+        "ds_read_b128 %6, %11\n\t"
+        "ds_read_b128 %7, %11 offset:4096"
         : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]),
           "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
-        : "v"(lo), "v"(hi)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
 }
 
@@ -305,6 +307,7 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
 // Per-wave LDS ring: kStages slots of one K step of the 64 x 128 weight tile.
 constexpr int kStages = 4;
 constexpr int kSlotBytes = kStepK * kTileN;            // 8 KB
+static_assert(kStepKNK * kTileNNK == kSlotBytes, "both layouts move 8 KB per step");
 constexpr int kRingBytes = kStages * kSlotBytes;       // 32 KB per wave
 constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
 
@@ -312,10 +315,12 @@ constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
 // Scales are loaded as the aligned dword that holds them and the byte is
 // selected when the step is consumed: a byte load would be zero-extended where
 // the compiler chooses, which can force an early wait on the load.
+template <bool KN>
 struct StepRegs {
-    v4i alo, ahi;         // x1 row: K [16g, +16) and K [32 + 16g, +16) of the step
-    uint32_t sa;          // dword holding the x1 scale of 32-block 2ks + g
-    uint32_t sb[4];       // dword holding the scale byte of column group j
+    v4i a[KN ? 2 : 4];    // x1 row bytes: [K,N] K [16g, +16), [32 + 16g, +16) of the
+                          // 64-K step; [N,K] the same for both 64-K halves
+    uint32_t sa;          // dword holding the x1 scales of the step
+    uint32_t sb[KN ? 4 : 2];  // dword holding the weight scales of column group j
 };
 
 // Destination row and weight of the tile's 32 rows, loaded when the item
@@ -359,6 +364,7 @@ __device__ __forceinline__ int row_dst(const FusedParams &p, const RowInfo &ri) 
 // Epilogue: weight each row by its logit and scatter-add (or store) it.
 // acc element (j, r) of lane (c, g) is row 8(r/4) + 4g + r%4 and output column
 // n0 + 32j + c, so each atomic instruction covers 32 adjacent columns.
+template <int NJ>
 __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)[4],
                                          int m0, int n0, bool store_rows, RowInfo ri) {
     const int lane = threadIdx.x & (kWaveSize - 1);
@@ -372,7 +378,7 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
         if (dst < 0) continue;
         const int t = m0 + row;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int col = n0 + 32 * j + c;
             if (col >= p.N) continue;
             const float v = acc[j][r] * w;
@@ -473,38 +479,49 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         }
         sb_shift = 8 * (2 * (c & 1) + g);
     } else {
-        // load u, lane l: column 16u + l/4; physical chunk l%4 of the slot holds
-        // logical chunk (l%4) ^ ((l/4 >> 1) & 3) of that column
-        const int q = (lane & 3) ^ (((lane >> 2) >> 1) & 3);
+        // load u, lane l: tile column 8u + l/8 (its 128-byte K segment of the
+        // step); it fills physical chunk l%8 of that column's 128-byte slot
+        // row, which holds logical chunk (l%8) ^ ((col >> 1) & 7), col = 8u + l/8
 #pragma unroll
         for (int uu = 0; uu < kTileLoads; ++uu) {
-            const int col = n0 + 16 * (u0 + uu) + (lane >> 2);
-            vb[uu] = (col < N ? col : n0) * K + 16 * q;
+            const int u = u0 + uu;
+            const int tcol = 8 * u + (lane >> 3);
+            const int col = n0 + tcol;
+            vb[uu] = (col < N ? col : n0) * K + 16 * ((lane & 7) ^ ((tcol >> 1) & 7));
         }
+        // scale bytes (col, 32-block 4ks + b) of [N, K/64, 2]: the aligned
+        // dword at col * KS + 4 ks holds the step's four
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const int cj = n0 + 32 * j + c;
             vsb[j] = (cj < N ? cj : n0) * KS;
         }
+        vsb[2] = vsb[3] = 0;
     }
 
     const RowInfo rinfo = load_row_info(p, m0, mcount);
     v16f acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = v16f{};
-    StepRegs regs[D];
+    StepRegs<KN> regs[D];
+    constexpr int kStep = KN ? kStepK : kStepKNK;    // K elements per step
+    constexpr int kAL = KN ? 2 : 4;                  // x1 loads per step
+    constexpr int kSB = KN ? 4 : 2;                  // weight-scale loads per step
 
     auto issue = [&](int ks, int slot) {
-        const int k0 = ks * kStepK;
+        const int k0 = ks * kStep;
         __builtin_amdgcn_sched_barrier(0);
-        StepRegs &r = regs[slot];
-        r.alo = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0, 0);
-        r.ahi = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32, 0);
-        r.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, (2 * ks) & ~3, 0);
+        StepRegs<KN> &r = regs[slot];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int q = 0; q < kAL; ++q)
+            r.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32 * q, 0);
+        // x1 scale bytes of the step: [K,N] (2 ks + g) & 3 of the dword at
+        // (2 ks) & ~3; [N,K] bytes 0..3 of the dword at 4 ks
+        r.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, KN ? (2 * ks) & ~3 : 4 * ks, 0);
+#pragma unroll
+        for (int j = 0; j < kSB; ++j)
             r.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
-                                                           KN ? ks * 2 * N : (2 * ks) & ~3, 0);
+                                                           KN ? ks * 2 * N : 4 * ks, 0);
         // (the instruction's immediate offset would move both addresses, so
         // each 1 KB destination gets its own LDS pointer)
 #pragma unroll
@@ -522,11 +539,15 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     // B operands of one step in registers, double-buffered across steps.
     using BTile = std::conditional_t<KN, v2i[16], v4i[8]>;
     BTile bt[2];
-    uint32_t nk_lo = 0, nk_hi = 0;
+    // [N,K] reads: 64-K half s, 16-byte half h of the lane's 32 operand bytes
+    // = logical chunk 4s + 2h + g of column 32j + c (column c's slot row at
+    // 128 c, group j 4 KB further)
+    uint32_t nk_off[4] = {0, 0, 0, 0};
     if (!KN) {
-        const int f = (c >> 1) & 3;
-        nk_lo = c * 64 + 16 * (g ^ f);
-        nk_hi = c * 64 + 16 * ((2 + g) ^ f);
+        const int f = (c >> 1) & 7;
+#pragma unroll
+        for (int sh = 0; sh < 4; ++sh)
+            nk_off[sh] = c * 128 + 16 * ((2 * sh + g) ^ f);   // sh = 2s + h
     }
     auto read_b = [&](int slot, BTile &b) {
         const uint32_t base = lds_addr(ring + slot * kSlotBytes);
@@ -535,32 +556,44 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
                                    base + tr_addr[3]};
             lds_issue_kn(a, b);
         } else {
-            lds_issue_nk(base + nk_lo, base + nk_hi, b);
+            const uint32_t a[4] = {base + nk_off[0], base + nk_off[1], base + nk_off[2],
+                                   base + nk_off[3]};
+            lds_issue_nk(a, b);
         }
     };
 
     auto mma = [&](int slot, const BTile &b, bool live, int ks) {
-        StepRegs &r = regs[slot];
+        StepRegs<KN> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
-        const v8i a = (arow_ok && live) ? cat(r.alo, r.ahi) : v8i{};
-        // byte (2 ks + g) & 3 of the scale dwords
-        const int sh = 8 * (2 * (ks & 1) + g);
-        const uint32_t sa = r.sa >> sh;
+        const bool on = arow_ok && live;
+        if constexpr (KN) {
+            const v8i a = on ? cat(r.a[0], r.a[1]) : v8i{};
+            // byte (2 ks + g) & 3 of the x1 scale dword
+            const uint32_t sa = r.sa >> (8 * (2 * (ks & 1) + g));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (KN) {
+            for (int j = 0; j < 4; ++j) {
                 const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
                                 b[4 * j + 2].x, b[4 * j + 2].y, b[4 * j + 3].x, b[4 * j + 3].y};
                 acc[j] = mfma<FMT, 0>(a, bj, acc[j], sa, r.sb[j] >> sb_shift);
-            } else {
-                acc[j] = mfma<FMT, 0>(a, cat(b[j], b[4 + j]), acc[j], sa, r.sb[j] >> sh);
+            }
+        } else {
+            // two 64-K halves s, two 32-column groups j; the scale of 32-block
+            // 4 ks + 2 s + g is byte 2 s + g of each scale dword
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const v8i a = on ? cat(r.a[2 * s2], r.a[2 * s2 + 1]) : v8i{};
+                const int shf = 8 * (2 * s2 + g);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[j] = mfma<FMT, 0>(a, cat(b[2 * (2 * s2) + j], b[2 * (2 * s2 + 1) + j]), acc[j],
+                                          r.sa >> shf, r.sb[j] >> shf);
             }
         }
     };
 
-    // Vector-memory instructions per step, in issue order: x1 (2), x1 scale
-    // (1), weight scales (4), weight tile (all 8, or this wave's 2).
+    // Vector-memory instructions per step, in issue order: x1 (2 or 4), x1
+    // scale (1), weight scales (4 or 2), weight tile (all 8, or this wave's 2).
     // Every iteration issues the same groups (past the last step the last
     // step is re-read; those are L2 hits and are never consumed), so each
     // wait is a constant count of later groups allowed to be pending.  The
@@ -572,7 +605,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     //   runs step i's MFMAs (operands read in the previous iteration);
     //   refills step i's slot and registers with step i + D;
     //   waits for the LDS reads of step i + 1.
-    constexpr int kOpsPerStep = 3 + 4 + kTileLoads;
+    constexpr int kOpsPerStep = kAL + 1 + kSB + kTileLoads;
     static_assert((D - 1) * kOpsPerStep < 64, "vmcnt range");
     static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
     const int n_steps = ks1 - ks0;
@@ -603,7 +636,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     }
     // Drain the trailing re-reads before the ring is reused.
     wait_vmcnt<0>();
-    epilogue(p, acc, m0, n0, store_rows, rinfo);
+    epilogue<KN ? 4 : 2>(p, acc, m0, n0, store_rows, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
@@ -652,13 +685,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
     __shared__ int64_t s_scan[kBlockThreads];
     __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock * kRingBytes];
 
-    const int n_tiles = (p.N + kTileN - 1) / kTileN;
+    constexpr int kTN = TRANS ? kTileNNK : kTileN;   // columns per item
+    const int n_tiles = (p.N + kTN - 1) / kTN;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
     build_work_list(p, n_tiles, wl, s_scan);
     if (p.det_total && blockIdx.x == 0 && threadIdx.x == 0) *p.det_total = wl.routed_tokens;
 
     const bool store_rows = p.wbuf != nullptr;
-    const int k_steps = p.K / kStepK;
+    const int k_steps = p.K / (TRANS ? kStepKNK : kStepK);
     const int blocks = gridDim.x;
     int S = p.split_k;
     const int base_units = wl.litems + (wl.sitems + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -721,7 +755,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            routed_item<FMT, !TRANS, true>(p, e, m0, mcount, nt * kTileN, ks0, ks1, store_rows,
+            routed_item<FMT, !TRANS, true>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
                                            s_ring, w);
         } else {
             const int64_t it = (u - coop_units) * kWavesPerBlock + w;
@@ -742,7 +776,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
-            routed_item<FMT, !TRANS, false>(p, e, m0, mcount, nt * kTileN, ks0, ks1,
+            routed_item<FMT, !TRANS, false>(p, e, m0, mcount, nt * kTN, ks0, ks1,
                                             store_rows, own, w);
         }
     }

@@ -103,9 +103,16 @@ struct WorkList {
 constexpr int kCoopMinRows = 64;
 constexpr int kCoopRows = kTileM * kWavesPerBlock;   // 128
 
+// Rows of one cooperative unit: experts with more than 128 rows use 256-row
+// groups (each wave two 32-row fragments: twice the MFMAs per streamed and
+// per LDS-read weight step), smaller ones 128-row groups.
+__device__ __forceinline__ int coop_group_rows(int cnt) {
+    return cnt > kCoopRows ? 2 * kCoopRows : kCoopRows;
+}
+
 constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 
-__device__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
+__device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
                                 int64_t *s_scan) {
     const int tid = threadIdx.x;
     static_assert(kPerThread == 4, "one thread reads 4 consecutive group_list entries");
@@ -155,7 +162,8 @@ __device__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
         }
         run += c[i];
         const int64_t si = cnt >= kCoopMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
-        const int64_t li = cnt >= kCoopMinRows ? ((cnt + kCoopRows - 1) / kCoopRows) * n_tiles : 0;
+        const int gr = coop_group_rows(cnt);
+        const int64_t li = cnt >= kCoopMinRows ? ((cnt + gr - 1) / gr) * n_tiles : 0;
         items[i] = si | (li << 32);
         isum += items[i];
     }
@@ -315,16 +323,17 @@ constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
 // Scales are loaded as the aligned dword that holds them and the byte is
 // selected when the step is consumed: a byte load would be zero-extended where
 // the compiler chooses, which can force an early wait on the load.
-template <bool KN>
+template <bool KN, int RF>
 struct StepRegs {
-    v4i a[KN ? 2 : 4];    // x1 row bytes: [K,N] K [16g, +16), [32 + 16g, +16) of the
-                          // 64-K step; [N,K] the same for both 64-K halves
-    uint32_t sa;          // dword holding the x1 scales of the step
+    v4i a[RF][KN ? 2 : 4];    // x1 row bytes of fragment f: [K,N] K [16g, +16),
+                              // [32 + 16g, +16) of the 64-K step; [N,K] the
+                              // same for both 64-K halves
+    uint32_t sa[RF];          // dword holding the x1 scales of the step
     uint32_t sb[KN ? 4 : 2];  // dword holding the weight scales of column group j
 };
 
-// Destination row and weight of the tile's 32 rows, loaded when the item
-// starts (their latency hides behind the weight stream): lane l < 32 holds row
+// Destination row and weight of the tile's 32 (or 64) rows, loaded when the
+// item starts (their latency hides behind the weight stream): lane l holds row
 // l's, and the epilogue fetches them with a lane shuffle.  A row past the
 // expert's last token, or with row_index outside [0, batch) (flagged), gets
 // dst = -1 and is skipped.
@@ -334,10 +343,12 @@ struct RowInfo {
     bool live;    // lane < 32 and the row is one of the expert's tokens
 };
 
+template <int RF>
 __device__ __forceinline__ RowInfo load_row_info(const FusedParams &p, int m0, int mcount) {
     const int lane = threadIdx.x & (kWaveSize - 1);
-    RowInfo ri{v2i{0, 0}, 0.0f, lane < kTileM && lane < mcount};
-    const int cnt = mcount < kTileM ? (mcount > 0 ? mcount : 0) : kTileM;
+    constexpr int kRows = kTileM * RF;
+    RowInfo ri{v2i{0, 0}, 0.0f, lane < kRows && lane < mcount};
+    const int cnt = mcount < kRows ? (mcount > 0 ? mcount : 0) : kRows;
     const rsrc_t rr = make_rsrc(p.row_index + m0, static_cast<int64_t>(cnt) * 8);
     ri.dst = __builtin_amdgcn_raw_buffer_load_b64(rr, 8 * lane, 0, 0);
     if (p.logit) {
@@ -364,15 +375,18 @@ __device__ __forceinline__ int row_dst(const FusedParams &p, const RowInfo &ri) 
 // Epilogue: weight each row by its logit and scatter-add (or store) it.
 // acc element (j, r) of lane (c, g) is row 8(r/4) + 4g + r%4 and output column
 // n0 + 32j + c, so each atomic instruction covers 32 adjacent columns.
-template <int NJ>
-__device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)[4],
+template <int NJ, int RF>
+__device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs)[RF][4],
                                          int m0, int n0, bool store_rows, RowInfo ri) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
     const int my_dst = row_dst(p, ri);
 #pragma unroll
+    for (int f = 0; f < RF; ++f) {
+    const v16f (&acc)[4] = accs[f];
+#pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+        const int row = 32 * f + 8 * (r >> 2) + 4 * g + (r & 3);
         const int dst = __shfl(my_dst, row);
         const float w = __shfl(ri.w, row);
         if (dst < 0) continue;
@@ -387,6 +401,7 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&acc)
             else
                 unsafeAtomicAdd(p.out + static_cast<int64_t>(dst) * p.N + col, v);
         }
+    }
     }
 }
 
@@ -420,10 +435,11 @@ static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
                   kCoopStagesNK * kSlotBytes <= kWavesPerBlock * kRingBytes,
               "cooperative ring fits the block's LDS");
 
-template <int FMT, bool KN, bool COOP>
-__device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
+template <int FMT, bool KN, bool COOP, int RF>
+__device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                             int ks0, int ks1, bool store_rows, char *ring, int w) {
-    constexpr int D = COOP ? (KN ? kCoopStagesKN : kCoopStagesNK) : kStages;
+    static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
+    constexpr int D = !COOP ? kStages : RF == 2 ? 4 : (KN ? kCoopStagesKN : kCoopStagesNK);
     constexpr int kTileLoads = COOP ? kBLoadsPerStep / kWavesPerBlock : kBLoadsPerStep;
     // The item is wave-uniform; say so, so that descriptors and offsets stay
     // in SGPRs (a descriptor in VGPRs turns every buffer load into a loop).
@@ -441,12 +457,17 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     // (a cooperative wave past the expert's last row has mcount <= 0: its
     // loads have an empty range and return zeros, its epilogue writes nothing)
     if (mcount < 0) mcount = 0;
-    const bool arow_ok = c < mcount;
-    const int arow = arow_ok ? c : 0;
+    bool arow_ok[RF];
+    int va[RF], vsa[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+        arow_ok[f] = kTileM * f + c < mcount;
+        const int arow = arow_ok[f] ? kTileM * f + c : 0;
+        va[f] = arow * K + 16 * g;
+        vsa[f] = arow * KS;       // + (2 ks) & ~3 or 4 ks: KS is a multiple of 4
+    }
     const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
-    const int va = arow * K + 16 * g;
-    const int vsa = arow * KS;     // + (2 ks) & ~3: KS is a multiple of 4
     const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * K * N, static_cast<int64_t>(K) * N);
     const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(KS) * N);
     const int u0 = COOP ? w * kTileLoads : 0;   // first tile load this wave issues
@@ -499,11 +520,13 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
         vsb[2] = vsb[3] = 0;
     }
 
-    const RowInfo rinfo = load_row_info(p, m0, mcount);
-    v16f acc[4];
+    const RowInfo rinfo = load_row_info<RF>(p, m0, mcount);
+    v16f acc[RF][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = v16f{};
-    StepRegs<KN> regs[D];
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[f][j] = v16f{};
+    StepRegs<KN, RF> regs[D];
     constexpr int kStep = KN ? kStepK : kStepKNK;    // K elements per step
     constexpr int kAL = KN ? 2 : 4;                  // x1 loads per step
     constexpr int kSB = KN ? 4 : 2;                  // weight-scale loads per step
@@ -511,13 +534,17 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     auto issue = [&](int ks, int slot) {
         const int k0 = ks * kStep;
         __builtin_amdgcn_sched_barrier(0);
-        StepRegs<KN> &r = regs[slot];
+        StepRegs<KN, RF> &r = regs[slot];
 #pragma unroll
-        for (int q = 0; q < kAL; ++q)
-            r.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, k0 + 32 * q, 0);
+        for (int f = 0; f < RF; ++f)
+#pragma unroll
+            for (int q = 0; q < kAL; ++q)
+                r.a[f][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[f], k0 + 32 * q, 0);
         // x1 scale bytes of the step: [K,N] (2 ks + g) & 3 of the dword at
         // (2 ks) & ~3; [N,K] bytes 0..3 of the dword at 4 ks
-        r.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, KN ? (2 * ks) & ~3 : 4 * ks, 0);
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+            r.sa[f] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f], KN ? (2 * ks) & ~3 : 4 * ks, 0);
 #pragma unroll
         for (int j = 0; j < kSB; ++j)
             r.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
@@ -563,31 +590,34 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     };
 
     auto mma = [&](int slot, const BTile &b, bool live, int ks) {
-        StepRegs<KN> &r = regs[slot];
+        StepRegs<KN, RF> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
-        const bool on = arow_ok && live;
-        if constexpr (KN) {
-            const v8i a = on ? cat(r.a[0], r.a[1]) : v8i{};
-            // byte (2 ks + g) & 3 of the x1 scale dword
-            const uint32_t sa = r.sa >> (8 * (2 * (ks & 1) + g));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
-                                b[4 * j + 2].x, b[4 * j + 2].y, b[4 * j + 3].x, b[4 * j + 3].y};
-                acc[j] = mfma<FMT, 0>(a, bj, acc[j], sa, r.sb[j] >> sb_shift);
-            }
-        } else {
-            // two 64-K halves s, two 32-column groups j; the scale of 32-block
-            // 4 ks + 2 s + g is byte 2 s + g of each scale dword
+        for (int f = 0; f < RF; ++f) {
+            const bool on = arow_ok[f] && live;
+            if constexpr (KN) {
+                const v8i a = on ? cat(r.a[f][0], r.a[f][1]) : v8i{};
+                // byte (2 ks + g) & 3 of the x1 scale dword
+                const uint32_t sa = r.sa[f] >> (8 * (2 * (ks & 1) + g));
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const v8i a = on ? cat(r.a[2 * s2], r.a[2 * s2 + 1]) : v8i{};
-                const int shf = 8 * (2 * s2 + g);
+                for (int j = 0; j < 4; ++j) {
+                    const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
+                                    b[4 * j + 2].x, b[4 * j + 2].y, b[4 * j + 3].x, b[4 * j + 3].y};
+                    acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j] >> sb_shift);
+                }
+            } else {
+                // two 64-K halves s, two 32-column groups j; the scale of
+                // 32-block 4 ks + 2 s + g is byte 2 s + g of each scale dword
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[j] = mfma<FMT, 0>(a, cat(b[2 * (2 * s2) + j], b[2 * (2 * s2 + 1) + j]), acc[j],
-                                          r.sa >> shf, r.sb[j] >> shf);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const v8i a = on ? cat(r.a[f][2 * s2], r.a[f][2 * s2 + 1]) : v8i{};
+                    const int shf = 8 * (2 * s2 + g);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[f][j] = mfma<FMT, 0>(a, cat(b[2 * (2 * s2) + j], b[2 * (2 * s2 + 1) + j]),
+                                                 acc[f][j], r.sa[f] >> shf, r.sb[j] >> shf);
+                }
             }
         }
     };
@@ -605,7 +635,7 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     //   runs step i's MFMAs (operands read in the previous iteration);
     //   refills step i's slot and registers with step i + D;
     //   waits for the LDS reads of step i + 1.
-    constexpr int kOpsPerStep = kAL + 1 + kSB + kTileLoads;
+    constexpr int kOpsPerStep = RF * (kAL + 1) + kSB + kTileLoads;
     static_assert((D - 1) * kOpsPerStep < 64, "vmcnt range");
     static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
     const int n_steps = ks1 - ks0;
@@ -636,14 +666,14 @@ __device__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int
     }
     // Drain the trailing re-reads before the ring is reused.
     wait_vmcnt<0>();
-    epilogue<KN ? 4 : 2>(p, acc, m0, n0, store_rows, rinfo);
+    epilogue<KN ? 4 : 2, RF>(p, acc, m0, n0, store_rows, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
 // contiguous slice of the R*N elements per wave, so every wave carries the
 // same small share (done after its routed work).  Lane l handles elements
 // 64i + l of the slice: every load and atomic covers 64 adjacent elements.
-__device__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) {
+__device__ __forceinline__ void shared_slice(const FusedParams &p, int64_t wave, int64_t waves) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int64_t total = static_cast<int64_t>(p.shared_rows) * p.N;
     int64_t per = (total + waves - 1) / waves;
@@ -744,19 +774,25 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
             const int e_pref = __builtin_amdgcn_readfirstlane(s_lpref[e]);
-            const int mg_count = (e_cnt + kCoopRows - 1) / kCoopRows;
+            const int gr = coop_group_rows(e_cnt);
+            const int mg_count = (e_cnt + gr - 1) / gr;
             const int64_t local = u - static_cast<int64_t>(e_pref) * S;
             const int mg = static_cast<int>(local % mg_count);
             const int64_t rest = local / mg_count;
             const int s = static_cast<int>(rest % S);
             const int nt = static_cast<int>(rest / S);
-            const int row0 = mg * kCoopRows + w * kTileM;   // this wave's rows
-            const int mcount = min(kTileM, e_cnt - row0);
+            const int wr = gr / kWavesPerBlock;               // rows per wave: 32 or 64
+            const int row0 = mg * gr + w * wr;                // this wave's rows
+            const int mcount = min(wr, e_cnt - row0);
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            routed_item<FMT, !TRANS, true>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
-                                           s_ring, w);
+            if (gr > kCoopRows)
+                routed_item<FMT, !TRANS, true, 2>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
+                                                  s_ring, w);
+            else
+                routed_item<FMT, !TRANS, true, 1>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
+                                                  s_ring, w);
         } else {
             const int64_t it = (u - coop_units) * kWavesPerBlock + w;
             if (it >= wave_items) continue;
@@ -776,8 +812,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
-            routed_item<FMT, !TRANS, false>(p, e, m0, mcount, nt * kTN, ks0, ks1,
-                                            store_rows, own, w);
+            routed_item<FMT, !TRANS, false, 1>(p, e, m0, mcount, nt * kTN, ks0, ks1,
+                                               store_rows, own, w);
         }
     }
     // The shared-expert term last: at the start its loads would delay the

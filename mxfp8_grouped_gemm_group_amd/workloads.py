@@ -134,9 +134,21 @@ SMALL_T = _reg(Workload("small_t", batch=64, M=200, K=640, N=576, E=5, fp8="e5m2
                         transpose_x2=True, groups=(33, 0, 64, 100, 3), group_list_type=0,
                         exp_range=(-6, 6), shared_weight=0.5, out_init="normal", seed=1022))
 
+# Large experts at a size the oracle checks element by element: 300 rows (two
+# row groups of 256, the second with 44 rows), 141 (one group of 256 with two
+# full, one partial and one empty wave), 70 (a 128-row group), 5 (a 32-row
+# tile); partial column tiles in both layouts.
+SMALL_BIG_N = _reg(Workload("small_big_n", batch=100, M=516, K=768, N=320, E=5, fp8="e4m3fn",
+                            groups=(0, 300, 70, 5, 141), group_list_type=1, exp_range=(-4, 4),
+                            row_index="perm", shared_rows=30, shared_weight=0.5,
+                            shared_offset=50, out_init="normal", seed=1023))
+SMALL_BIG_T = _reg(Workload("small_big_t", batch=86, M=516, K=640, N=352, E=4, fp8="e5m2",
+                            transpose_x2=True, groups=(141, 5, 300, 70), group_list_type=0,
+                            exp_range=(-4, 4), row_index="perm", seed=1024))
+
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
-for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T):
+for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))
 

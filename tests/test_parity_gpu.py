@@ -85,7 +85,9 @@ def slack_for(inp, rows=None):
 # Full element-by-element parity on small ragged cases (several n-tiles,
 # ragged M tails, empty experts, both layouts and FP8 kinds).
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact", "small_t_exact"])
+@pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact", "small_t_exact",
+                                  "small_big_n", "small_big_t", "small_big_n_exact",
+                                  "small_big_t_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]
@@ -112,7 +114,8 @@ def test_full_shapes_sampled(name):
     assert_parity(got[torch.as_tensor(rows, device=DEV)], ref, mag, exact=w.exact, what=name)
 
 
-@pytest.mark.parametrize("name", ["c5", "c5_exact", "small_n", "small_t"])
+@pytest.mark.parametrize("name", ["c5", "c5_exact", "small_n", "small_t", "small_big_n",
+                                  "small_big_t_exact"])
 def test_deterministic_mode(name):
     """Deterministic mode: bitwise repeatable, within tolerance of the oracle
     (bit-exact on integer data)."""

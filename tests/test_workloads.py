@@ -7,7 +7,7 @@ from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_inputs, as_nu
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "p1_tc_a", "p1_tc_b",
-                                  "p2_ragged", "small_n", "small_t"])
+                                  "p2_ragged", "small_n", "small_t", "small_big_n", "small_big_t"])
 def test_counts(name):
     w = WORKLOADS[name]
     c = w.counts()
@@ -25,7 +25,8 @@ def test_zipf_routing_has_empty_and_heavy_experts(name):
     assert c.max() > 500
 
 
-@pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact"])
+@pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact", "small_big_n",
+                                  "small_big_t_exact"])
 def test_make_inputs_shapes_and_determinism(name):
     w = WORKLOADS[name]
     a = make_inputs(w)

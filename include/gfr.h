@@ -54,7 +54,9 @@ enum gfr_status {
     GFR_ERR_BAD_SHAPE = 2,       /* negative or inconsistent sizes */
     GFR_ERR_BAD_OFFSET = 3,      /* shared_input_offset < 0 or off + rows > batch */
     GFR_ERR_UNSUPPORTED = 4,     /* valid per the pages but not implemented here */
-    GFR_ERR_BAD_ALIGNMENT = 5,   /* x1 / x2 / scale not 16-byte aligned */
+    GFR_ERR_BAD_ALIGNMENT = 5,   /* x1 / x2 / scale / shared_input not 16-byte aligned,
+                                    out not 4-byte (deterministic mode: 16-byte) aligned,
+                                    workspace not 256-byte aligned */
     GFR_ERR_WORKSPACE_TOO_SMALL = 6,
     GFR_ERR_BAD_ARG = 7,         /* unknown enum value (fp8_kind, group_list_type) */
     GFR_ERR_HIP = 8              /* a HIP runtime call failed */
@@ -80,7 +82,8 @@ typedef struct gfr_options {
     /* 0: scatter-add with FP32 atomics (default).  1: deterministic — the
      * matmul writes logit-weighted rows to the workspace, then each output row
      * is reduced in a fixed order: initial value, tokens in ascending t, then
-     * the shared term.  Needs gfr_workspace_size() bytes of workspace. */
+     * the shared term.  Needs gfr_workspace_size() bytes of workspace
+     * (256-byte aligned) and a 16-byte aligned out (GFR_ERR_BAD_ALIGNMENT). */
     int deterministic;
     /* Device workspace (may be NULL when 0 bytes are required). */
     void *workspace;

@@ -104,6 +104,7 @@ int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale
         if (!opts->workspace || opts->workspace_bytes < d.total)
             return GFR_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(opts->workspace, 256)) return GFR_ERR_BAD_ALIGNMENT;
+        if (!aligned(out, 16)) return GFR_ERR_BAD_ALIGNMENT;   // float4 row reduction
     }
     if (!shared_input) shared_rows = 0;
 

@@ -49,10 +49,11 @@ struct FusedParams {
 //   counts        int32 [batch]    tokens per output row (cleared each call)
 //   cursor        int32 [batch]    fill positions
 //   offsets       int32 [batch+1]  exclusive prefix of counts
-//   tokens        int32 [M]        tokens grouped by output row
+//   tokens        int32 [M]        tokens grouped by output row (any order)
+//   sorted        int32 [M]        the same, ascending within each row
 //   total_tokens  int32            routed tokens (sum of group counts)
 struct DetLayout {
-    size_t wbuf, counts, cursor, offsets, tokens, total_tokens, total;
+    size_t wbuf, counts, cursor, offsets, tokens, sorted, total_tokens, total;
 };
 DetLayout det_layout(int64_t M, int64_t N, int64_t batch);
 

@@ -862,72 +862,93 @@ __global__ void det_fill_kernel(FusedParams p, int *cursor, int *tokens) {
     }
 }
 
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-    return v;
-}
+constexpr int kDetSortTile = 512;   // tokens compared per LDS pass
 
-constexpr int kDetSortCap = 512;  // tokens per output row ordered in LDS
-
-// One wave per output row.  The row's tokens (filled in arbitrary order) are
-// put in ascending t — by rank (count of smaller tokens; tokens are distinct)
-// into LDS when the row has at most kDetSortCap of them, otherwise by repeated
-// wave-wide minimum searches — and reduced in that order:
-//   out[b] = ((init + W[t_1]) + W[t_2]) + ... + shared term.
-__global__ __launch_bounds__(kBlockThreads) void det_reduce_kernel(FusedParams p,
-                                                                   const int *offsets,
-                                                                   const int *tokens) {
-    __shared__ int s_sorted[kWavesPerBlock][kDetSortCap];
+// One wave per output row: the row's tokens (filled in arbitrary order) are
+// written to `sorted` in ascending t.  Tokens are distinct, so the position of
+// t is the number of smaller tokens in the row (counted against LDS tiles of
+// the row's list).
+__global__ __launch_bounds__(kBlockThreads) void det_sort_kernel(FusedParams p, const int *offsets,
+                                                               const int *tokens, int *sorted) {
+    __shared__ int s_tile[kWavesPerBlock][kDetSortTile];
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wv = threadIdx.x >> 6;
-    int *sorted = s_sorted[wv];
+    int *tile = s_tile[wv];
     const int wave = blockIdx.x * kWavesPerBlock + wv;
     const int waves = gridDim.x * kWavesPerBlock;
     for (int b = wave; b < p.batch; b += waves) {
         const int o0 = offsets[b], L = offsets[b + 1] - o0;
-        const bool in_lds = L <= kDetSortCap;
-        if (in_lds) {
-            for (int i = lane; i < L; i += kWaveSize) {
-                const int ti = tokens[o0 + i];
-                int rank = 0;
-                for (int j = 0; j < L; ++j) rank += tokens[o0 + j] < ti;
-                sorted[rank] = ti;
+        for (int i0 = 0; i0 < L; i0 += kWaveSize) {
+            const int i = i0 + lane;
+            const int ti = i < L ? tokens[o0 + i] : 0;
+            int rank = 0;
+            for (int j0 = 0; j0 < L; j0 += kDetSortTile) {
+                const int jn = L - j0 < kDetSortTile ? L - j0 : kDetSortTile;
+                __builtin_amdgcn_wave_barrier();
+                for (int j = lane; j < jn; j += kWaveSize) tile[j] = tokens[o0 + j0 + j];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                for (int j = 0; j < jn; ++j) rank += tile[j] < ti;
             }
+            if (i < L) sorted[o0 + rank] = ti;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        const bool has_shared = p.shared && b >= p.shared_off && b < p.shared_off + p.shared_rows;
-        for (int col0 = 0; col0 < p.N; col0 += kWaveSize) {
-            const int col = col0 + lane;
-            const bool ok = col < p.N;
-            float acc = ok ? p.out[static_cast<int64_t>(b) * p.N + col] : 0.0f;
-            int prev = -1;
-            for (int i = 0; i < L; ++i) {
-                int t;
-                if (in_lds) {
-                    t = sorted[i];
-                } else {
-                    int m = 0x7fffffff;
-                    for (int j = lane; j < L; j += kWaveSize) {
-                        const int tj = tokens[o0 + j];
-                        if (tj > prev && tj < m) m = tj;
-                    }
-                    t = wave_min(m);
-                    prev = t;
+    }
+}
+
+// out[b, c] = ((init + W[t_1, c]) + W[t_2, c]) + ... + shared term, with
+// t_1 < t_2 < ... the tokens routed to row b: the same order for every
+// element and every run.  Work item = (row, 256 columns); lane l handles
+// columns 4l .. 4l + 3 of the item (N is a multiple of 4), loading a few
+// tokens' rows ahead of the additions.
+__global__ __launch_bounds__(kBlockThreads) void det_reduce_kernel(FusedParams p,
+                                                                   const int *offsets,
+                                                                   const int *sorted) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int waves = gridDim.x * kWavesPerBlock;
+    constexpr int kCols = 4 * kWaveSize;
+    const int chunks = (p.N + kCols - 1) / kCols;
+    const int64_t items = static_cast<int64_t>(p.batch) * chunks;
+    constexpr int kAhead = 4;
+    for (int64_t it = wave; it < items; it += waves) {
+        const int b = static_cast<int>(it / chunks);
+        const int col = static_cast<int>(it % chunks) * kCols + 4 * lane;
+        const bool ok = col < p.N;
+        const int o0 = offsets[b], L = offsets[b + 1] - o0;
+        float4 acc = ok ? *reinterpret_cast<const float4 *>(p.out + static_cast<int64_t>(b) * p.N + col)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i0 = 0; i0 < L; i0 += kAhead) {
+            float4 v[kAhead];
+#pragma unroll
+            for (int k = 0; k < kAhead; ++k) {
+                const int i = i0 + k;
+                v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (ok && i < L) {
+                    const int t = sorted[o0 + i];
+                    v[k] = *reinterpret_cast<const float4 *>(p.wbuf + static_cast<int64_t>(t) * p.N + col);
                 }
-                if (ok) acc += p.wbuf[static_cast<int64_t>(t) * p.N + col];
             }
-            if (ok && has_shared) {
-                const uint16_t h = p.shared[static_cast<int64_t>(b - p.shared_off) * p.N + col];
-                acc += p.shared_w * __uint_as_float(static_cast<uint32_t>(h) << 16);
+#pragma unroll
+            for (int k = 0; k < kAhead; ++k) {
+                if (i0 + k < L) {
+                    acc.x += v[k].x;
+                    acc.y += v[k].y;
+                    acc.z += v[k].z;
+                    acc.w += v[k].w;
+                }
             }
-            if (ok) p.out[static_cast<int64_t>(b) * p.N + col] = acc;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (!ok) continue;
+        if (p.shared && b >= p.shared_off && b < p.shared_off + p.shared_rows) {
+            const uint2 h = *reinterpret_cast<const uint2 *>(
+                p.shared + static_cast<int64_t>(b - p.shared_off) * p.N + col);
+            acc.x += p.shared_w * __uint_as_float(h.x << 16);
+            acc.y += p.shared_w * __uint_as_float(h.x & 0xffff0000u);
+            acc.z += p.shared_w * __uint_as_float(h.y << 16);
+            acc.w += p.shared_w * __uint_as_float(h.y & 0xffff0000u);
+        }
+        *reinterpret_cast<float4 *>(p.out + static_cast<int64_t>(b) * p.N + col) = acc;
     }
 }
 
@@ -967,7 +988,8 @@ DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
     d.cursor = d.counts + up(static_cast<size_t>(batch) * sizeof(int));
     d.offsets = d.cursor + up(static_cast<size_t>(batch) * sizeof(int));
     d.tokens = d.offsets + up((static_cast<size_t>(batch) + 1) * sizeof(int));
-    d.total_tokens = d.tokens + up(static_cast<size_t>(M) * sizeof(int));
+    d.sorted = d.tokens + up(static_cast<size_t>(M) * sizeof(int));
+    d.total_tokens = d.sorted + up(static_cast<size_t>(M) * sizeof(int));
     d.total = d.total_tokens + 256;
     return d;
 }
@@ -998,14 +1020,17 @@ hipError_t launch_deterministic_reduce(const FusedParams &p, void *workspace,
     int *cursor = reinterpret_cast<int *>(ws + d.cursor);
     int *offsets = reinterpret_cast<int *>(ws + d.offsets);
     int *tokens = reinterpret_cast<int *>(ws + d.tokens);
+    int *sorted = reinterpret_cast<int *>(ws + d.sorted);
     const int cu = device_cu_count();
     hipLaunchKernelGGL(det_count_kernel, dim3(cu), dim3(kBlockThreads), 0, stream, p, counts);
     hipLaunchKernelGGL(det_scan_kernel, dim3(1), dim3(kBlockThreads), 0, stream, p, counts,
                        offsets, cursor);
     hipLaunchKernelGGL(det_fill_kernel, dim3(cu), dim3(kBlockThreads), 0, stream, p, cursor,
                        tokens);
-    hipLaunchKernelGGL(det_reduce_kernel, dim3(cu * 2), dim3(kBlockThreads), 0, stream, p,
-                       offsets, tokens);
+    hipLaunchKernelGGL(det_sort_kernel, dim3(cu), dim3(kBlockThreads), 0, stream, p, offsets,
+                       tokens, sorted);
+    hipLaunchKernelGGL(det_reduce_kernel, dim3(cu * 4), dim3(kBlockThreads), 0, stream, p,
+                       offsets, sorted);
     return hipGetLastError();
 }
 

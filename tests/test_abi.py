@@ -81,6 +81,16 @@ def test_deterministic_needs_workspace():
     assert _call(opts=ctypes.byref(opts)) == 6
 
 
+def test_deterministic_alignment():
+    big = 1 << 40
+    # workspace not 256-byte aligned
+    opts = GfrOptions(1, 0x10010, big, None, 0)
+    assert _call(opts=ctypes.byref(opts)) == 5
+    # out only 4-byte aligned: fine for atomics, not for the float4 row reduction
+    opts = GfrOptions(1, 0x10000, big, None, 0)
+    assert _call(out=0x10004, opts=ctypes.byref(opts)) == 5
+
+
 def test_empty_output_is_a_noop():
     # N = 0 or batch = 0: valid per the empty-tensor rules, returns before any launch
     assert _call(N=0) == 0

@@ -115,6 +115,47 @@ def test_tiny_matches_independent_numpy(case):
     assert np.all(np.abs(got - ref) <= 1e-13 * mag + 1e-300)
 
 
+# Per-expert weight scales: a leading expert axis, (e, n, ceil(k/64), 2) when
+# x2 is transposed (CANN aclnnGroupedMatmulFinalizeRoutingV3, Atlas 350 scale
+# notes) and (e, ceil(k/64), n, 2) otherwise (the 3-D layout's reading).
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c['seed']}")
+def test_tiny_per_expert_scales_match_independent_numpy(case):
+    c = tiny_case(**case, per_expert=True)
+    assert c["scale"].ndim == 4 and c["scale"].shape[0] == case["E"]
+    got, mag = _run(c)
+    ref = numpy_reference(c)
+    assert np.all(np.abs(got - ref) <= 1e-13 * mag + 1e-300)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_per_expert_scales_identical_copies_equal_shared(transpose):
+    c = tiny_case(seed=7, E=3, M=9, K=128, N=5, transpose=transpose, kind=0, gtype=1)
+    a, _ = _run(c)
+    b, _ = _run(c, scale=np.ascontiguousarray(np.broadcast_to(c["scale"], (3,) + c["scale"].shape)))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_per_expert_scales_select_the_experts_slice(transpose):
+    """Each expert's rows use only its own slice: running one expert at a time
+    (the others' tokens given logit 0) with that slice as a 3-D scale, and
+    summing the routed parts, reproduces the 4-D run."""
+    c = tiny_case(seed=11, E=3, M=10, K=192, N=4, transpose=transpose, kind=1, gtype=1,
+                  groups=[4, 3, 3], per_expert=True, shared=False)
+    full, mag = _run(c)
+    init = c["out_init"].astype(np.float64)
+    total = init.copy()
+    start = 0
+    for e, cnt in enumerate(c["group_list"]):
+        lg = np.zeros_like(c["logit"])
+        lg[start:start + cnt] = c["logit"][start:start + cnt]
+        part, _ = _run(c, scale=np.ascontiguousarray(c["scale"][e]), logit=lg,
+                       out_init=np.zeros_like(c["out_init"]))
+        total += part
+        start += cnt
+    assert np.all(np.abs(full - total) <= 1e-13 * mag + 1e-300)
+
+
 @pytest.mark.parametrize("transpose", [False, True])
 def test_textbook_plain_matmul(transpose):
     """One expert, unit scales, unit logits, identity routing, zero init, no

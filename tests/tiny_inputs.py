@@ -34,7 +34,7 @@ def _finite_codes(kind):
 
 def tiny_case(seed, E, M, K, N, transpose, kind, gtype, groups=None, batch=None,
               routing="random", unit_scales=False, logit="random", shared=True,
-              exact=False):
+              exact=False, per_expert=False):
     rng = np.random.default_rng(seed)
     KB = (K + 63) // 64
     if exact:
@@ -53,6 +53,8 @@ def tiny_case(seed, E, M, K, N, transpose, kind, gtype, groups=None, batch=None,
         pts = (127 + rng.integers(lo, hi + 1, size=(M, KB, 2))).astype(np.uint8)
         sc = (127 + rng.integers(lo, hi + 1,
                                  size=(N, KB, 2) if transpose else (KB, N, 2))).astype(np.uint8)
+    if per_expert:   # a leading expert axis: (E, N, KB, 2) or (E, KB, N, 2)
+        sc = (127 + rng.integers(lo, hi + 1, size=(E,) + sc.shape)).astype(np.uint8)
     if groups is None:
         used = int(rng.integers(M // 2, M + 1))
         cuts = np.sort(rng.integers(0, used + 1, size=E - 1))
@@ -96,15 +98,20 @@ def numpy_reference(c):
     s1 = np.exp2(c["pertoken_scale"].astype(np.float64) - 127).reshape(M, -1)
     x1dq = x1 * np.repeat(s1, 32, axis=1)[:, :K]
     x2 = decode_np(c["x2"], kind)
-    if c["transpose_x2"]:
-        N = x2.shape[1]
-        s2 = np.exp2(c["scale"].astype(np.float64) - 127).reshape(N, -1)       # [N, 2KB]
-        x2dq = np.transpose(x2 * np.repeat(s2, 32, axis=1)[:, :K][None], (0, 2, 1))
-    else:
-        N = x2.shape[2]
-        s3 = np.exp2(c["scale"].astype(np.float64) - 127)                        # [KB, N, 2]
-        s2 = np.moveaxis(s3, 2, 1).reshape(-1, N)                                 # [2KB, N]
-        x2dq = x2 * np.repeat(s2, 32, axis=0)[:K][None]
+    E = x2.shape[0]
+    sc = c["scale"]
+    sc4 = sc if sc.ndim == 4 else np.broadcast_to(sc, (E,) + sc.shape)   # per-expert view
+    x2dq = np.empty((E, K, x2.shape[1] if c["transpose_x2"] else x2.shape[2]))
+    for e in range(E):
+        if c["transpose_x2"]:
+            N = x2.shape[1]
+            s2 = np.exp2(sc4[e].astype(np.float64) - 127).reshape(N, -1)       # [N, 2KB]
+            x2dq[e] = (x2[e] * np.repeat(s2, 32, axis=1)[:, :K]).T
+        else:
+            N = x2.shape[2]
+            s3 = np.exp2(sc4[e].astype(np.float64) - 127)                        # [KB, N, 2]
+            s2 = np.moveaxis(s3, 2, 1).reshape(-1, N)                             # [2KB, N]
+            x2dq[e] = x2[e] * np.repeat(s2, 32, axis=0)[:K]
     counts = (np.diff(np.concatenate([[0], c["group_list"]])) if c["group_list_type"] == 0
               else c["group_list"])
     out = c["out_init"].astype(np.float64).copy()

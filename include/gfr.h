@@ -93,6 +93,11 @@ typedef struct gfr_options {
     /* K-split factor for the atomic mode; 0 = chosen on the device from the
      * routed work size.  Ignored (1) in deterministic mode. */
     int split_k;
+    /* 0: scale is shared by all experts (3-D, [P1] §3.1).  1: scale carries a
+     * leading expert axis ([P3] Atlas 350 scale notes: (e, n, ceil(k/64), 2)
+     * when transpose_x2, by the same reading (e, ceil(k/64), n, 2)
+     * otherwise); expert e's rows use slice e. */
+    int scale_per_expert;
 } gfr_options;
 
 /*
@@ -101,7 +106,8 @@ typedef struct gfr_options {
  *  x1              [M, K] FP8 (fp8_kind), routed tokens sorted by expert.
  *  x2              [E, K, N] FP8, or [E, N, K] when transpose_x2 != 0.
  *  scale           E8M0 bytes, [ceil(K/64), N, 2], or [N, ceil(K/64), 2] when
- *                  transpose_x2 != 0; shared by all experts ([P1] §3.1).
+ *                  transpose_x2 != 0; shared by all experts ([P1] §3.1), or
+ *                  with a leading [E] axis (gfr_options.scale_per_expert).
  *  pertoken_scale  E8M0 bytes, [M, ceil(K/64), 2].
  *  group_list      int64 [E], format per group_list_type.
  *  logit           float32 [M], or NULL for weight 1 ([P1] §5.1 has_logit).

@@ -31,7 +31,7 @@ class GfrError(RuntimeError):
 class GfrOptions(ctypes.Structure):
     _fields_ = [("deterministic", ctypes.c_int), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p),
-                ("split_k", ctypes.c_int)]
+                ("split_k", ctypes.c_int), ("scale_per_expert", ctypes.c_int)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -67,7 +67,7 @@ def status_string(code: int) -> str:
 
 
 def workspace_size(M: int, K: int, N: int, E: int, batch: int, deterministic: bool = False) -> int:
-    opts = GfrOptions(int(deterministic), None, 0, None, 0)
+    opts = GfrOptions(int(deterministic), None, 0, None, 0, 0)
     n = ctypes.c_size_t(0)
     rc = load_library().gfr_workspace_size(M, K, N, E, batch, ctypes.byref(opts), ctypes.byref(n))
     if rc:
@@ -92,7 +92,7 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
 
     x1 [M,K] / x2 [E,K,N] (or [E,N,K] when transpose_x2) are float8_e4m3fn or
     float8_e5m2; scale / pertoken_scale hold E8M0 codes (uint8 or
-    float8_e8m0fnu); group_list int64 [E]; logit float32 [M] or None;
+    float8_e8m0fnu); a 4-D scale (leading expert axis) is per expert; group_list int64 [E]; logit float32 [M] or None;
     row_index int64 [M]; shared_input bfloat16 [R,N] or None; out float32
     [batch,N].  ``status`` (int32 CUDA tensor, 1 element) receives device-side
     data-error bits.  ``workspace`` (uint8 CUDA tensor) is allocated here when
@@ -111,7 +111,10 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
         _need(x2.shape[1] == K, "x2 [E,K,N] does not match K")
     KB = (K + 63) // 64
     _need(scale.dtype in _E8M0 and pertoken_scale.dtype in _E8M0, "scales must be E8M0 bytes")
-    _need(tuple(scale.shape) == ((N, KB, 2) if transpose_x2 else (KB, N, 2)), "bad scale shape")
+    s3 = (N, KB, 2) if transpose_x2 else (KB, N, 2)
+    per_expert = scale.dim() == 4
+    _need(tuple(scale.shape) == ((E,) + s3 if per_expert else s3),
+          "bad scale shape (3-D shared, or 4-D with a leading expert axis)")
     _need(tuple(pertoken_scale.shape) == (M, KB, 2), "bad pertoken_scale shape")
     _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
     _need(row_index.dtype == torch.int64 and tuple(row_index.shape) == (M,), "bad row_index")
@@ -140,7 +143,7 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
     opts = GfrOptions(int(bool(deterministic)), _ptr(workspace), ws_bytes, _ptr(status),
-                      int(split_k))
+                      int(split_k), int(per_expert))
     with torch.cuda.device(dev):
         rc = lib.gmm_finalize_routing_ex(
             _ptr(x1), _ptr(x2), _ptr(scale), _ptr(pertoken_scale), _ptr(group_list),

@@ -99,6 +99,8 @@ int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale
     if (rc != GFR_OK) return rc;
     if (N == 0 || batch == 0) return GFR_OK;  // empty output: nothing to do
     const bool det = opts && opts->deterministic;
+    const int per_expert = opts ? opts->scale_per_expert : 0;
+    if (per_expert != 0 && per_expert != 1) return GFR_ERR_BAD_ARG;
     if (det) {
         const gfr::DetLayout d = gfr::det_layout(M, N, batch);
         if (!opts->workspace || opts->workspace_bytes < d.total)
@@ -129,6 +131,7 @@ int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale
     p.batch = static_cast<int32_t>(batch);
     p.group_list_type = group_list_type;
     p.split_k = opts ? opts->split_k : 0;
+    p.scale_e_stride = per_expert ? (K / 32) * N : 0;   // ceil(K/64) * N * 2 bytes
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (det) {

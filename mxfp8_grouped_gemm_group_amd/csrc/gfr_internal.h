@@ -42,6 +42,7 @@ struct FusedParams {
     int32_t M, K, N, E, batch;
     int32_t group_list_type;
     int32_t split_k;           // 0: chosen on the device
+    int64_t scale_e_stride;    // bytes between experts' weight scales (0: shared)
 };
 
 // Deterministic-mode workspace layout (all offsets 256-byte aligned):

@@ -469,7 +469,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
     const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * K * N, static_cast<int64_t>(K) * N);
-    const rsrc_t rsb = make_rsrc(p.scale, static_cast<int64_t>(KS) * N);
+    const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     const int u0 = COOP ? w * kTileLoads : 0;   // first tile load this wave issues
 
     // Weight-tile load offsets (lane part) and weight-scale offsets.  Columns

@@ -54,6 +54,7 @@ class Workload:
     exact: bool = False                  # integer-valued variant, exact in FP32
     seed: int = 0
     topk: int = 0                        # informational (M = batch * topk)
+    scale_per_expert: bool = False       # weight scales with a leading expert axis
 
     @property
     def fp8_kind(self) -> int:
@@ -82,7 +83,7 @@ class Workload:
         M_r = int(c.sum())
         K, N = self.K, self.N
         kb32 = 2 * ((K + 63) // 64)
-        b = active * K * N + M_r * K + M_r * kb32 + N * kb32
+        b = active * K * N + M_r * K + M_r * kb32 + N * kb32 * (active if self.scale_per_expert else 1)
         b += (4 * M_r if self.logit != "none" else 0) + 8 * M_r + 8 * self.E
         b += 8 * self.batch * N + 2 * self.R * N
         return b
@@ -146,9 +147,18 @@ SMALL_BIG_T = _reg(Workload("small_big_t", batch=86, M=516, K=640, N=352, E=4, f
                             transpose_x2=True, groups=(141, 5, 300, 70), group_list_type=0,
                             exp_range=(-4, 4), row_index="perm", seed=1024))
 
+# Per-expert weight scales (a leading expert axis on scale; CANN V3 Atlas 350
+# scale notes).
+SMALL_N_PE = _reg(replace(SMALL_N, name="small_n_pe", scale_per_expert=True, seed=1031))
+SMALL_BIG_T_PE = _reg(replace(SMALL_BIG_T, name="small_big_t_pe", scale_per_expert=True,
+                              seed=1032))
+C3_PE = _reg(replace(C3, name="c3_pe", scale_per_expert=True, seed=1033))
+C5_PE = _reg(replace(C5, name="c5_pe", scale_per_expert=True, seed=1035))
+
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
-for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T):
+for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_N_PE,
+              SMALL_BIG_T_PE):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))
 
@@ -224,6 +234,8 @@ def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
     lo, hi = (0, 1) if w.exact else w.exp_range
     pts = (127 + rng.integers(lo, hi + 1, size=(M, KB, 2))).astype(np.uint8)
     sc_shape = (N, KB, 2) if w.transpose_x2 else (KB, N, 2)
+    if w.scale_per_expert:
+        sc_shape = (E,) + sc_shape
     sc = (127 + rng.integers(lo, hi + 1, size=sc_shape)).astype(np.uint8)
 
     counts = _counts(w)

@@ -91,6 +91,11 @@ def test_deterministic_alignment():
     assert _call(out=0x10004, opts=ctypes.byref(opts)) == 5
 
 
+def test_scale_per_expert_flag_is_validated():
+    opts = GfrOptions(0, None, 0, None, 0, 2)
+    assert _call(opts=ctypes.byref(opts)) == 7
+
+
 def test_empty_output_is_a_noop():
     # N = 0 or batch = 0: valid per the empty-tensor rules, returns before any launch
     assert _call(N=0) == 0

@@ -26,7 +26,7 @@ def test_zipf_routing_has_empty_and_heavy_experts(name):
 
 
 @pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact", "small_big_n",
-                                  "small_big_t_exact"])
+                                  "small_big_t_exact", "small_n_pe", "small_big_t_pe"])
 def test_make_inputs_shapes_and_determinism(name):
     w = WORKLOADS[name]
     a = make_inputs(w)
@@ -34,7 +34,8 @@ def test_make_inputs_shapes_and_determinism(name):
     KB = (w.K + 63) // 64
     assert a["x1"].shape == (w.M, w.K)
     assert a["x2"].shape == ((w.E, w.N, w.K) if w.transpose_x2 else (w.E, w.K, w.N))
-    assert a["scale"].shape == ((w.N, KB, 2) if w.transpose_x2 else (KB, w.N, 2))
+    s3 = (w.N, KB, 2) if w.transpose_x2 else (KB, w.N, 2)
+    assert a["scale"].shape == (((w.E,) + s3) if w.scale_per_expert else s3)
     assert a["pertoken_scale"].shape == (w.M, KB, 2)
     assert a["out"].shape == (w.batch, w.N) and a["out"].dtype == torch.float32
     assert a["shared_input"].shape == (w.R, w.N)

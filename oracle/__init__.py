@@ -57,7 +57,8 @@ def _lib() -> ctypes.CDLL:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build()
         lib = ctypes.CDLL(_LIB)
-        for name in ("oracle_decode_e4m3fn", "oracle_decode_e5m2", "oracle_decode_e8m0"):
+        for name in ("oracle_decode_e4m3fn", "oracle_decode_e5m2", "oracle_decode_e8m0",
+                     "oracle_decode_e2m1"):
             f = getattr(lib, name)
             f.argtypes = [ctypes.c_uint8]
             f.restype = ctypes.c_double
@@ -84,14 +85,27 @@ def _lib() -> ctypes.CDLL:
 
 
 def decode(kind: str, code: int) -> float:
-    """Decode one code; kind in {'e4m3fn', 'e5m2', 'e8m0', 'bf16'}."""
+    """Decode one code; kind in {'e4m3fn', 'e5m2', 'e2m1', 'e8m0', 'bf16'}."""
     lib = _lib()
     return {
         "e4m3fn": lib.oracle_decode_e4m3fn,
         "e5m2": lib.oracle_decode_e5m2,
+        "e2m1": lib.oracle_decode_e2m1,
         "e8m0": lib.oracle_decode_e8m0,
         "bf16": lib.oracle_decode_bf16,
     }[kind](code)
+
+
+E2M1 = 2   # element kind of the MXFP4 variant: two E2M1 codes per byte
+
+
+def _logical_sizes(x1, x2, transpose_x2, fp8_kind):
+    """(M, K, N, E) from the stored arrays; E2M1 rows hold two elements per byte."""
+    per = 2 if fp8_kind == E2M1 else 1
+    M, K = x1.shape[0], x1.shape[1] * per
+    E = x2.shape[0]
+    N = x2.shape[1] if transpose_x2 else x2.shape[2] * per
+    return M, K, N, E
 
 
 def expert_ranges(group_list, group_list_type: int, M: int):
@@ -120,7 +134,8 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
                          rows=None):
     """Run the oracle on host numpy arrays.
 
-    x1, x2, scale, pertoken_scale: uint8 codes (FP8 / E8M0); shared_input:
+    x1, x2, scale, pertoken_scale: uint8 codes (FP8 / E8M0; with fp8_kind 2
+    x1 and x2 hold two E2M1 codes per byte along their last axis); shared_input:
     uint16 bf16 bit patterns or None; logit: float32 or None; group_list and
     row_index: int64; out_init: float32 [batch, N].  ``scale`` may carry a
     leading expert axis (4-D).  ``rows`` selects output rows (default: all).
@@ -134,9 +149,7 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
     g = np.ascontiguousarray(group_list, dtype=np.int64)
     ri = np.ascontiguousarray(row_index, dtype=np.int64)
     init = np.ascontiguousarray(out_init, dtype=np.float32)
-    M, K = x1.shape
-    E = x2.shape[0]
-    N = x2.shape[1] if transpose_x2 else x2.shape[2]
+    M, K, N, E = _logical_sizes(x1, x2, transpose_x2, fp8_kind)
     batch = init.shape[0]
     assert init.shape == (batch, N)
     scale_per_expert = 1 if scale.ndim == 4 else 0
@@ -177,9 +190,7 @@ def mx_group_slack(x1, x2, scale, pertoken_scale, group_list, group_list_type, l
     pts = _u8(pertoken_scale)
     g = np.ascontiguousarray(group_list, dtype=np.int64)
     ri = np.ascontiguousarray(row_index, dtype=np.int64)
-    M, K = x1.shape
-    E = x2.shape[0]
-    N = x2.shape[1] if transpose_x2 else x2.shape[2]
+    M, K, N, E = _logical_sizes(x1, x2, transpose_x2, fp8_kind)
     lg = None if logit is None else np.ascontiguousarray(logit, dtype=np.float32)
     if rows is None:
         rows_arr, n_rows = None, batch

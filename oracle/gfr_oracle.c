@@ -16,7 +16,8 @@
  *   out[row_index[t], n] += w_t * sum_k  dq1(t,k) * dq2(e(t),k,n)
  *   out[off + r, n]      += shared_input_weight * shared_input[r, n]
  *
- * with dq = FP8 value * 2^(E8M0 byte - 127), one E8M0 scale per 32 consecutive
+ * with dq = FP8 (or, in the MXFP4 variant, FP4 E2M1) value * 2^(E8M0 byte - 127),
+ * one E8M0 scale per 32 consecutive
  * K elements (the reading of the "[ceil(K/64), ..., 2]" scale layout: sub-block
  * j of 64-block b covers k in [64b+32j, 64b+32j+32)), w_t = logit[t] (1 when
  * logit is absent), and e(t) the expert whose group_list range holds t.
@@ -83,6 +84,22 @@ double oracle_decode_e5m2(uint8_t b)
     return s ? -v : v;
 }
 
+/* FP4 E2M1 (the MXFP4 element, [P3] Atlas 350 MX notes): 1 sign, 2 exponent
+ * (bias 1), 1 mantissa bit in the low four bits of c; exponent 0 is
+ * subnormal; no infinities or NaNs. */
+double oracle_decode_e2m1(uint8_t c)
+{
+    int s = (c >> 3) & 1;
+    int e = (c >> 1) & 3;
+    int m = c & 1;
+    double v;
+    if (e == 0)
+        v = (double)m / 2.0;
+    else
+        v = ldexp(1.0 + (double)m / 2.0, e - 1);
+    return s ? -v : v;
+}
+
 /* E8M0 (unsigned, exponent only, bias 127): 2^(b-127); 0xFF is NaN. */
 double oracle_decode_e8m0(uint8_t b)
 {
@@ -137,15 +154,51 @@ int oracle_expert_ranges(const int64_t *group_list, int64_t E, int type,
     return ORACLE_OK;
 }
 
-/* Value of every FP8 code of the chosen kind, and of every E8M0 code, built
- * once per call by the decoders above (a cache of them, nothing more). */
+/* Element kinds: 0 FP8 E4M3FN, 1 FP8 E5M2, 2 FP4 E2M1 (two per byte). */
+#define ORACLE_E2M1 2
+
+/* Value of every element code of the chosen kind, and of every E8M0 code,
+ * built once per call by the decoders above (a cache of them, nothing more). */
 static void decode_tables(int fp8_kind, double fp8v[256], double e8m0v[256])
 {
     for (int c = 0; c < 256; ++c) {
-        fp8v[c] = fp8_kind == 0 ? oracle_decode_e4m3fn((uint8_t)c)
-                                : oracle_decode_e5m2((uint8_t)c);
+        if (fp8_kind == ORACLE_E2M1)
+            fp8v[c] = c < 16 ? oracle_decode_e2m1((uint8_t)c) : NAN;
+        else
+            fp8v[c] = fp8_kind == 0 ? oracle_decode_e4m3fn((uint8_t)c)
+                                    : oracle_decode_e5m2((uint8_t)c);
         e8m0v[c] = oracle_decode_e8m0((uint8_t)c);
     }
+}
+
+/* Bytes of a stored row of `len` elements: one code per byte for FP8, two for
+ * E2M1. */
+static int64_t row_bytes(int64_t len, int fp8_kind)
+{
+    return fp8_kind == ORACLE_E2M1 ? len / 2 : len;
+}
+
+/* Code of element i of a stored row.  E2M1 rows hold element 2j in the low
+ * nibble and element 2j+1 in the high nibble of byte j (the reading of the
+ * MXFP4 packing: pairs along the row's contiguous dimension, which is why the
+ * pages require an even k, and an even n for a non-transposed x2). */
+static uint8_t code_at(const uint8_t *row, int64_t i, int fp8_kind)
+{
+    if (fp8_kind != ORACLE_E2M1)
+        return row[i];
+    const uint8_t b = row[i / 2];
+    return (i & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+}
+
+/* Arguments every entry point accepts: a known kind, and the even sizes the
+ * E2M1 packing needs. */
+static int kind_ok(int fp8_kind, int64_t K, int64_t N, int transpose_x2)
+{
+    if (fp8_kind == 0 || fp8_kind == 1)
+        return 1;
+    if (fp8_kind != ORACLE_E2M1)
+        return 0;
+    return K % 2 == 0 && (transpose_x2 || N % 2 == 0);
 }
 
 /* ---------------------------------------------------------------------------
@@ -190,7 +243,7 @@ int oracle_gmm_finalize_routing(
 {
     if (M < 0 || K <= 0 || N < 0 || E <= 0 || batch < 0 || n_rows < 0)
         return ORACLE_BAD_ARG;
-    if (fp8_kind != 0 && fp8_kind != 1)
+    if (!kind_ok(fp8_kind, K, N, transpose_x2))
         return ORACLE_BAD_ARG;
     if (rows == NULL && n_rows != batch)
         return ORACLE_BAD_ARG;
@@ -265,13 +318,15 @@ int oracle_gmm_finalize_routing(
              * each element's sum is the same sequence either way. */
             const uint8_t *ps_row = pertoken_scale + t * KB * 2;
             const uint8_t *sc = scale + (scale_per_expert ? e * KB * N * 2 : 0);
+            const uint8_t *x1_row = x1 + t * row_bytes(K, fp8_kind);
             if (!transpose_x2) {
-                const uint8_t *w2 = x2 + e * K * N; /* w2[k*N + n] */
                 for (int64_t k = 0; k < K; ++k) {
-                    const double a = fp8v[x1[t * K + k]] *
+                    /* row k of expert e's [K, N] weight */
+                    const uint8_t *w2 = x2 + (e * K + k) * row_bytes(N, fp8_kind);
+                    const double a = fp8v[code_at(x1_row, k, fp8_kind)] *
                                      e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
                     for (int64_t n = 0; n < N; ++n) {
-                        const double bw = fp8v[w2[k * N + n]] *
+                        const double bw = fp8v[code_at(w2, n, fp8_kind)] *
                                           e8m0v[sc[((k / 64) * N + n) * 2 + (k / 32) % 2]];
                         const double term = a * bw;
                         acc[n] += term;
@@ -279,12 +334,13 @@ int oracle_gmm_finalize_routing(
                     }
                 }
             } else {
-                const uint8_t *w2 = x2 + e * N * K; /* w2[n*K + k] */
                 for (int64_t n = 0; n < N; ++n) {
+                    /* row n of expert e's [N, K] weight */
+                    const uint8_t *w2 = x2 + (e * N + n) * row_bytes(K, fp8_kind);
                     for (int64_t k = 0; k < K; ++k) {
-                        const double a = fp8v[x1[t * K + k]] *
+                        const double a = fp8v[code_at(x1_row, k, fp8_kind)] *
                                          e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
-                        const double bw = fp8v[w2[n * K + k]] *
+                        const double bw = fp8v[code_at(w2, k, fp8_kind)] *
                                           e8m0v[sc[(n * KB + k / 64) * 2 + (k / 32) % 2]];
                         const double term = a * bw;
                         acc[n] += term;
@@ -343,7 +399,7 @@ int oracle_mx_group_slack(
     const int64_t *rows, int64_t n_rows, double *slack_out)
 {
     if (M < 0 || K <= 0 || N < 0 || E <= 0 || batch < 0 || n_rows < 0 ||
-        (fp8_kind != 0 && fp8_kind != 1) || (rows == NULL && n_rows != batch))
+        !kind_ok(fp8_kind, K, N, transpose_x2) || (rows == NULL && n_rows != batch))
         return ORACLE_BAD_ARG;
     const int64_t KB = (K + 63) / 64;
     double fp8v[256], e8m0v[256];
@@ -383,12 +439,15 @@ int oracle_mx_group_slack(
                     double mx = 0.0;
                     int cnt = 0;
                     for (int64_t k = g0; k < g0 + 8 && k < K; ++k) {
-                        const double a = fp8v[x1[t * K + k]] *
-                                         e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
+                        const double a =
+                            fp8v[code_at(x1 + t * row_bytes(K, fp8_kind), k, fp8_kind)] *
+                            e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
                         const double bw = transpose_x2
-                            ? fp8v[x2[e * N * K + n * K + k]] *
+                            ? fp8v[code_at(x2 + (e * N + n) * row_bytes(K, fp8_kind), k,
+                                           fp8_kind)] *
                                   e8m0v[sc[(n * KB + k / 64) * 2 + (k / 32) % 2]]
-                            : fp8v[x2[e * K * N + k * N + n]] *
+                            : fp8v[code_at(x2 + (e * K + k) * row_bytes(N, fp8_kind), n,
+                                           fp8_kind)] *
                                   e8m0v[sc[((k / 64) * N + n) * 2 + (k / 32) % 2]];
                         term[cnt] = fabs(a * bw);
                         if (term[cnt] > mx)

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from tests.tiny_inputs import tiny_case, decode_np, numpy_reference
+from tests.tiny_inputs import E2M1_VALUES, decode_np, numpy_reference, tiny_case, unpack_e2m1
 
 
 # ----------------------------------------------------------------------------
@@ -105,6 +105,65 @@ CASES = [dict(seed=s, E=E, M=M, K=K, N=N, transpose=tr, kind=kd, gtype=gt)
              (1, 3, 32, 2, False, 0, 1), (2, 5, 64, 3, True, 1, 0),
              (3, 8, 96, 5, False, 1, 1), (3, 7, 128, 4, True, 0, 0),
              (2, 6, 160, 5, False, 0, 0), (3, 8, 128, 5, True, 1, 1)])]
+
+
+def test_decode_e2m1_value_set():
+    assert [oracle.decode("e2m1", c) for c in range(16)] == list(E2M1_VALUES)
+    assert math.copysign(1.0, oracle.decode("e2m1", 8)) == -1.0
+
+
+# MXFP4 ([P3] Atlas 350 MX notes): x1 / x2 hold two E2M1 codes per byte along
+# their contiguous axis (element 2j in the low nibble, the reading of the
+# packing); K even, N even when x2 is not transposed.
+FP4_CASES = [dict(seed=100 + s, E=E, M=M, K=K, N=N, transpose=tr, kind=2, gtype=gt)
+             for s, (E, M, K, N, tr, gt) in enumerate([
+                 (1, 3, 32, 2, False, 1), (2, 5, 64, 3, True, 0), (3, 8, 96, 6, False, 1),
+                 (3, 7, 128, 4, True, 0), (2, 6, 192, 8, False, 0)])]
+
+
+@pytest.mark.parametrize("case", FP4_CASES, ids=lambda c: f"s{c['seed']}")
+def test_tiny_fp4_matches_independent_numpy(case):
+    c = tiny_case(**case)
+    got, mag = _run(c)
+    ref = numpy_reference(c)
+    assert np.all(np.abs(got - ref) <= 1e-13 * mag + 1e-300)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_fp4_textbook_plain_matmul(transpose):
+    c = tiny_case(seed=43, E=1, M=6, K=128, N=6, transpose=transpose, kind=2, gtype=1,
+                  groups=[6], batch=6, routing="identity", unit_scales=True,
+                  logit="ones", shared=False)
+    got, _ = _run(c, out_init=np.zeros_like(c["out_init"]))
+    a = E2M1_VALUES[unpack_e2m1(c["x1"])]
+    b = E2M1_VALUES[unpack_e2m1(c["x2"][0])]
+    if transpose:
+        b = b.T
+    assert np.array_equal(got, a @ b)
+
+
+@pytest.mark.parametrize("K,N,transpose,ok", [(64, 3, False, False), (64, 3, True, True),
+                                              (63, 4, True, False), (64, 4, False, True)])
+def test_fp4_packing_needs_even_sizes(K, N, transpose, ok):
+    """The C entry point takes logical sizes: an odd N (non-transposed) or an
+    odd K cannot be packed two per byte and is rejected (-1)."""
+    import ctypes
+    lib = oracle._lib()
+    KB = (K + 63) // 64
+    x1 = np.zeros((1, K), np.uint8)
+    x2 = np.zeros((1, K, N), np.uint8)
+    sc = np.full((KB * N * 2,), 127, np.uint8)
+    pts = np.full((KB * 2,), 127, np.uint8)
+    g = np.array([1], np.int64)
+    ri = np.zeros(1, np.int64)
+    init = np.zeros((1, N), np.float32)
+    res = np.zeros((1, N))
+    mag = np.zeros((1, N))
+    rc = lib.oracle_gmm_finalize_routing(
+        x1.ctypes.data, x2.ctypes.data, sc.ctypes.data, 0, pts.ctypes.data, g.ctypes.data, 1,
+        None, ri.ctypes.data, None, 1.0, 0, 0, init.ctypes.data, int(transpose), 2,
+        1, K, N, 1, 1, None, 1, res.ctypes.data, mag.ctypes.data)
+    assert (rc == 0) == ok and (ok or rc == -1)
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c['seed']}")

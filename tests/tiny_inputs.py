@@ -13,11 +13,35 @@ import torch
 _F8 = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
 
 
+# The FP4 E2M1 value set (OCP Microscaling formats v1.0, element table): codes
+# 0..7 are +0, 0.5, 1, 1.5, 2, 3, 4, 6 and codes 8..15 their negatives.
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def unpack_e2m1(packed):
+    """[..., L/2] bytes -> [..., L] codes, element 2j from the low nibble of byte j."""
+    packed = np.ascontiguousarray(packed)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.uint8)
+    out[..., 0::2] = packed & 15
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def pack_e2m1(codes):
+    """[..., L] codes (0..15) -> [..., L/2] bytes (inverse of unpack_e2m1)."""
+    codes = np.ascontiguousarray(codes).astype(np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
 def decode_np(codes, kind):
-    """Decode raw codes with torch: kind 0/1 (FP8 E4M3FN/E5M2) or 'bf16'."""
+    """Decode raw codes: kind 0/1 (FP8 E4M3FN/E5M2, with torch), 2 (packed
+    E2M1, with the value table) or 'bf16' (with torch)."""
     codes = np.ascontiguousarray(codes)
     if kind == "bf16":
         return torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    if kind == 2:
+        return E2M1_VALUES[unpack_e2m1(codes)]
     return torch.from_numpy(codes).view(_F8[kind]).to(torch.float64).numpy()
 
 
@@ -37,9 +61,13 @@ def tiny_case(seed, E, M, K, N, transpose, kind, gtype, groups=None, batch=None,
               exact=False, per_expert=False):
     rng = np.random.default_rng(seed)
     KB = (K + 63) // 64
-    if exact:
+    x2s = (E, N, K) if transpose else (E, K, N)
+    if kind == 2:   # packed E2M1 along the last axis
+        pool = np.array([0, 2, 4, 10, 12], np.uint8) if exact else np.arange(16, dtype=np.uint8)
+        x1 = pack_e2m1(rng.choice(pool, size=(M, K)))       # exact: 0, +-1, +-2
+        x2 = pack_e2m1(rng.choice(pool, size=x2s))
+    elif exact:
         x1 = _encode(rng.integers(-2, 3, size=(M, K)), kind)
-        x2s = (E, N, K) if transpose else (E, K, N)
         x2 = _encode(rng.integers(-2, 3, size=x2s), kind)
     else:
         fc = _finite_codes(kind)
@@ -93,7 +121,7 @@ def tiny_case(seed, E, M, K, N, transpose, kind, gtype, groups=None, batch=None,
 def numpy_reference(c):
     """Independent float64 formulation (see module docstring)."""
     kind = c["fp8_kind"]
-    x1 = decode_np(c["x1"], kind)
+    x1 = decode_np(c["x1"], kind)      # E2M1: unpacked to [M, K] here
     M, K = x1.shape
     s1 = np.exp2(c["pertoken_scale"].astype(np.float64) - 127).reshape(M, -1)
     x1dq = x1 * np.repeat(s1, 32, axis=1)[:, :K]

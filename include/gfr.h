@@ -62,8 +62,10 @@ enum gfr_status {
     GFR_ERR_HIP = 8              /* a HIP runtime call failed */
 };
 
-/* FP8 element formats of x1 and x2 ([P1] §3.1: FP8 E4M3FN or E5M2). */
-enum gfr_fp8_kind { GFR_FP8_E4M3FN = 0, GFR_FP8_E5M2 = 1 };
+/* Element formats of x1 and x2 ([P1] §3.1: FP8 E4M3FN or E5M2; [P3] Atlas
+ * 350 MX notes: the MXFP4 variant, FP4 E2M1 elements stored two per byte
+ * along the contiguous axis, element 2j in the low nibble of byte j). */
+enum gfr_fp8_kind { GFR_FP8_E4M3FN = 0, GFR_FP8_E5M2 = 1, GFR_FP4_E2M1 = 2 };
 
 /* group_list formats ([P1] §4.3): 0 = prefix sums, expert i owns
  * [group_list[i-1], group_list[i]) with group_list[-1] = 0; 1 = counts, expert
@@ -119,13 +121,17 @@ typedef struct gfr_options {
  *  out             float32 [batch, N]; read as the initial value and updated
  *                  in place ([P1] §3.1, §5.4).
  *  transpose_x2    0 or 1 (scale layout follows it, [P3] Atlas 350 notes).
- *  fp8_kind        gfr_fp8_kind of both x1 and x2.
+ *  fp8_kind        gfr_fp8_kind of both x1 and x2.  With GFR_FP4_E2M1, x1 is
+ *                  [M, K/2] bytes and x2 [E, N, K/2] bytes (packed along K); M,
+ *                  K, N stay element counts.
  *  M, K, N, E, batch, shared_rows: sizes.  M = 0 leaves only the shared term;
  *                  N = 0 or batch = 0 is a no-op ([P3] empty-tensor notes).
  *  stream          hipStream_t.
  *
  * Implementation limits (GFR_ERR_UNSUPPORTED): K % 128 != 0, N % 16 != 0,
- * E outside [1, 1024], M or batch >= 2^31.  x1, x2 and scale must be 16-byte
+ * E outside [1, 1024], M or batch >= 2^31; for GFR_FP4_E2M1 also K % 256 != 0
+ * or transpose_x2 == 0 (the pages allow a non-transposed MXFP4 x2, packed
+ * along N; this implementation takes the transposed layout only).  x1, x2 and scale must be 16-byte
  * aligned (GFR_ERR_BAD_ALIGNMENT).  Atomic mode needs no workspace.
  * Returns a gfr_status.
  */

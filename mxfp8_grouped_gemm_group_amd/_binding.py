@@ -18,7 +18,8 @@ GFR_OK = 0
 DEV_BAD_GROUP_LIST = 0x1
 DEV_BAD_ROW_INDEX = 0x2
 
-_FP8_KIND = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
+_FP8_KIND = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1, torch.float4_e2m1fn_x2: 2}
+_PACKED = torch.float4_e2m1fn_x2   # two E2M1 elements per byte along the last axis
 _E8M0 = (torch.uint8, torch.float8_e8m0fnu)
 
 
@@ -91,7 +92,8 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
     """out += routed expert rows + shared term, in place; returns out.
 
     x1 [M,K] / x2 [E,K,N] (or [E,N,K] when transpose_x2) are float8_e4m3fn or
-    float8_e5m2; scale / pertoken_scale hold E8M0 codes (uint8 or
+    float8_e5m2, or float4_e2m1fn_x2 (MXFP4: the last axis holds half as many
+    bytes as elements); scale / pertoken_scale hold E8M0 codes (uint8 or
     float8_e8m0fnu); a 4-D scale (leading expert axis) is per expert; group_list int64 [E]; logit float32 [M] or None;
     row_index int64 [M]; shared_input bfloat16 [R,N] or None; out float32
     [batch,N].  ``status`` (int32 CUDA tensor, 1 element) receives device-side
@@ -99,15 +101,16 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
     the deterministic mode needs one and none is given.
     """
     lib = load_library()
-    _need(x1.dtype in _FP8_KIND and x2.dtype == x1.dtype, "x1/x2 must share an FP8 dtype")
+    _need(x1.dtype in _FP8_KIND and x2.dtype == x1.dtype, "x1/x2 must share an FP8 / FP4 dtype")
     _need(x1.dim() == 2 and x2.dim() == 3, "x1 must be 2-D and x2 3-D")
-    M, K = x1.shape
+    per = 2 if x1.dtype == _PACKED else 1     # elements per stored byte along the last axis
+    M, K = x1.shape[0], x1.shape[1] * per
     E = x2.shape[0]
     if transpose_x2:
         N = x2.shape[1]
-        _need(x2.shape[2] == K, "x2 [E,N,K] does not match K")
+        _need(x2.shape[2] * per == K, "x2 [E,N,K] does not match K")
     else:
-        N = x2.shape[2]
+        N = x2.shape[2] * per
         _need(x2.shape[1] == K, "x2 [E,K,N] does not match K")
     KB = (K + 63) // 64
     _need(scale.dtype in _E8M0 and pertoken_scale.dtype in _E8M0, "scales must be E8M0 bytes")

@@ -105,13 +105,17 @@ constexpr int kCoopRows = kTileM * kWavesPerBlock;   // 128
 
 // Rows of one cooperative unit: experts with more than 128 rows use 256-row
 // groups (each wave two 32-row fragments: twice the MFMAs per streamed and
-// per LDS-read weight step), smaller ones 128-row groups.
+// per LDS-read weight step), smaller ones 128-row groups.  FP4 units keep one
+// fragment (two would not fit the register file next to FP4's 8 MFMAs per
+// step).
+template <int FMT>
 __device__ __forceinline__ int coop_group_rows(int cnt) {
-    return cnt > kCoopRows ? 2 * kCoopRows : kCoopRows;
+    return (FMT != 4 && cnt > kCoopRows) ? 2 * kCoopRows : kCoopRows;
 }
 
 constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 
+template <int FMT>
 __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
                                 int64_t *s_scan) {
     const int tid = threadIdx.x;
@@ -162,7 +166,7 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         }
         run += c[i];
         const int64_t si = cnt >= kCoopMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
-        const int gr = coop_group_rows(cnt);
+        const int gr = coop_group_rows<FMT>(cnt);
         const int64_t li = cnt >= kCoopMinRows ? ((cnt + gr - 1) / gr) * n_tiles : 0;
         items[i] = si | (li << 32);
         isum += items[i];
@@ -323,13 +327,13 @@ constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
 // Scales are loaded as the aligned dword that holds them and the byte is
 // selected when the step is consumed: a byte load would be zero-extended where
 // the compiler chooses, which can force an early wait on the load.
-template <bool KN, int RF>
+template <bool KN, int RF, bool FP4>
 struct StepRegs {
-    v4i a[RF][KN ? 2 : 4];    // x1 row bytes of fragment f: [K,N] K [16g, +16),
-                              // [32 + 16g, +16) of the 64-K step; [N,K] the
-                              // same for both 64-K halves
-    uint32_t sa[RF];          // dword holding the x1 scales of the step
-    uint32_t sb[KN ? 4 : 2];  // dword holding the weight scales of column group j
+    v4i a[RF][KN ? 2 : 4];    // x1 row bytes of fragment f: [K,N] bytes [16g, +16),
+                              // [32 + 16g, +16) of the step's 64; [N,K] bytes
+                              // 32q + 16g (+16) of the step's 128
+    uint32_t sa[RF][FP4 ? 2 : 1];          // x1 scale bytes of the step
+    uint32_t sb[KN ? 4 : 2][FP4 ? 2 : 1];  // weight scale bytes of column group j
 };
 
 // Destination row and weight of the tile's 32 (or 64) rows, loaded when the
@@ -439,6 +443,13 @@ template <int FMT, bool KN, bool COOP, int RF>
 __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                             int ks0, int ks1, bool store_rows, char *ring, int w) {
     static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
+    // FP4 E2M1 (MFMA format 4): elements packed two per byte along K; only the
+    // [N, K] weight layout.  An FP4 MFMA operand is 16 bytes per lane: lane
+    // (c, g) holds K [32g, 32g + 32) of its row / column, nibble i = K 32g + i
+    // (low nibble first) -- measured with one-hot operands against an FP8
+    // operand of known layout.
+    constexpr bool FP4 = FMT == 4;
+    static_assert(!(FP4 && KN), "FP4 weights only in the [N, K] layout");
     constexpr int D = !COOP ? kStages : RF == 2 ? 4 : (KN ? kCoopStagesKN : kCoopStagesNK);
     constexpr int kTileLoads = COOP ? kBLoadsPerStep / kWavesPerBlock : kBLoadsPerStep;
     // The item is wave-uniform; say so, so that descriptors and offsets stay
@@ -453,6 +464,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
+    const int Kb = FP4 ? K / 2 : K;    // bytes of one x1 row / one [N, K] weight column
     // x1 rows of this tile; padding rows read row 0 and are zeroed before use
     // (a cooperative wave past the expert's last row has mcount <= 0: its
     // loads have an empty range and return zeros, its epilogue writes nothing)
@@ -463,12 +475,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     for (int f = 0; f < RF; ++f) {
         arow_ok[f] = kTileM * f + c < mcount;
         const int arow = arow_ok[f] ? kTileM * f + c : 0;
-        va[f] = arow * K + 16 * g;
+        va[f] = arow * Kb + 16 * g;
         vsa[f] = arow * KS;       // + (2 ks) & ~3 or 4 ks: KS is a multiple of 4
     }
-    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * Kb, static_cast<int64_t>(mcount) * Kb);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
-    const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * K * N, static_cast<int64_t>(K) * N);
+    const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * Kb * N, static_cast<int64_t>(Kb) * N);
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     const int u0 = COOP ? w * kTileLoads : 0;   // first tile load this wave issues
 
@@ -508,7 +520,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             const int u = u0 + uu;
             const int tcol = 8 * u + (lane >> 3);
             const int col = n0 + tcol;
-            vb[uu] = (col < N ? col : n0) * K + 16 * ((lane & 7) ^ ((tcol >> 1) & 7));
+            vb[uu] = (col < N ? col : n0) * Kb + 16 * ((lane & 7) ^ ((tcol >> 1) & 7));
         }
         // scale bytes (col, 32-block 4ks + b) of [N, K/64, 2]: the aligned
         // dword at col * KS + 4 ks holds the step's four
@@ -526,29 +538,46 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     for (int f = 0; f < RF; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[f][j] = v16f{};
-    StepRegs<KN, RF> regs[D];
-    constexpr int kStep = KN ? kStepK : kStepKNK;    // K elements per step
+    StepRegs<KN, RF, FP4> regs[D];
+    constexpr int kStepB = KN ? kStepK : kStepKNK;   // bytes of a row (column) per step
     constexpr int kAL = KN ? 2 : 4;                  // x1 loads per step
     constexpr int kSB = KN ? 4 : 2;                  // weight-scale loads per step
+    // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4 (FP8) or 8 (FP4)
+    constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
 
     auto issue = [&](int ks, int slot) {
-        const int k0 = ks * kStep;
+        const int k0 = ks * kStepB;
         __builtin_amdgcn_sched_barrier(0);
-        StepRegs<KN, RF> &r = regs[slot];
+        StepRegs<KN, RF, FP4> &r = regs[slot];
 #pragma unroll
         for (int f = 0; f < RF; ++f)
 #pragma unroll
             for (int q = 0; q < kAL; ++q)
                 r.a[f][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[f], k0 + 32 * q, 0);
         // x1 scale bytes of the step: [K,N] (2 ks + g) & 3 of the dword at
-        // (2 ks) & ~3; [N,K] bytes 0..3 of the dword at 4 ks
+        // (2 ks) & ~3; [N,K] the step's kBlk bytes at kBlk ks
 #pragma unroll
-        for (int f = 0; f < RF; ++f)
-            r.sa[f] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f], KN ? (2 * ks) & ~3 : 4 * ks, 0);
+        for (int f = 0; f < RF; ++f) {
+            if constexpr (FP4) {
+                const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[f], kBlk * ks, 0);
+                r.sa[f][0] = v.x;
+                r.sa[f][1] = v.y;
+            } else {
+                r.sa[f][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f],
+                                                                  KN ? (2 * ks) & ~3 : kBlk * ks, 0);
+            }
+        }
 #pragma unroll
-        for (int j = 0; j < kSB; ++j)
-            r.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
-                                                           KN ? ks * 2 * N : 4 * ks, 0);
+        for (int j = 0; j < kSB; ++j) {
+            if constexpr (FP4) {
+                const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[j], kBlk * ks, 0);
+                r.sb[j][0] = v.x;
+                r.sb[j][1] = v.y;
+            } else {
+                r.sb[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
+                                                                  KN ? ks * 2 * N : kBlk * ks, 0);
+            }
+        }
         // (the instruction's immediate offset would move both addresses, so
         // each 1 KB destination gets its own LDS pointer)
 #pragma unroll
@@ -590,7 +619,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     };
 
     auto mma = [&](int slot, const BTile &b, bool live, int ks) {
-        StepRegs<KN, RF> &r = regs[slot];
+        StepRegs<KN, RF, FP4> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
 #pragma unroll
@@ -599,12 +628,29 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             if constexpr (KN) {
                 const v8i a = on ? cat(r.a[f][0], r.a[f][1]) : v8i{};
                 // byte (2 ks + g) & 3 of the x1 scale dword
-                const uint32_t sa = r.sa[f] >> (8 * (2 * (ks & 1) + g));
+                const uint32_t sa = r.sa[f][0] >> (8 * (2 * (ks & 1) + g));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
                                     b[4 * j + 2].x, b[4 * j + 2].y, b[4 * j + 3].x, b[4 * j + 3].y};
-                    acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j] >> sb_shift);
+                    acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
+                }
+            } else if constexpr (FP4) {
+                // four 64-K sub-steps s, two 32-column groups j; operand =
+                // 16 bytes (chunk 2s + g of the lane's row / column); scale of
+                // 32-block 8 ks + 2 s + g = byte 2 s + g of the step's 8; odd
+                // sub-steps accumulate into acc[f][2 + j] (fewer back-to-back
+                // dependent MFMAs), summed before the epilogue
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const v4i z = {0, 0, 0, 0};
+                    const v8i a = on ? cat(r.a[f][s4], z) : v8i{};
+                    const int shf = 8 * (2 * (s4 & 1) + g);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[f][j + 2 * (s4 & 1)] =
+                            mfma<FMT, 0>(a, cat(b[2 * s4 + j], z), acc[f][j + 2 * (s4 & 1)],
+                                         r.sa[f][s4 >> 1] >> shf, r.sb[j][s4 >> 1] >> shf);
                 }
             } else {
                 // two 64-K halves s, two 32-column groups j; the scale of
@@ -616,7 +662,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         acc[f][j] = mfma<FMT, 0>(a, cat(b[2 * (2 * s2) + j], b[2 * (2 * s2 + 1) + j]),
-                                                 acc[f][j], r.sa[f] >> shf, r.sb[j] >> shf);
+                                                 acc[f][j], r.sa[f][0] >> shf, r.sb[j][0] >> shf);
                 }
             }
         }
@@ -666,6 +712,13 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
     // Drain the trailing re-reads before the ring is reused.
     wait_vmcnt<0>();
+    if constexpr (FP4) {
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+            acc[f][0] += acc[f][2];
+            acc[f][1] += acc[f][3];
+        }
+    }
     epilogue<KN ? 4 : 2, RF>(p, acc, m0, n0, store_rows, rinfo);
 }
 
@@ -718,11 +771,13 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
     constexpr int kTN = TRANS ? kTileNNK : kTileN;   // columns per item
     const int n_tiles = (p.N + kTN - 1) / kTN;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
-    build_work_list(p, n_tiles, wl, s_scan);
+    build_work_list<FMT>(p, n_tiles, wl, s_scan);
     if (p.det_total && blockIdx.x == 0 && threadIdx.x == 0) *p.det_total = wl.routed_tokens;
 
     const bool store_rows = p.wbuf != nullptr;
-    const int k_steps = p.K / (TRANS ? kStepKNK : kStepK);
+    // K elements per step: 64 ([K,N] FP8), 128 ([N,K] FP8), 256 ([N,K] FP4):
+    // one step always moves 8 KB of the weight tile
+    const int k_steps = p.K / (FMT == 4 ? 2 * kStepKNK : TRANS ? kStepKNK : kStepK);
     const int blocks = gridDim.x;
     int S = p.split_k;
     const int base_units = wl.litems + (wl.sitems + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -774,7 +829,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
             const int e_pref = __builtin_amdgcn_readfirstlane(s_lpref[e]);
-            const int gr = coop_group_rows(e_cnt);
+            const int gr = coop_group_rows<FMT>(e_cnt);
             const int mg_count = (e_cnt + gr - 1) / gr;
             const int64_t local = u - static_cast<int64_t>(e_pref) * S;
             const int mg = static_cast<int>(local % mg_count);
@@ -787,9 +842,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            if (gr > kCoopRows)
-                routed_item<FMT, !TRANS, true, 2>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
-                                                  s_ring, w);
+            if (FMT != 4 && gr > kCoopRows)
+                routed_item<FMT, !TRANS, true, FMT == 4 ? 1 : 2>(p, e, m0, mcount, nt * kTN, ks0,
+                                                                 ks1, store_rows, s_ring, w);
             else
                 routed_item<FMT, !TRANS, true, 1>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
                                                   s_ring, w);
@@ -996,6 +1051,8 @@ DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
 
 hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
                         hipStream_t stream) {
+    if (fp8_kind == GFR_FP4_E2M1)   // the host admits the [N, K] layout only
+        return launch_fused_t<4, true>(p, stream);
     if (fp8_kind == GFR_FP8_E4M3FN)
         return transpose_x2 ? launch_fused_t<0, true>(p, stream) : launch_fused_t<0, false>(p, stream);
     return transpose_x2 ? launch_fused_t<1, true>(p, stream) : launch_fused_t<1, false>(p, stream);

@@ -27,8 +27,9 @@ from typing import Dict, Optional, Sequence, Tuple, Union
 import numpy as np
 import torch
 
-FP8_DTYPES = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
-FP8_KIND = {"e4m3fn": 0, "e5m2": 1}
+FP8_DTYPES = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2,
+              "e2m1": torch.float4_e2m1fn_x2}
+FP8_KIND = {"e4m3fn": 0, "e5m2": 1, "e2m1": 2}
 
 
 @dataclass(frozen=True)
@@ -40,7 +41,7 @@ class Workload:
     N: int
     E: int
     M: int
-    fp8: str = "e4m3fn"                 # "e4m3fn" | "e5m2"
+    fp8: str = "e4m3fn"                 # "e4m3fn" | "e5m2" | "e2m1" (MXFP4, packed)
     transpose_x2: bool = False
     group_list_type: int = 1             # 0 prefix sums, 1 counts
     groups: Union[str, Tuple] = "uniform"  # "uniform" | ("zipf", s) | explicit counts
@@ -83,7 +84,9 @@ class Workload:
         M_r = int(c.sum())
         K, N = self.K, self.N
         kb32 = 2 * ((K + 63) // 64)
-        b = active * K * N + M_r * K + M_r * kb32 + N * kb32 * (active if self.scale_per_expert else 1)
+        eb = 0.5 if self.fp8 == "e2m1" else 1   # bytes per element of x1 / x2
+        b = int(eb * (active * K * N + M_r * K))
+        b += M_r * kb32 + N * kb32 * (active if self.scale_per_expert else 1)
         b += (4 * M_r if self.logit != "none" else 0) + 8 * M_r + 8 * self.E
         b += 8 * self.batch * N + 2 * self.R * N
         return b
@@ -155,10 +158,19 @@ SMALL_BIG_T_PE = _reg(replace(SMALL_BIG_T, name="small_big_t_pe", scale_per_expe
 C3_PE = _reg(replace(C3, name="c3_pe", scale_per_expert=True, seed=1033))
 C5_PE = _reg(replace(C5, name="c5_pe", scale_per_expert=True, seed=1035))
 
+# MXFP4 ([P3] Atlas 350 MX notes): E2M1 x1 and transposed x2, two elements per
+# byte; K a multiple of 256.
+SMALL_T_FP4 = _reg(replace(SMALL_T, name="small_t_fp4", fp8="e2m1", K=768, seed=1041))
+SMALL_BIG_T_FP4 = _reg(replace(SMALL_BIG_T, name="small_big_t_fp4", fp8="e2m1", K=768,
+                               seed=1042))
+C2_FP4 = _reg(replace(C2, name="c2_fp4", fp8="e2m1", seed=1043))
+C3_FP4T = _reg(replace(C3, name="c3_fp4t", fp8="e2m1", transpose_x2=True, seed=1044))
+C5_FP4 = _reg(replace(C5, name="c5_fp4", fp8="e2m1", seed=1045))
+
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_N_PE,
-              SMALL_BIG_T_PE):
+              SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))
 
@@ -211,6 +223,25 @@ def _fp8_from_normal(shape, dtype, gen, device, exact: bool) -> torch.Tensor:
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dtype)
 
 
+# E2M1 magnitudes by code 0..7 and the midpoints between them: a value goes to
+# the nearest code (input drawing only; the operator never encodes).
+_E2M1_MID = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def _e2m1_from_normal(shape, gen, device, exact):
+    """N(0,1) (or, exact: uniform over {0, +-1, +-2}) rounded to E2M1 codes and
+    packed two per byte along the last axis (element 2j in the low nibble)."""
+    if exact:
+        v = torch.randint(-2, 3, shape, generator=gen, device=device).to(torch.float32)
+    else:
+        v = torch.randn(shape, generator=gen, device=device)
+    mid = torch.tensor(_E2M1_MID, device=device)
+    code = torch.bucketize(v.abs(), mid).to(torch.uint8)
+    code = code | ((v < 0) & (code > 0)).to(torch.uint8) << 3
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous()          # uint8; the caller views it as float4_e2m1fn_x2
+
+
 def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
     """Draw one invocation's inputs.  Returns a dict keyed by argument name.
 
@@ -225,11 +256,19 @@ def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
     M, K, N, E, B = w.M, w.K, w.N, w.E, w.batch
     KB = (K + 63) // 64
 
-    x1 = _fp8_from_normal((M, K), dt, gen, device, w.exact)
     x2_shape = (N, K) if w.transpose_x2 else (K, N)
-    x2 = torch.empty((E,) + x2_shape, dtype=dt, device=device)
-    for e in range(E):  # per expert, so large configs never hold an FP32 copy
-        x2[e] = _fp8_from_normal(x2_shape, dt, gen, device, w.exact)
+    if w.fp8 == "e2m1":
+        x1 = _e2m1_from_normal((M, K), gen, device, w.exact).view(dt)
+        x2 = torch.empty((E,) + x2_shape[:-1] + (x2_shape[-1] // 2,), dtype=torch.uint8,
+                         device=device)
+        for e in range(E):
+            x2[e] = _e2m1_from_normal(x2_shape, gen, device, w.exact)
+        x2 = x2.view(dt)
+    else:
+        x1 = _fp8_from_normal((M, K), dt, gen, device, w.exact)
+        x2 = torch.empty((E,) + x2_shape, dtype=dt, device=device)
+        for e in range(E):  # per expert, so large configs never hold an FP32 copy
+            x2[e] = _fp8_from_normal(x2_shape, dt, gen, device, w.exact)
 
     lo, hi = (0, 1) if w.exact else w.exp_range
     pts = (127 + rng.integers(lo, hi + 1, size=(M, KB, 2))).astype(np.uint8)
@@ -292,7 +331,7 @@ def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
 def as_numpy(inputs: dict) -> dict:
     """Host numpy copies of an input dict in the oracle's raw-code form."""
     def u8(x):
-        return x.detach().cpu().contiguous().view(torch.uint8).numpy()
+        return x.detach().contiguous().view(torch.uint8).cpu().numpy()
 
     d = dict(inputs)
     d["x1"] = u8(inputs["x1"])

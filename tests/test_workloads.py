@@ -7,7 +7,8 @@ from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_inputs, as_nu
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "p1_tc_a", "p1_tc_b",
-                                  "p2_ragged", "small_n", "small_t", "small_big_n", "small_big_t"])
+                                  "p2_ragged", "small_n", "small_t", "small_big_n", "small_big_t",
+                                  "small_t_fp4", "c5_fp4"])
 def test_counts(name):
     w = WORKLOADS[name]
     c = w.counts()
@@ -26,14 +27,16 @@ def test_zipf_routing_has_empty_and_heavy_experts(name):
 
 
 @pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact", "small_big_n",
-                                  "small_big_t_exact", "small_n_pe", "small_big_t_pe"])
+                                  "small_big_t_exact", "small_n_pe", "small_big_t_pe",
+                                  "small_t_fp4", "small_big_t_fp4_exact"])
 def test_make_inputs_shapes_and_determinism(name):
     w = WORKLOADS[name]
     a = make_inputs(w)
     b = make_inputs(w)
     KB = (w.K + 63) // 64
-    assert a["x1"].shape == (w.M, w.K)
-    assert a["x2"].shape == ((w.E, w.N, w.K) if w.transpose_x2 else (w.E, w.K, w.N))
+    per = 2 if w.fp8 == "e2m1" else 1       # MXFP4: two elements per byte along the last axis
+    assert a["x1"].shape == (w.M, w.K // per)
+    assert a["x2"].shape == ((w.E, w.N, w.K // per) if w.transpose_x2 else (w.E, w.K, w.N // per))
     s3 = (w.N, KB, 2) if w.transpose_x2 else (KB, w.N, 2)
     assert a["scale"].shape == (((w.E,) + s3) if w.scale_per_expert else s3)
     assert a["pertoken_scale"].shape == (w.M, KB, 2)
@@ -46,7 +49,10 @@ def test_make_inputs_shapes_and_determinism(name):
     na, nb = as_numpy(a), as_numpy(b)
     for k in ("x1", "x2", "scale", "pertoken_scale", "row_index", "out_init", "logit"):
         assert np.array_equal(na[k], nb[k])
-    if w.exact:
+    if w.exact and w.fp8 == "e2m1":
+        codes = np.concatenate([na["x1"] & 15, na["x1"] >> 4])   # E2M1 0, +-1, +-2 only
+        assert set(np.unique(codes)) <= {0, 2, 4, 10, 12}
+    elif w.exact:
         v = a["x1"].to(torch.float32)
         assert torch.equal(v, v.round()) and v.abs().max() <= 2
 

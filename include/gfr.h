@@ -122,17 +122,18 @@ typedef struct gfr_options {
  *                  in place ([P1] §3.1, §5.4).
  *  transpose_x2    0 or 1 (scale layout follows it, [P3] Atlas 350 notes).
  *  fp8_kind        gfr_fp8_kind of both x1 and x2.  With GFR_FP4_E2M1, x1 is
- *                  [M, K/2] bytes and x2 [E, N, K/2] bytes (packed along K); M,
- *                  K, N stay element counts.
+ *                  [M, K/2] bytes and x2 [E, N, K/2] bytes (transposed, packed
+ *                  along K) or [E, K, N/2] bytes (packed along N); M, K, N stay
+ *                  element counts.
  *  M, K, N, E, batch, shared_rows: sizes.  M = 0 leaves only the shared term;
  *                  N = 0 or batch = 0 is a no-op ([P3] empty-tensor notes).
  *  stream          hipStream_t.
  *
  * Implementation limits (GFR_ERR_UNSUPPORTED): K % 128 != 0, N % 16 != 0,
  * E outside [1, 1024], M or batch >= 2^31; for GFR_FP4_E2M1 also K % 256 != 0
- * or transpose_x2 == 0 (the pages allow a non-transposed MXFP4 x2, packed
- * along N; this implementation takes the transposed layout only).  x1, x2 and scale must be 16-byte
- * aligned (GFR_ERR_BAD_ALIGNMENT).  Atomic mode needs no workspace.
+ * with transpose_x2 == 1, N % 32 != 0 with transpose_x2 == 0.  x1, x2 and
+ * scale must be 16-byte aligned (GFR_ERR_BAD_ALIGNMENT).  Atomic mode needs no
+ * workspace.
  * Returns a gfr_status.
  */
 int gmm_finalize_routing(const void *x1, const void *x2, const uint8_t *scale,

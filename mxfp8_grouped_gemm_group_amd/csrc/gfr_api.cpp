@@ -43,7 +43,9 @@ int validate(const void *x1, const void *x2, const uint8_t *scale, const uint8_t
     if (group_list_type != GFR_GROUP_LIST_CUMSUM && group_list_type != GFR_GROUP_LIST_COUNT)
         return GFR_ERR_BAD_ARG;
     if (transpose_x2 != 0 && transpose_x2 != 1) return GFR_ERR_BAD_ARG;
-    if (fp8_kind == GFR_FP4_E2M1 && (K % 256 != 0 || transpose_x2 != 1))
+    // E2M1 weight rows / columns are read in whole 16-byte chunks: [N, K] steps
+    // are 256 K wide, and a [K, N] row (N / 2 bytes) must be 16-byte aligned.
+    if (fp8_kind == GFR_FP4_E2M1 && (transpose_x2 ? K % 256 != 0 : N % 32 != 0))
         return GFR_ERR_UNSUPPORTED;
     const bool routed = M > 0 && N > 0 && batch > 0;
     if (routed && (!x1 || !x2 || !scale || !pts || !group_list || !row_index))
@@ -70,7 +72,7 @@ const char *gfr_status_string(int status) {
     case GFR_ERR_NULL_ARG: return "a required pointer is NULL";
     case GFR_ERR_BAD_SHAPE: return "negative or inconsistent sizes";
     case GFR_ERR_BAD_OFFSET: return "shared_input_offset out of range (need 0 <= offset and offset + shared_rows <= batch)";
-    case GFR_ERR_UNSUPPORTED: return "unsupported configuration (needs K % 128 == 0, N % 16 == 0, 1 <= E <= 1024, M, batch < 2^31; E2M1 also K % 256 == 0 and transposed weights)";
+    case GFR_ERR_UNSUPPORTED: return "unsupported configuration (needs K % 128 == 0, N % 16 == 0, 1 <= E <= 1024, M, batch < 2^31; E2M1 also K % 256 == 0 with [N,K] weights, N % 32 == 0 with [K,N])";
     case GFR_ERR_BAD_ALIGNMENT: return "x1, x2, scale and shared_input must be 16-byte aligned";
     case GFR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small (query gfr_workspace_size)";
     case GFR_ERR_BAD_ARG: return "unknown fp8_kind, group_list_type or transpose flag";

@@ -277,6 +277,30 @@ __device__ __forceinline__ void lds_wait(v2i (&t)[16]) {
                  : "memory");
 }
 
+// The FP4 [K, N] tile's operands of one step: ds_read_b64_tr_b4.  Measured
+// semantics: in each group of 16 lanes, output lane j receives nibble j of the
+// 8-byte rows addressed by lanes i = 0..15, as its nibble i (low nibble
+// first).  So if lane i points at K row k0 + i, columns c0 .. c0 + 15 (8
+// bytes), lane j gets K rows k0 .. k0 + 15 of column c0 + j: 8 bytes of its
+// operand.  For 32-column group j the reads at a[j] and 16 rows further give
+// operand bytes 0-7 (t[2j]) and 8-15 (t[2j + 1]).
+#define GFR_TR2(J)                                              \
+    "ds_read_b64_tr_b4 %[t" #J "0], %[a" #J "]\n\t"             \
+    "ds_read_b64_tr_b4 %[t" #J "1], %[a" #J "] offset:2048\n\t"
+__device__ __forceinline__ void lds_issue_kn4(const uint32_t (&a)[8], v2i (&t)[16]) {
+    static_assert(16 * kTileN == 2048, "row offset of the second read");
+    asm volatile(GFR_TR2(0) GFR_TR2(1) GFR_TR2(2) GFR_TR2(3) GFR_TR2(4) GFR_TR2(5) GFR_TR2(6)
+                     GFR_TR2(7)
+                 : [t00] "=&v"(t[0]), [t01] "=&v"(t[1]), [t10] "=&v"(t[2]), [t11] "=&v"(t[3]),
+                   [t20] "=&v"(t[4]), [t21] "=&v"(t[5]), [t30] "=&v"(t[6]), [t31] "=&v"(t[7]),
+                   [t40] "=&v"(t[8]), [t41] "=&v"(t[9]), [t50] "=&v"(t[10]), [t51] "=&v"(t[11]),
+                   [t60] "=&v"(t[12]), [t61] "=&v"(t[13]), [t70] "=&v"(t[14]), [t71] "=&v"(t[15])
+                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]),
+                   [a4] "v"(a[4]), [a5] "v"(a[5]), [a6] "v"(a[6]), [a7] "v"(a[7])
+                 : "memory");
+}
+#undef GFR_TR2
+
 // The [N, K] tile's operands of one step: 16-byte reads at a[sh] (column
 // group 0, t[2 sh]) and a[sh] + 4096 (column group 1, t[2 sh + 1]), issued
 // without waiting.
@@ -327,13 +351,13 @@ constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
 // Scales are loaded as the aligned dword that holds them and the byte is
 // selected when the step is consumed: a byte load would be zero-extended where
 // the compiler chooses, which can force an early wait on the load.
-template <bool KN, int RF, bool FP4>
+template <int AL, int RF, int SB, int SW>
 struct StepRegs {
-    v4i a[RF][KN ? 2 : 4];    // x1 row bytes of fragment f: [K,N] bytes [16g, +16),
-                              // [32 + 16g, +16) of the step's 64; [N,K] bytes
-                              // 32q + 16g (+16) of the step's 128
-    uint32_t sa[RF][FP4 ? 2 : 1];          // x1 scale bytes of the step
-    uint32_t sb[KN ? 4 : 2][FP4 ? 2 : 1];  // weight scale bytes of column group j
+    v4i a[RF][AL];       // x1 row bytes of fragment f: FP8 [K,N] bytes [16g, +16),
+                         // [32 + 16g, +16) of the step's 64; [N,K] bytes 32q + 16g
+                         // of the step's 128; FP4 [K,N] bytes [16g, +16) of 32
+    uint32_t sa[RF][SW]; // x1 scale bytes of the step
+    uint32_t sb[SB][SW]; // weight scale bytes of column group j
 };
 
 // Destination row and weight of the tile's 32 (or 64) rows, loaded when the
@@ -379,15 +403,15 @@ __device__ __forceinline__ int row_dst(const FusedParams &p, const RowInfo &ri) 
 // Epilogue: weight each row by its logit and scatter-add (or store) it.
 // acc element (j, r) of lane (c, g) is row 8(r/4) + 4g + r%4 and output column
 // n0 + 32j + c, so each atomic instruction covers 32 adjacent columns.
-template <int NJ, int RF>
-__device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs)[RF][4],
+template <int NJ, int RF, int NA>
+__device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs)[RF][NA],
                                          int m0, int n0, bool store_rows, RowInfo ri) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int c = lane & 31, g = lane >> 5;
     const int my_dst = row_dst(p, ri);
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
-    const v16f (&acc)[4] = accs[f];
+    const v16f (&acc)[NA] = accs[f];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 32 * f + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -435,22 +459,29 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs
 // ---------------------------------------------------------------------------
 constexpr int kCoopStagesKN = 8;   // vmcnt range caps these: (D - 1) * ops < 64
 constexpr int kCoopStagesNK = 8;
+constexpr int kCoopStagesKN4 = 6;  // FP4 [K, N]: eight weight-scale loads per step
 static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
-                  kCoopStagesNK * kSlotBytes <= kWavesPerBlock * kRingBytes,
+                  kCoopStagesNK * kSlotBytes <= kWavesPerBlock * kRingBytes &&
+                  kCoopStagesKN4 * kSlotBytes <= kWavesPerBlock * kRingBytes,
               "cooperative ring fits the block's LDS");
 
 template <int FMT, bool KN, bool COOP, int RF>
 __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                             int ks0, int ks1, bool store_rows, char *ring, int w) {
     static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
-    // FP4 E2M1 (MFMA format 4): elements packed two per byte along K; only the
-    // [N, K] weight layout.  An FP4 MFMA operand is 16 bytes per lane: lane
-    // (c, g) holds K [32g, 32g + 32) of its row / column, nibble i = K 32g + i
-    // (low nibble first) -- measured with one-hot operands against an FP8
-    // operand of known layout.
+    // FP4 E2M1 (MFMA format 4): elements packed two per byte along the
+    // contiguous axis (x1 and [N, K] weights along K, [K, N] weights along N).
+    // An FP4 MFMA operand is 16 bytes per lane: lane (c, g) holds K
+    // [32g, 32g + 32) of its row / column, nibble i = K 32g + i (low nibble
+    // first) -- measured with one-hot operands against an FP8 operand of known
+    // layout.  FP4 [K, N] steps are 64 K x 256 columns (the slot keeps 64 rows
+    // of 128 bytes), eight MFMAs per step.
     constexpr bool FP4 = FMT == 4;
-    static_assert(!(FP4 && KN), "FP4 weights only in the [N, K] layout");
-    constexpr int D = !COOP ? kStages : RF == 2 ? 4 : (KN ? kCoopStagesKN : kCoopStagesNK);
+    constexpr bool KN4 = FP4 && KN;
+    constexpr int D = !COOP ? kStages
+                      : RF == 2 ? 4
+                      : KN4 ? kCoopStagesKN4
+                      : (KN ? kCoopStagesKN : kCoopStagesNK);
     constexpr int kTileLoads = COOP ? kBLoadsPerStep / kWavesPerBlock : kBLoadsPerStep;
     // The item is wave-uniform; say so, so that descriptors and offsets stay
     // in SGPRs (a descriptor in VGPRs turns every buffer load into a loop).
@@ -465,6 +496,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
     const int Kb = FP4 ? K / 2 : K;    // bytes of one x1 row / one [N, K] weight column
+    const int Nb = FP4 ? N / 2 : N;    // bytes of one [K, N] weight row
     // x1 rows of this tile; padding rows read row 0 and are zeroed before use
     // (a cooperative wave past the expert's last row has mcount <= 0: its
     // loads have an empty range and return zeros, its epilogue writes nothing)
@@ -487,11 +519,36 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // Weight-tile load offsets (lane part) and weight-scale offsets.  Columns
     // past N (last partial n-tile) re-read column n0; their results are never
     // written.
-    int vb[KN ? 1 : kTileLoads];
-    int vsb[4];
-    uint32_t tr_addr[4] = {0, 0, 0, 0};   // [K,N]: per 32-column group, slot-relative
+    int vb[KN ? (KN4 ? 2 : 1) : kTileLoads];
+    int vsb[KN4 ? 8 : 4];
+    uint32_t tr_addr[KN4 ? 8 : 4] = {};   // [K,N]: per 32-column group, slot-relative
     int sb_shift = 0;
-    if (KN) {
+    if constexpr (KN4) {
+        // load u, lane l: K row r = 8u + l/8 (row offset in soffset); it fills
+        // physical chunk l%8 of the slot row, which holds logical chunk
+        // (l%8) ^ ((r >> 1) & 7) = (l%8) ^ (4 (u & 1) + l/16): one offset for
+        // even and one for odd loads.  Chunk = 16 bytes = 32 columns.
+        const int n0b = n0 / 2;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int cb = n0b + 16 * ((lane & 7) ^ (4 * par + (lane >> 4)));
+            vb[par] = (lane >> 3) * Nb + (cb < Nb ? cb : n0b);
+        }
+        // transpose reads: lane s of 16-lane group G reads K row 32g + s (16
+        // rows further in the second read), the 8 bytes of columns
+        // 32j + 16(G & 1) .. + 15 (half G & 1 of logical chunk j); the slot
+        // row pitch is 128 bytes, and (row >> 1) & 7 = s >> 1
+        const int G = lane >> 4, sl = lane & 15;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            tr_addr[j] = (32 * g + sl) * kTileN + 16 * (j ^ (sl >> 1)) + 8 * (G & 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = n0 + 32 * j + c;
+            vsb[j] = ((col < N ? col : n0) & ~1) * 2;
+        }
+        sb_shift = 8 * (2 * (c & 1) + g);
+    } else if (KN) {
         // load u, lane l: K row r = 8u + l/8 (row offset in soffset); it fills
         // physical chunk l%8 of the slot row, which holds logical chunk
         // (l%8) ^ ((r >> 1) & 3) = (l%8) ^ ((l >> 4) & 3)
@@ -533,22 +590,26 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
 
     const RowInfo rinfo = load_row_info<RF>(p, m0, mcount);
-    v16f acc[RF][4];
+    constexpr int NA = KN4 ? 8 : 4;   // accumulators per row fragment
+    v16f acc[RF][NA];
 #pragma unroll
     for (int f = 0; f < RF; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[f][j] = v16f{};
-    StepRegs<KN, RF, FP4> regs[D];
-    constexpr int kStepB = KN ? kStepK : kStepKNK;   // bytes of a row (column) per step
-    constexpr int kAL = KN ? 2 : 4;                  // x1 loads per step
-    constexpr int kSB = KN ? 4 : 2;                  // weight-scale loads per step
+        for (int j = 0; j < NA; ++j) acc[f][j] = v16f{};
+    // bytes of an x1 row per step: FP8 [K,N] 64, FP4 [K,N] 32, [N,K] 128 (the
+    // [N,K] weight column moves the same 128 bytes)
+    constexpr int kStepA = KN ? (FP4 ? kStepK / 2 : kStepK) : kStepKNK;
+    constexpr int kAL = KN ? (FP4 ? 1 : 2) : 4;      // x1 loads per step
+    constexpr int kSB = KN4 ? 8 : KN ? 4 : 2;        // weight-scale loads per step
+    constexpr int kSW = FP4 && !KN ? 2 : 1;          // dwords per scale load
     // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4 (FP8) or 8 (FP4)
     constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
+    StepRegs<kAL, RF, kSB, kSW> regs[D];
 
     auto issue = [&](int ks, int slot) {
-        const int k0 = ks * kStepB;
+        const int k0 = ks * kStepA;
         __builtin_amdgcn_sched_barrier(0);
-        StepRegs<KN, RF, FP4> &r = regs[slot];
+        StepRegs<kAL, RF, kSB, kSW> &r = regs[slot];
 #pragma unroll
         for (int f = 0; f < RF; ++f)
 #pragma unroll
@@ -558,7 +619,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // (2 ks) & ~3; [N,K] the step's kBlk bytes at kBlk ks
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-            if constexpr (FP4) {
+            if constexpr (kSW == 2) {
                 const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[f], kBlk * ks, 0);
                 r.sa[f][0] = v.x;
                 r.sa[f][1] = v.y;
@@ -569,7 +630,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
 #pragma unroll
         for (int j = 0; j < kSB; ++j) {
-            if constexpr (FP4) {
+            if constexpr (kSW == 2) {
                 const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[j], kBlk * ks, 0);
                 r.sb[j][0] = v.x;
                 r.sb[j][1] = v.y;
@@ -585,7 +646,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             const int u = u0 + uu;
             lds_void_t *dst = (lds_void_t *)(ring + slot * kSlotBytes + u * 1024);
             if (KN)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[0], (k0 + 8 * u) * N, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[KN4 ? (u & 1) : 0],
+                                                         (ks * kStepK + 8 * u) * Nb, 0, 0);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[uu], k0, 0, 0);
         }
@@ -607,7 +669,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
     auto read_b = [&](int slot, BTile &b) {
         const uint32_t base = lds_addr(ring + slot * kSlotBytes);
-        if constexpr (KN) {
+        if constexpr (KN4) {
+            uint32_t a[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = base + tr_addr[j];
+            lds_issue_kn4(a, b);
+        } else if constexpr (KN) {
             const uint32_t a[4] = {base + tr_addr[0], base + tr_addr[1], base + tr_addr[2],
                                    base + tr_addr[3]};
             lds_issue_kn(a, b);
@@ -619,13 +686,24 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     };
 
     auto mma = [&](int slot, const BTile &b, bool live, int ks) {
-        StepRegs<KN, RF, FP4> &r = regs[slot];
+        StepRegs<kAL, RF, kSB, kSW> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
             const bool on = arow_ok[f] && live;
-            if constexpr (KN) {
+            if constexpr (KN4) {
+                // one 64-K step, eight 32-column groups; 16-byte operands
+                const v4i z = {0, 0, 0, 0};
+                const v8i a = on ? cat(r.a[f][0], z) : v8i{};
+                const uint32_t sa = r.sa[f][0] >> (8 * (2 * (ks & 1) + g));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const v8i bj = {b[2 * j].x, b[2 * j].y, b[2 * j + 1].x, b[2 * j + 1].y,
+                                    0, 0, 0, 0};
+                    acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
+                }
+            } else if constexpr (KN) {
                 const v8i a = on ? cat(r.a[f][0], r.a[f][1]) : v8i{};
                 // byte (2 ks + g) & 3 of the x1 scale dword
                 const uint32_t sa = r.sa[f][0] >> (8 * (2 * (ks & 1) + g));
@@ -712,14 +790,14 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
     // Drain the trailing re-reads before the ring is reused.
     wait_vmcnt<0>();
-    if constexpr (FP4) {
+    if constexpr (FP4 && !KN) {
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
             acc[f][0] += acc[f][2];
             acc[f][1] += acc[f][3];
         }
     }
-    epilogue<KN ? 4 : 2, RF>(p, acc, m0, n0, store_rows, rinfo);
+    epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
@@ -768,16 +846,17 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
     __shared__ int64_t s_scan[kBlockThreads];
     __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock * kRingBytes];
 
-    constexpr int kTN = TRANS ? kTileNNK : kTileN;   // columns per item
+    // columns per item: [N, K] 64, [K, N] 128 (FP8) or 256 (FP4)
+    constexpr int kTN = TRANS ? kTileNNK : (FMT == 4 ? 2 * kTileN : kTileN);
     const int n_tiles = (p.N + kTN - 1) / kTN;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
     build_work_list<FMT>(p, n_tiles, wl, s_scan);
     if (p.det_total && blockIdx.x == 0 && threadIdx.x == 0) *p.det_total = wl.routed_tokens;
 
     const bool store_rows = p.wbuf != nullptr;
-    // K elements per step: 64 ([K,N] FP8), 128 ([N,K] FP8), 256 ([N,K] FP4):
-    // one step always moves 8 KB of the weight tile
-    const int k_steps = p.K / (FMT == 4 ? 2 * kStepKNK : TRANS ? kStepKNK : kStepK);
+    // K elements per step: 64 ([K,N]), 128 ([N,K] FP8), 256 ([N,K] FP4): one
+    // step always moves 8 KB of the weight tile
+    const int k_steps = p.K / (!TRANS ? kStepK : FMT == 4 ? 2 * kStepKNK : kStepKNK);
     const int blocks = gridDim.x;
     int S = p.split_k;
     const int base_units = wl.litems + (wl.sitems + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -1051,8 +1130,8 @@ DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
 
 hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
                         hipStream_t stream) {
-    if (fp8_kind == GFR_FP4_E2M1)   // the host admits the [N, K] layout only
-        return launch_fused_t<4, true>(p, stream);
+    if (fp8_kind == GFR_FP4_E2M1)
+        return transpose_x2 ? launch_fused_t<4, true>(p, stream) : launch_fused_t<4, false>(p, stream);
     if (fp8_kind == GFR_FP8_E4M3FN)
         return transpose_x2 ? launch_fused_t<0, true>(p, stream) : launch_fused_t<0, false>(p, stream);
     return transpose_x2 ? launch_fused_t<1, true>(p, stream) : launch_fused_t<1, false>(p, stream);

@@ -159,18 +159,27 @@ C3_PE = _reg(replace(C3, name="c3_pe", scale_per_expert=True, seed=1033))
 C5_PE = _reg(replace(C5, name="c5_pe", scale_per_expert=True, seed=1035))
 
 # MXFP4 ([P3] Atlas 350 MX notes): E2M1 x1 and transposed x2, two elements per
-# byte; K a multiple of 256.
+# byte along K; K a multiple of 256 ...
 SMALL_T_FP4 = _reg(replace(SMALL_T, name="small_t_fp4", fp8="e2m1", K=768, seed=1041))
 SMALL_BIG_T_FP4 = _reg(replace(SMALL_BIG_T, name="small_big_t_fp4", fp8="e2m1", K=768,
                                seed=1042))
 C2_FP4 = _reg(replace(C2, name="c2_fp4", fp8="e2m1", seed=1043))
 C3_FP4T = _reg(replace(C3, name="c3_fp4t", fp8="e2m1", transpose_x2=True, seed=1044))
 C5_FP4 = _reg(replace(C5, name="c5_fp4", fp8="e2m1", seed=1045))
+# ... and with [K, N] x2 packed along N (N a multiple of 32); K = 640 is not a
+# multiple of 256.
+SMALL_N_FP4 = _reg(replace(SMALL_N, name="small_n_fp4", fp8="e2m1", seed=1046))
+SMALL_BIG_N_FP4 = _reg(replace(SMALL_BIG_N, name="small_big_n_fp4", fp8="e2m1", K=640,
+                               seed=1047))
+C1_FP4 = _reg(replace(C1, name="c1_fp4", fp8="e2m1", seed=1048))
+C3_FP4 = _reg(replace(C3, name="c3_fp4", fp8="e2m1", seed=1049))
+C4_FP4 = _reg(replace(C4, name="c4_fp4", fp8="e2m1", seed=1050))
 
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_N_PE,
-              SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T):
+              SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
+              SMALL_BIG_N_FP4, C3_FP4):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))
 

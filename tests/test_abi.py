@@ -69,7 +69,8 @@ def _call(**over):
     (dict(x1=0x10004), 5), (dict(x2=0x10008), 5), (dict(scale=0x10001), 5),
     (dict(shared=0x10002), 5),
     (dict(kind=3), 7), (dict(gtype=2), 7), (dict(trans=3), 7),
-    (dict(kind=2), 4), (dict(kind=2, trans=1, K=8064), 4),   # MXFP4: [N,K] x2, K % 256
+    # MXFP4: [K,N] x2 needs N % 32 (16-byte rows), [N,K] x2 K % 256
+    (dict(kind=2, N=4112), 4), (dict(kind=2, trans=1, K=8064), 4),
 ])
 def test_host_validation(over, code):
     assert _call(**over) == code

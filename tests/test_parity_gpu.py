@@ -90,7 +90,8 @@ def slack_for(inp, rows=None):
                                   "small_big_t_exact", "small_n_pe", "small_big_t_pe",
                                   "small_n_pe_exact", "small_big_t_pe_exact", "small_t_fp4",
                                   "small_big_t_fp4", "small_t_fp4_exact",
-                                  "small_big_t_fp4_exact"])
+                                  "small_big_t_fp4_exact", "small_n_fp4", "small_big_n_fp4",
+                                  "small_n_fp4_exact", "small_big_n_fp4_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]
@@ -107,7 +108,8 @@ def test_small_full(name, split_k):
 @pytest.mark.parametrize("name", ["c1_exact", "c2_exact", "c3_exact", "c4_exact", "c5_exact",
                                   "c1", "c2", "c3", "c4", "c5",
                                   "p1_tc_a", "p1_tc_b", "p2_ragged", "c3_pe", "c5_pe",
-                                  "c2_fp4", "c3_fp4t", "c3_fp4t_exact", "c5_fp4"])
+                                  "c2_fp4", "c3_fp4t", "c3_fp4t_exact", "c5_fp4",
+                                  "c1_fp4", "c3_fp4", "c3_fp4_exact", "c4_fp4"])
 def test_full_shapes_sampled(name):
     w = WORKLOADS[name]
     print(f"case {name}", flush=True)
@@ -119,7 +121,7 @@ def test_full_shapes_sampled(name):
 
 
 @pytest.mark.parametrize("name", ["c5", "c5_exact", "small_n", "small_t", "small_big_n",
-                                  "small_big_t_exact", "small_t_fp4"])
+                                  "small_big_t_exact", "small_t_fp4", "small_big_n_fp4"])
 def test_deterministic_mode(name):
     """Deterministic mode: bitwise repeatable, within tolerance of the oracle
     (bit-exact on integer data)."""

@@ -28,7 +28,8 @@ def test_zipf_routing_has_empty_and_heavy_experts(name):
 
 @pytest.mark.parametrize("name", ["small_n", "small_t", "small_n_exact", "small_big_n",
                                   "small_big_t_exact", "small_n_pe", "small_big_t_pe",
-                                  "small_t_fp4", "small_big_t_fp4_exact"])
+                                  "small_t_fp4", "small_big_t_fp4_exact",
+                                  "small_big_n_fp4_exact"])
 def test_make_inputs_shapes_and_determinism(name):
     w = WORKLOADS[name]
     a = make_inputs(w)

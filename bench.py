@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MXFP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
 
 
 def parse():
@@ -181,8 +182,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 (fp8 x fp8 x e8m0 -> f32)",
-        "data": "synthetic (seeded; FP8 from N(0,1), E8M0 exponents uniform)",
+        "dtype": ("mxfp4 (e2m1 x e2m1 x e8m0 -> f32)" if w.fp8 == "e2m1"
+                  else "mxfp8 (fp8 x fp8 x e8m0 -> f32)"),
+        "data": (f"synthetic (seeded; {'E2M1' if w.fp8 == 'e2m1' else 'FP8'} from N(0,1), "
+                 "E8M0 exponents uniform)"),
         "config": {
             "workload": f"{w.name}: M={w.M} K={w.K} N={w.N} E={w.E} batch={w.batch} "
                         f"fp8={w.fp8} transpose_x2={w.transpose_x2} "
@@ -201,7 +204,8 @@ def main():
             "kernel": "fused_kernel (gfr grouped MXFP8 GEMM + finalize routing)",
             "algorithmic_bytes_per_launch": alg_bytes,
             "mean_launch_ms": round(mean_launch_ms, 5),
-            "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
+            "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 /
+                               (MXFP4_PEAK_TFLOPS if w.fp8 == "e2m1" else MXFP8_PEAK_TFLOPS), 4),
         },
         "cpu_baseline": None,
     }

@@ -7,7 +7,9 @@ with the GPU library (``mxfp8_grouped_gemm_group_amd``) and never imports it.
 The arithmetic lives in ``gfr_oracle.c`` (plain C, double precision, built with
 gcc into ``liboracle.so``); this module only marshals numpy arrays to it.  See
 the header of ``gfr_oracle.c`` for the operator's definition and the pages each
-step follows.
+step follows.  ``oracle.gemm1`` adds the upstream step of the MoE FFN (gate||up
+matmul through the same C definition, SwiGLU and MX block quantisation in
+float64 numpy).
 """
 from __future__ import annotations
 

@@ -164,6 +164,57 @@ int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale
 int gfr_workspace_size(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
                        const gfr_options *opts, size_t *bytes);
 
+/*
+ * gfr_gemm1_swiglu_quant — the upstream step of the MoE FFN whose output is
+ * this library's x1 / pertoken_scale: the gate||up grouped matmul and SwiGLU
+ * of "LLaDA2.0-mini MoE 融合算子实战：基于 PyPTO 的 Grouped GEMM 单内核实现"
+ * ([P2] §3.1 w13 layout, §3.2 two-stage expert FFN, §3.3 SwiGLU), with MXFP8
+ * operands as in [P1], followed by MX block quantisation.  For every expert e
+ * and token t in its group_list range:
+ *
+ *   gate_up[t, j] = sum_k dq(xin[t, k]) * dq(w13[e, k, j]),  j < 2I  (FP32)
+ *   sw[t, i]      = SiLU(gate_up[t, i]) * gate_up[t, I + i],
+ *                   SiLU(g) = g / (1 + exp(-g))   (FP32; first I columns gate)
+ *
+ * and each 32-element block i in [32b, 32b + 32) of row t is encoded as
+ *   X = floor(log2(max |sw|)) - emax   (emax 8 for E4M3FN, 15 for E5M2;
+ *       -127 for an all-zero block; clamped to >= -127),
+ *   x1_out[t, i] = FP8 code nearest to sw[t, i] / 2^X (ties to even,
+ *       saturating at the largest finite value),
+ *   x1_scale_out[t, b / 2, b % 2] = X + 127 (E8M0).
+ * The pages define only the dequantisation of MX data; this encoding is the
+ * OCP Microscaling rule, and dequantising the output reproduces sw within
+ * half a code step (values that scale past the largest finite code saturate).
+ *
+ *  xin             [M, H] FP8 (fp8_kind), tokens sorted by expert.
+ *  w13             [E, H, 2I] FP8, or [E, 2I, H] when transpose_w13 != 0.
+ *  scale           E8M0 bytes, [ceil(H/64), 2I, 2], or [2I, ceil(H/64), 2]
+ *                  when transpose_w13; a leading [E] axis with
+ *                  gfr_options.scale_per_expert.
+ *  xin_scale       E8M0 bytes, [M, ceil(H/64), 2].
+ *  group_list      int64 [E], format per group_list_type.
+ *  x1_out          [M, I] FP8 codes of out_kind (written; rows of tokens in no
+ *                  expert's range are left untouched).
+ *  x1_scale_out    [M, I/64, 2] E8M0 bytes (written, same rows).
+ *  transpose_w13   0 or 1.
+ *  fp8_kind        GFR_FP8_E4M3FN or GFR_FP8_E5M2 (xin and w13).
+ *  out_kind        GFR_FP8_E4M3FN or GFR_FP8_E5M2 (x1_out).
+ *  M, H, I, E      sizes; M = 0 or I = 0 is a no-op.
+ *  stream          hipStream_t.
+ *  opts            may be NULL; only scale_per_expert and status_dev are used
+ *                  (the output is written once per element: no atomics, no
+ *                  K split, bitwise repeatable).
+ *
+ * Limits (GFR_ERR_UNSUPPORTED): H % 128 != 0, I % 64 != 0, E outside
+ * [1, 1024], 2I * H >= 2^31, GFR_FP4_E2M1 input.  xin, w13 and scale must be
+ * 16-byte aligned.  Returns a gfr_status.
+ */
+int gfr_gemm1_swiglu_quant(const void *xin, const void *w13, const uint8_t *scale,
+                           const uint8_t *xin_scale, const int64_t *group_list,
+                           int group_list_type, void *x1_out, uint8_t *x1_scale_out,
+                           int transpose_w13, int fp8_kind, int out_kind, int64_t M, int64_t H,
+                           int64_t I, int64_t E, void *stream, const gfr_options *opts);
+
 /* Static, NUL-terminated description of a gfr_status. */
 const char *gfr_status_string(int status);
 

@@ -5,8 +5,8 @@ include/gfr.h); this package is its thin Python binding plus the seeded input
 generators (``workloads``).  The library is loaded on first use and its absence
 is an error: there is no fallback implementation.
 """
-from ._binding import (DEV_BAD_GROUP_LIST, DEV_BAD_ROW_INDEX, GfrError, gmm_finalize_routing,
-                       load_library, status_string, workspace_size)
+from ._binding import (DEV_BAD_GROUP_LIST, DEV_BAD_ROW_INDEX, GfrError, gemm1_swiglu_quant,
+                       gmm_finalize_routing, load_library, status_string, workspace_size)
 
-__all__ = ["gmm_finalize_routing", "workspace_size", "status_string", "load_library",
-           "GfrError", "DEV_BAD_GROUP_LIST", "DEV_BAD_ROW_INDEX"]
+__all__ = ["gmm_finalize_routing", "gemm1_swiglu_quant", "workspace_size", "status_string",
+           "load_library", "GfrError", "DEV_BAD_GROUP_LIST", "DEV_BAD_ROW_INDEX"]

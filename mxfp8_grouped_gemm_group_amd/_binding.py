@@ -57,6 +57,10 @@ def load_library() -> ctypes.CDLL:
         lib.gfr_workspace_size.argtypes = [ctypes.c_int64] * 5 + [
             ctypes.POINTER(GfrOptions), ctypes.POINTER(ctypes.c_size_t)]
         lib.gfr_workspace_size.restype = ctypes.c_int
+        lib.gfr_gemm1_swiglu_quant.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [
+            ctypes.c_void_p] * 2 + [ctypes.c_int] * 3 + [ctypes.c_int64] * 4 + [
+            ctypes.c_void_p, ctypes.POINTER(GfrOptions)]
+        lib.gfr_gemm1_swiglu_quant.restype = ctypes.c_int
         lib.gfr_status_string.argtypes = [ctypes.c_int]
         lib.gfr_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -157,3 +161,64 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
     if rc:
         raise GfrError(rc, status_string(rc))
     return out
+
+
+def gemm1_swiglu_quant(xin, w13, scale, xin_scale, group_list, group_list_type,
+                       transpose_w13=False, out_dtype=torch.float8_e4m3fn, *, x1_out=None,
+                       x1_scale_out=None, status=None, stream=None):
+    """Upstream step of the MoE FFN: gate||up grouped matmul, SwiGLU, MX
+    quantisation (include/gfr.h, gfr_gemm1_swiglu_quant).
+
+    xin float8 [M, H]; w13 [E, H, 2I] (or [E, 2I, H] with transpose_w13) of
+    xin's dtype; scale E8M0 [ceil(H/64), 2I, 2] (or [2I, ceil(H/64), 2]; 4-D
+    with a leading expert axis for per-expert scales); xin_scale E8M0
+    [M, ceil(H/64), 2]; group_list int64 [E].  Returns (x1, x1_scale): out_dtype
+    [M, I] and uint8 [M, I/64, 2], ready to be gmm_finalize_routing's x1 and
+    pertoken_scale.  Rows of tokens in no expert's range are left as they were
+    in x1_out / x1_scale_out (zeros when the call allocates them)."""
+    lib = load_library()
+    _need(xin.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) and w13.dtype == xin.dtype,
+          "xin/w13 must share an FP8 dtype")
+    _need(out_dtype in (torch.float8_e4m3fn, torch.float8_e5m2), "out_dtype must be FP8")
+    _need(xin.dim() == 2 and w13.dim() == 3, "xin must be 2-D and w13 3-D")
+    M, H = xin.shape
+    E = w13.shape[0]
+    if transpose_w13:
+        _need(w13.shape[2] == H, "w13 [E,2I,H] does not match H")
+        N2 = w13.shape[1]
+    else:
+        _need(w13.shape[1] == H, "w13 [E,H,2I] does not match H")
+        N2 = w13.shape[2]
+    _need(N2 % 2 == 0, "w13 must have an even number (2I) of columns")
+    I = N2 // 2
+    KB = (H + 63) // 64
+    s3 = (N2, KB, 2) if transpose_w13 else (KB, N2, 2)
+    _need(scale.dtype in _E8M0 and xin_scale.dtype in _E8M0, "scales must be E8M0 bytes")
+    per_expert = scale.dim() == 4
+    _need(tuple(scale.shape) == ((E,) + s3 if per_expert else s3), "bad scale shape")
+    _need(tuple(xin_scale.shape) == (M, KB, 2), "bad xin_scale shape")
+    _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
+    dev = xin.device
+    if x1_out is None:
+        x1_out = torch.zeros((M, I), dtype=torch.uint8, device=dev).view(out_dtype)
+    if x1_scale_out is None:
+        x1_scale_out = torch.zeros((M, (I + 63) // 64, 2), dtype=torch.uint8, device=dev)
+    _need(x1_out.dtype == out_dtype and tuple(x1_out.shape) == (M, I), "bad x1_out")
+    _need(x1_scale_out.dtype in _E8M0 and tuple(x1_scale_out.shape) == (M, (I + 63) // 64, 2),
+          "bad x1_scale_out")
+    for t in (xin, w13, scale, xin_scale, group_list, x1_out, x1_scale_out, status):
+        if t is not None:
+            _need(t.is_cuda and t.device == dev, "all tensors must be on xin's CUDA device")
+            _need(t.is_contiguous(), "all tensors must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    opts = GfrOptions(0, None, 0, _ptr(status), 0, int(per_expert))
+    with torch.cuda.device(dev):
+        rc = lib.gfr_gemm1_swiglu_quant(
+            _ptr(xin), _ptr(w13), _ptr(scale), _ptr(xin_scale), _ptr(group_list),
+            int(group_list_type), _ptr(x1_out), _ptr(x1_scale_out), int(bool(transpose_w13)),
+            _FP8_KIND[xin.dtype], _FP8_KIND[out_dtype], M, H, I, E, ctypes.c_void_p(stream),
+            ctypes.byref(opts))
+    if rc:
+        raise GfrError(rc, status_string(rc))
+    return x1_out, x1_scale_out

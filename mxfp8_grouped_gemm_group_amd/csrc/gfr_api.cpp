@@ -168,4 +168,54 @@ int gmm_finalize_routing(const void *x1, const void *x2, const uint8_t *scale,
                                    E, batch, shared_rows, stream, nullptr);
 }
 
+int gfr_gemm1_swiglu_quant(const void *xin, const void *w13, const uint8_t *scale,
+                           const uint8_t *xin_scale, const int64_t *group_list,
+                           int group_list_type, void *x1_out, uint8_t *x1_scale_out,
+                           int transpose_w13, int fp8_kind, int out_kind, int64_t M, int64_t H,
+                           int64_t I, int64_t E, void *stream, const gfr_options *opts) {
+    if (M < 0 || H <= 0 || I < 0 || E <= 0) return GFR_ERR_BAD_SHAPE;
+    if (fp8_kind != GFR_FP8_E4M3FN && fp8_kind != GFR_FP8_E5M2 && fp8_kind != GFR_FP4_E2M1)
+        return GFR_ERR_BAD_ARG;
+    if (out_kind != GFR_FP8_E4M3FN && out_kind != GFR_FP8_E5M2) return GFR_ERR_BAD_ARG;
+    if (group_list_type != GFR_GROUP_LIST_CUMSUM && group_list_type != GFR_GROUP_LIST_COUNT)
+        return GFR_ERR_BAD_ARG;
+    if (transpose_w13 != 0 && transpose_w13 != 1) return GFR_ERR_BAD_ARG;
+    const int per_expert = opts ? opts->scale_per_expert : 0;
+    if (per_expert != 0 && per_expert != 1) return GFR_ERR_BAD_ARG;
+    if (fp8_kind == GFR_FP4_E2M1) return GFR_ERR_UNSUPPORTED;
+    // the x2 limits of the main operator with N = 2I, and whole 64-column
+    // output blocks (one item covers 64 or 32 outputs, two MX blocks or one)
+    int rc = check_sizes(M, H, 2 * I, E, M);
+    if (rc != GFR_OK) return rc;
+    if (I % 64 != 0) return GFR_ERR_UNSUPPORTED;
+    if (M == 0 || I == 0) return GFR_OK;   // nothing to produce
+    if (!xin || !w13 || !scale || !xin_scale || !group_list || !x1_out || !x1_scale_out)
+        return GFR_ERR_NULL_ARG;
+    if (!aligned(xin, 16) || !aligned(w13, 16) || !aligned(scale, 16)) return GFR_ERR_BAD_ALIGNMENT;
+
+    gfr::FusedParams p{};
+    p.x1 = static_cast<const uint8_t *>(xin);
+    p.x2 = static_cast<const uint8_t *>(w13);
+    p.scale = scale;
+    p.pts = xin_scale;
+    p.group_list = group_list;
+    p.status = opts ? opts->status_dev : nullptr;
+    p.M = static_cast<int32_t>(M);
+    p.K = static_cast<int32_t>(H);
+    p.N = static_cast<int32_t>(2 * I);
+    p.E = static_cast<int32_t>(E);
+    p.batch = static_cast<int32_t>(M);
+    p.group_list_type = group_list_type;
+    p.split_k = 1;
+    p.scale_e_stride = per_expert ? (H / 32) * (2 * I) : 0;
+    p.q_out = static_cast<uint8_t *>(x1_out);
+    p.qs_out = x1_scale_out;
+    p.I = static_cast<int32_t>(I);
+    p.out_kind = out_kind;
+    if (gfr::launch_gemm1(p, transpose_w13, fp8_kind, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return GFR_ERR_HIP;
+    return GFR_OK;
+}
+
 }  // extern "C"

@@ -43,6 +43,12 @@ struct FusedParams {
     int32_t group_list_type;
     int32_t split_k;           // 0: chosen on the device
     int64_t scale_e_stride;    // bytes between experts' weight scales (0: shared)
+    // Upstream step (gate||up matmul + SwiGLU + MX quantisation); x2 then
+    // holds 2I columns (N = 2I) and the output goes to q_out / qs_out.
+    uint8_t *q_out;            // [M, I] FP8 codes
+    uint8_t *qs_out;           // [M, I/64, 2] E8M0 block scales
+    int32_t I;
+    int32_t out_kind;          // 0 E4M3FN, 1 E5M2
 };
 
 // Deterministic-mode workspace layout (all offsets 256-byte aligned):
@@ -60,6 +66,8 @@ DetLayout det_layout(int64_t M, int64_t N, int64_t batch);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
+                        hipStream_t stream);
+hipError_t launch_gemm1(const FusedParams &p, int transpose_w13, int fp8_kind,
                         hipStream_t stream);
 hipError_t launch_deterministic_prep(const FusedParams &p, void *workspace,
                                      hipStream_t stream);

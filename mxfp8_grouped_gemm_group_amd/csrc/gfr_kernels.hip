@@ -433,6 +433,74 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs
     }
 }
 
+// FP32 -> FP8 code nearest to y, ties to even, saturating at the largest
+// finite value (E4M3FN: bias 7, 3 mantissa bits, 0x7E = 448; E5M2: bias 15,
+// 2 bits, 0x7B = 57344).  With e = max(floor(log2|y|), 1 - bias) the
+// representable magnitudes near |y| are multiples of 2^(e - mbits);
+// r = rint(|y| * 2^(mbits - e)) (exact scaling) and the code is
+// ((e + bias) << mbits) + r - 2^mbits, which carries r = 2^(mbits + 1) into
+// the next exponent and gives the subnormal codes for e = 1 - bias.
+template <int BIAS, int MBITS, int MAXCODE>
+__device__ __forceinline__ uint32_t fp8_encode(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80;
+    const float a = fabsf(y);
+    const int be = static_cast<int>(__float_as_uint(a) >> 23);   // a >= 0: no sign bit
+    const int e = max(be - 127, 1 - BIAS);                        // be = 0: zero or subnormal
+    const float sc = __uint_as_float(static_cast<uint32_t>(127 + MBITS - e) << 23);
+    const int r = static_cast<int>(rintf(a * sc));
+    const int code = min(((e + BIAS) << MBITS) + r - (1 << MBITS), MAXCODE);
+    return static_cast<uint32_t>(code) | sign;
+}
+
+// Epilogue of the upstream step: accumulator groups j < NJ/2 hold gate
+// columns n0 + 32j + c and groups j >= NJ/2 the matching up columns, so
+// sw = SiLU(gate) * up = gate / (1 + exp(-gate)) * up in FP32.  Each 32-column
+// group of a row is one MX block: its largest magnitude (a max over the 32
+// lanes of the half-wave that hold the row) gives the block exponent
+// X = floor(log2(amax)) - emax (emax 8 for E4M3FN, 15 for E5M2; -127 for an
+// all-zero block, never below -127), and each element is encoded as
+// fp8(sw * 2^-X).  Codes go to q_out[t, :] (32 adjacent bytes per row and
+// group), the scale byte X + 127 to qs_out[t, col / 32].
+template <int NJ, int RF, int NA>
+__device__ __forceinline__ void epilogue_swiglu(const FusedParams &p, const v16f (&accs)[RF][NA],
+                                                int m0, int mcount, int n0) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+    const int I = p.I;
+    const bool e5 = p.out_kind == GFR_FP8_E5M2;
+    const int emax = e5 ? 15 : 8;
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj) {
+            float sw[16], am[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float gt = accs[f][jj][r], ut = accs[f][jj + NJ / 2][r];
+                sw[r] = gt / (1.0f + expf(-gt)) * ut;
+                am[r] = fabsf(sw[r]);
+            }
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) am[r] = fmaxf(am[r], __shfl_xor(am[r], off));
+            const int col = n0 + 32 * jj + c;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * f + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (row >= mcount) continue;
+                const int be = static_cast<int>(__float_as_uint(am[r]) >> 23);
+                const int X = be == 0 ? -127 : max(be - 127 - emax, -127);
+                const float y = sw[r] * __uint_as_float(static_cast<uint32_t>(127 - X) << 23);
+                const uint32_t q = e5 ? fp8_encode<15, 2, 0x7B>(y) : fp8_encode<7, 3, 0x7E>(y);
+                const int64_t t = m0 + row;
+                p.q_out[t * I + col] = static_cast<uint8_t>(q);
+                if (c == 0) p.qs_out[t * (I / 32) + (n0 / 32 + jj)] = static_cast<uint8_t>(X + 127);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Routed item mainloop.  Per K step
 //   * the 64 x 128 weight tile is moved global -> LDS with 8 direct-to-LDS
@@ -465,7 +533,7 @@ static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
                   kCoopStagesKN4 * kSlotBytes <= kWavesPerBlock * kRingBytes,
               "cooperative ring fits the block's LDS");
 
-template <int FMT, bool KN, bool COOP, int RF>
+template <int FMT, bool KN, bool COOP, int RF, int OP>
 __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                             int ks0, int ks1, bool store_rows, char *ring, int w) {
     static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
@@ -478,6 +546,13 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // of 128 bytes), eight MFMAs per step.
     constexpr bool FP4 = FMT == 4;
     constexpr bool KN4 = FP4 && KN;
+    // OP 0: finalize routing (weight columns n0 + tile column).  OP 1: the
+    // upstream step -- the tile's first half of columns comes from the gate
+    // block [n0, n0 + half) and its second half from the up block
+    // [I + n0, I + n0 + half) of the 2I weight columns.
+    static_assert(OP == 0 || !FP4, "the upstream step is MXFP8 only");
+    constexpr int kHalf = (KN ? kTileN : kTileNNK) / 2;
+    const int up0 = OP == 1 ? __builtin_amdgcn_readfirstlane(p.I) : 0;
     constexpr int D = !COOP ? kStages
                       : RF == 2 ? 4
                       : KN4 ? kCoopStagesKN4
@@ -501,6 +576,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // (a cooperative wave past the expert's last row has mcount <= 0: its
     // loads have an empty range and return zeros, its epilogue writes nothing)
     if (mcount < 0) mcount = 0;
+    auto wcol = [&](int tc) { return OP == 0 || tc < kHalf ? n0 + tc : up0 + n0 + tc - kHalf; };
     bool arow_ok[RF];
     int va[RF], vsa[RF];
 #pragma unroll
@@ -552,7 +628,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // load u, lane l: K row r = 8u + l/8 (row offset in soffset); it fills
         // physical chunk l%8 of the slot row, which holds logical chunk
         // (l%8) ^ ((r >> 1) & 3) = (l%8) ^ ((l >> 4) & 3)
-        const int chunk_col = n0 + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+        const int chunk_col = wcol(16 * ((lane & 7) ^ ((lane >> 4) & 3)));
         vb[0] = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
         // transpose reads: lane s of 16-lane group G reads K row
         // 16g + (s >> 1) + (read's K offset), columns 32j + 16(G & 1) + 8(s & 1)
@@ -564,7 +640,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // the aligned dword holds columns col & ~1 and col | 1
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int col = n0 + 32 * j + c;
+            const int col = wcol(32 * j + c);
             vsb[j] = ((col < N ? col : n0) & ~1) * 2;
         }
         sb_shift = 8 * (2 * (c & 1) + g);
@@ -576,20 +652,21 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         for (int uu = 0; uu < kTileLoads; ++uu) {
             const int u = u0 + uu;
             const int tcol = 8 * u + (lane >> 3);
-            const int col = n0 + tcol;
+            const int col = wcol(tcol);
             vb[uu] = (col < N ? col : n0) * Kb + 16 * ((lane & 7) ^ ((tcol >> 1) & 7));
         }
         // scale bytes (col, 32-block 4ks + b) of [N, K/64, 2]: the aligned
         // dword at col * KS + 4 ks holds the step's four
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int cj = n0 + 32 * j + c;
+            const int cj = wcol(32 * j + c);
             vsb[j] = (cj < N ? cj : n0) * KS;
         }
         vsb[2] = vsb[3] = 0;
     }
 
-    const RowInfo rinfo = load_row_info<RF>(p, m0, mcount);
+    // (the upstream step has no row_index / logit)
+    const RowInfo rinfo = OP == 0 ? load_row_info<RF>(p, m0, mcount) : RowInfo{};
     constexpr int NA = KN4 ? 8 : 4;   // accumulators per row fragment
     v16f acc[RF][NA];
 #pragma unroll
@@ -797,7 +874,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             acc[f][1] += acc[f][3];
         }
     }
-    epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
+    if constexpr (OP == 1)
+        epilogue_swiglu<KN ? 4 : 2, RF, NA>(p, acc, m0, mcount, n0);
+    else
+        epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
@@ -837,8 +917,13 @@ __device__ __forceinline__ void shared_slice(const FusedParams &p, int64_t wave,
 // wave items of the small experts (expert, 32-row tile, 128-column tile, K
 // split), four consecutive ones per unit, one per wave.  Blocks take units
 // round-robin.
-template <int FMT, bool TRANS>
-__global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) {
+//
+// OP 0 is the finalize-routing operator; OP 1 the upstream step, whose items
+// cover a 64- ([K,N]) or 32-column ([N,K]) block of the I outputs (twice that
+// many weight columns: gate and up) and always the whole K range (its
+// epilogue is not linear, so there is no K split).
+template <int FMT, bool TRANS, int OP>
+__device__ __forceinline__ void run_units(const FusedParams &p) {
     __shared__ int s_start[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_spref[kMaxExperts + 1];
@@ -848,19 +933,21 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
 
     // columns per item: [N, K] 64, [K, N] 128 (FP8) or 256 (FP4)
     constexpr int kTN = TRANS ? kTileNNK : (FMT == 4 ? 2 * kTileN : kTileN);
-    const int n_tiles = (p.N + kTN - 1) / kTN;
+    constexpr int kOutN = OP == 0 ? kTN : kTN / 2;   // output columns per item
+    const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
     build_work_list<FMT>(p, n_tiles, wl, s_scan);
-    if (p.det_total && blockIdx.x == 0 && threadIdx.x == 0) *p.det_total = wl.routed_tokens;
+    if (OP == 0 && p.det_total && blockIdx.x == 0 && threadIdx.x == 0)
+        *p.det_total = wl.routed_tokens;
 
-    const bool store_rows = p.wbuf != nullptr;
+    const bool store_rows = OP == 0 && p.wbuf != nullptr;
     // K elements per step: 64 ([K,N]), 128 ([N,K] FP8), 256 ([N,K] FP4): one
     // step always moves 8 KB of the weight tile
     const int k_steps = p.K / (!TRANS ? kStepK : FMT == 4 ? 2 * kStepKNK : kStepKNK);
     const int blocks = gridDim.x;
     int S = p.split_k;
     const int base_units = wl.litems + (wl.sitems + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (store_rows) {
+    if (OP == 1 || store_rows) {
         S = 1;
     } else if (S <= 0) {
         // Enough K splits to give every block a unit (long K runs stream
@@ -922,11 +1009,11 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             if (FMT != 4 && gr > kCoopRows)
-                routed_item<FMT, !TRANS, true, FMT == 4 ? 1 : 2>(p, e, m0, mcount, nt * kTN, ks0,
-                                                                 ks1, store_rows, s_ring, w);
+                routed_item<FMT, !TRANS, true, FMT == 4 ? 1 : 2, OP>(
+                    p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
             else
-                routed_item<FMT, !TRANS, true, 1>(p, e, m0, mcount, nt * kTN, ks0, ks1, store_rows,
-                                                  s_ring, w);
+                routed_item<FMT, !TRANS, true, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
+                                                      store_rows, s_ring, w);
         } else {
             const int64_t it = (u - coop_units) * kWavesPerBlock + w;
             if (it >= wave_items) continue;
@@ -946,13 +1033,26 @@ __global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) 
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
-            routed_item<FMT, !TRANS, false, 1>(p, e, m0, mcount, nt * kTN, ks0, ks1,
-                                               store_rows, own, w);
+            routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
+                                                   store_rows, own, w);
         }
     }
     // The shared-expert term last: at the start its loads would delay the
     // first weight loads by a memory latency.
-    if (p.shared && !store_rows) shared_slice(p, blockIdx.x * kWavesPerBlock + w, waves);
+    if (OP == 0 && p.shared && !store_rows)
+        shared_slice(p, blockIdx.x * kWavesPerBlock + w, waves);
+}
+
+template <int FMT, bool TRANS>
+__global__ __launch_bounds__(kBlockThreads, 1) void fused_kernel(FusedParams p) {
+    run_units<FMT, TRANS, 0>(p);
+}
+
+// The upstream step of the MoE FFN: x2 = w13 ([E, H, 2I] or [E, 2I, H]),
+// x1 = the expert-sorted input tokens, output MX-quantised SwiGLU rows.
+template <int FMT, bool TRANS>
+__global__ __launch_bounds__(kBlockThreads, 1) void gemm1_swiglu_kernel(FusedParams p) {
+    run_units<FMT, TRANS, 1>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1112,6 +1212,14 @@ hipError_t launch_fused_t(const FusedParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int FMT, bool TRANS>
+hipError_t launch_gemm1_t(const FusedParams &p, hipStream_t stream) {
+    const int grid = device_cu_count();
+    hipLaunchKernelGGL((gemm1_swiglu_kernel<FMT, TRANS>), dim3(grid), dim3(kBlockThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
@@ -1126,6 +1234,13 @@ DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
     d.total_tokens = d.sorted + up(static_cast<size_t>(M) * sizeof(int));
     d.total = d.total_tokens + 256;
     return d;
+}
+
+hipError_t launch_gemm1(const FusedParams &p, int transpose_w13, int fp8_kind,
+                        hipStream_t stream) {
+    if (fp8_kind == GFR_FP8_E4M3FN)
+        return transpose_w13 ? launch_gemm1_t<0, true>(p, stream) : launch_gemm1_t<0, false>(p, stream);
+    return transpose_w13 ? launch_gemm1_t<1, true>(p, stream) : launch_gemm1_t<1, false>(p, stream);
 }
 
 hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,

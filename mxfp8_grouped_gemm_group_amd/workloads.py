@@ -368,3 +368,109 @@ def sample_rows(w: Workload, n: int, seed: int = 0) -> np.ndarray:
                 rows.add(r)
     rows.update({0, w.batch - 1})
     return np.array(sorted(rows), np.int64)
+
+
+# --------------------------------------------------------------------------
+# The upstream step of the MoE FFN (gate||up grouped matmul, SwiGLU, MX
+# quantisation; gfr_gemm1_swiglu_quant).  Shapes: the LLaDA2.0-mini grouped
+# GEMM page's model dimensions (H 2048, I 512, E 256) and its operator test's
+# token counts [0, 1, 2, 4, 8, 16, 32, 0]; the upstream steps of c2 and c3
+# (H = their N, I = their K: the step that produces their x1); small ragged
+# cases that span several tiles and every item class.  Drawing as for the
+# finalize-routing inputs: FP8 data from N(0,1), E8M0 exponents uniform.
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Gemm1Workload:
+    name: str
+    M: int
+    H: int
+    I: int
+    E: int
+    fp8: str = "e4m3fn"                    # xin / w13
+    out_fp8: str = "e4m3fn"                # x1 codes
+    transpose_w13: bool = False
+    group_list_type: int = 1
+    groups: Union[str, Tuple] = "uniform"
+    exp_range: Tuple[int, int] = (-3, 3)
+    scale_per_expert: bool = False
+    zero_rows: int = 0                     # leading xin rows set to zero (all-zero MX blocks)
+    seed: int = 0
+
+    def counts(self) -> np.ndarray:
+        return _counts(self)
+
+    def flops(self) -> int:
+        """2 * routed tokens * H * 2I."""
+        return 2 * int(self.counts().sum()) * self.H * 2 * self.I
+
+    def algorithmic_bytes(self) -> int:
+        """w13 of non-empty experts, xin, both scale tensors, group_list, and the
+        written x1 codes and scales of the routed rows."""
+        c = self.counts()
+        active = int((c > 0).sum())
+        M_r = int(c.sum())
+        H, N2 = self.H, 2 * self.I
+        kb32 = 2 * ((H + 63) // 64)
+        b = active * H * N2 + M_r * H + M_r * kb32
+        b += N2 * kb32 * (active if self.scale_per_expert else 1) + 8 * self.E
+        b += M_r * self.I + M_r * (self.I // 32)
+        return b
+
+
+GEMM1_WORKLOADS: Dict[str, Gemm1Workload] = {}
+
+
+def _reg1(w: Gemm1Workload) -> Gemm1Workload:
+    GEMM1_WORKLOADS[w.name] = w
+    return w
+
+
+_reg1(Gemm1Workload("g1_small", M=300, H=1024, I=384, E=7, groups=(0, 37, 1, 120, 0, 95, 47),
+                    exp_range=(-5, 5), zero_rows=2, seed=2001))
+_reg1(Gemm1Workload("g1_small_t", M=200, H=640, I=320, E=5, fp8="e5m2", transpose_w13=True,
+                    groups=(33, 0, 64, 100, 3), group_list_type=0, seed=2002))
+# large experts: 256-row cooperative groups (300, 141), a 128-row group (70),
+# a wave item (5)
+_reg1(Gemm1Workload("g1_big", M=516, H=768, I=192, E=5, out_fp8="e5m2",
+                    groups=(0, 300, 70, 5, 141), seed=2003))
+_reg1(Gemm1Workload("g1_big_t_pe", M=516, H=640, I=256, E=4, fp8="e5m2", out_fp8="e5m2",
+                    transpose_w13=True, groups=(141, 5, 300, 70), group_list_type=0,
+                    scale_per_expert=True, seed=2004))
+_reg1(Gemm1Workload("g1_llada_op", M=63, H=2048, I=512, E=8,
+                    groups=(0, 1, 2, 4, 8, 16, 32, 0), seed=2005))
+_reg1(Gemm1Workload("g1_llada", M=4096, H=2048, I=512, E=256, groups=("zipf", 1.2),
+                    seed=2006))
+_reg1(Gemm1Workload("g1_c2t", M=256, H=4096, I=6144, E=16, fp8="e5m2", transpose_w13=True,
+                    exp_range=(-4, 4), seed=2007))
+_reg1(Gemm1Workload("g1_c3", M=768, H=4096, I=8192, E=32, group_list_type=0, seed=2008))
+
+
+def make_gemm1_inputs(w: Gemm1Workload, device="cpu") -> dict:
+    """Draw one upstream-step invocation's inputs (keys: the binding's
+    argument names, plus out_dtype)."""
+    device = torch.device(device)
+    rng = np.random.default_rng(w.seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    dt = FP8_DTYPES[w.fp8]
+    M, H, N2, E = w.M, w.H, 2 * w.I, w.E
+    KB = (H + 63) // 64
+    xin = _fp8_from_normal((M, H), dt, gen, device, False)
+    if w.zero_rows:
+        xin[: w.zero_rows] = torch.zeros((w.zero_rows, H), dtype=torch.float32,
+                                         device=device).to(dt)
+    shape = (N2, H) if w.transpose_w13 else (H, N2)
+    w13 = torch.empty((E,) + shape, dtype=dt, device=device)
+    for e in range(E):
+        w13[e] = _fp8_from_normal(shape, dt, gen, device, False)
+    lo, hi = w.exp_range
+    xs = (127 + rng.integers(lo, hi + 1, size=(M, KB, 2))).astype(np.uint8)
+    sc_shape = (N2, KB, 2) if w.transpose_w13 else (KB, N2, 2)
+    if w.scale_per_expert:
+        sc_shape = (E,) + sc_shape
+    sc = (127 + rng.integers(lo, hi + 1, size=sc_shape)).astype(np.uint8)
+    gl = make_group_list(_counts(w), w.group_list_type)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return dict(xin=xin, w13=w13, scale=t(sc), xin_scale=t(xs), group_list=t(gl),
+                group_list_type=w.group_list_type, transpose_w13=bool(w.transpose_w13),
+                out_dtype=FP8_DTYPES[w.out_fp8])

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     lib = gfr.load_library()
     names = _declared_functions()
     assert {"gmm_finalize_routing", "gmm_finalize_routing_ex", "gfr_workspace_size",
-            "gfr_status_string"} <= names
+            "gfr_status_string", "gfr_gemm1_swiglu_quant"} <= names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -102,3 +102,35 @@ def test_empty_output_is_a_noop():
     # N = 0 or batch = 0: valid per the empty-tensor rules, returns before any launch
     assert _call(N=0) == 0
     assert _call(batch=0, R=0, shared=None) == 0
+
+
+def _call_gemm1(**over):
+    """gfr_gemm1_swiglu_quant with fake non-null pointers; only combinations
+    that fail host validation (or are no-ops) are used: nothing is launched."""
+    lib = gfr.load_library()
+    fake = 0x10000
+    a = dict(xin=fake, w13=fake, scale=fake, xs=fake, gl=fake, gtype=1, q=fake, qs=fake,
+             trans=0, kind=0, okind=0, M=768, H=4096, I=8192, E=32, stream=None, opts=None)
+    a.update(over)
+    return lib.gfr_gemm1_swiglu_quant(
+        a["xin"], a["w13"], a["scale"], a["xs"], a["gl"], a["gtype"], a["q"], a["qs"],
+        a["trans"], a["kind"], a["okind"], a["M"], a["H"], a["I"], a["E"], a["stream"], a["opts"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(xin=None), 1), (dict(w13=None), 1), (dict(scale=None), 1), (dict(xs=None), 1),
+    (dict(gl=None), 1), (dict(q=None), 1), (dict(qs=None), 1),
+    (dict(M=-1), 2), (dict(H=0), 2), (dict(I=-64), 2), (dict(E=0), 2),
+    (dict(H=4000), 4), (dict(I=8160), 4), (dict(E=1025), 4), (dict(kind=2), 4),
+    (dict(H=65536, I=32768), 4),                         # 2I * H >= 2^31
+    (dict(xin=0x10008), 5), (dict(w13=0x10004), 5), (dict(scale=0x10001), 5),
+    (dict(kind=3), 7), (dict(okind=2), 7), (dict(gtype=2), 7), (dict(trans=2), 7),
+    (dict(M=0, xin=None, gl=None), 0), (dict(I=0), 0),  # nothing to produce
+])
+def test_gemm1_host_validation(over, code):
+    assert _call_gemm1(**over) == code
+
+
+def test_gemm1_scale_per_expert_flag_is_validated():
+    opts = GfrOptions(0, None, 0, None, 0, 2)
+    assert _call_gemm1(opts=ctypes.byref(opts)) == 7

@@ -3,7 +3,8 @@ import numpy as np
 import pytest
 import torch
 
-from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_inputs, as_numpy, sample_rows
+from mxfp8_grouped_gemm_group_amd.workloads import (GEMM1_WORKLOADS, WORKLOADS, as_numpy,
+                                                    make_gemm1_inputs, make_inputs, sample_rows)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "p1_tc_a", "p1_tc_b",
@@ -63,3 +64,27 @@ def test_sample_rows_cover_shared_edges():
     r = sample_rows(w, 16)
     for e in (127, 128, 383, 384, 0, 511):
         assert e in r
+
+
+@pytest.mark.parametrize("name", ["g1_small", "g1_small_t", "g1_big", "g1_big_t_pe",
+                                  "g1_llada_op"])
+def test_gemm1_inputs_shapes_and_determinism(name):
+    w = GEMM1_WORKLOADS[name]
+    a, b = make_gemm1_inputs(w), make_gemm1_inputs(w)
+    KB = (w.H + 63) // 64
+    assert a["xin"].shape == (w.M, w.H)
+    assert a["w13"].shape == ((w.E, 2 * w.I, w.H) if w.transpose_w13 else (w.E, w.H, 2 * w.I))
+    s3 = (2 * w.I, KB, 2) if w.transpose_w13 else (KB, 2 * w.I, 2)
+    assert a["scale"].shape == (((w.E,) + s3) if w.scale_per_expert else s3)
+    assert a["xin_scale"].shape == (w.M, KB, 2)
+    for k in ("xin", "w13", "scale", "xin_scale", "group_list"):
+        assert torch.equal(a[k].view(torch.uint8) if a[k].dtype != torch.int64 else a[k],
+                           b[k].view(torch.uint8) if b[k].dtype != torch.int64 else b[k])
+    c = w.counts()
+    assert c.shape == (w.E,) and c.sum() <= w.M and w.I % 64 == 0 and w.H % 128 == 0
+    if w.zero_rows:
+        assert (a["xin"][: w.zero_rows].view(torch.uint8) == 0).all()
+
+
+def test_gemm1_llada_op_counts_follow_the_page():
+    assert list(GEMM1_WORKLOADS["g1_llada_op"].counts()) == [0, 1, 2, 4, 8, 16, 32, 0]

@@ -12,6 +12,11 @@ roofline   = the fused kernel against the HBM roofline (its algorithmic bytes
              stream), the binding roof for every configuration here
 cpu_baseline = the CPU oracle on a bounded sample of output rows of the same
              workload (single-threaded C, double precision)
+
+``--workload g1_*`` measures the upstream step of the FFN instead
+(gfr_gemm1_swiglu_quant: gate||up grouped matmul, SwiGLU, MX quantisation;
+default g1_c3, the step that produces c3's x1): value = 2*M*H*2I / t, the
+same roofline and CPU-oracle legs.
 """
 import argparse
 import json
@@ -32,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--workload", default="c3",
+                    help="a finalize-routing workload (c1..c5, ...) or an upstream-step one (g1_*)")
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -101,6 +107,122 @@ def cpu_baseline(w, inp, budget_s):
                       f"{w.N} columns) of workload {w.name}; {spent:.1f} s single-threaded"}
 
 
+def time_steps(step, args, dev):
+    """Warm up, then time exactly args.steps calls: whole-run events plus one
+    event pair per call, all on the launch stream.  Returns (ms_per_step,
+    mean_launch_ms)."""
+    import torch
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    return t_start.elapsed_time(t_end) / args.steps, sum(per_launch_ms) / len(per_launch_ms)
+
+
+def gemm1_cpu_baseline(w, inp, budget_s):
+    """Time the upstream-step oracle on a growing seeded sample of tokens."""
+    import numpy as np
+    import torch
+    from oracle import gemm1 as og
+    u8 = lambda x: x.detach().contiguous().view(torch.uint8).cpu().numpy()
+    h = [u8(inp["xin"]), u8(inp["w13"]), u8(inp["scale"]), u8(inp["xin_scale"]),
+         inp["group_list"].cpu().numpy()]
+    kind = 0 if w.fp8 == "e4m3fn" else 1
+    okind = 0 if w.out_fp8 == "e4m3fn" else 1
+    routed = np.flatnonzero(og.routed_tokens(h[4], w.group_list_type, w.M))
+    order = np.random.default_rng(12345).permutation(routed)
+    n, spent, done = 1, 0.0, 0
+    while done < order.size:
+        rows = order[done:done + n]
+        t0 = time.perf_counter()
+        og.gemm1_swiglu_quant(*h, w.group_list_type, w.transpose_w13, kind, okind, rows=rows)
+        spent += time.perf_counter() - t0
+        done += rows.size
+        if spent >= budget_s:
+            break
+        n = max(1, int(done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
+    flops = 2.0 * done * w.H * 2 * w.I
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {routed.size} routed tokens (all {w.I} outputs) of workload "
+                      f"{w.name}; {spent:.1f} s single-threaded"}
+
+
+def gemm1_main(args, w):
+    import torch
+    import mxfp8_grouped_gemm_group_amd as gfr
+    from mxfp8_grouped_gemm_group_amd import traffic as traffic_mod
+    from mxfp8_grouped_gemm_group_amd.workloads import make_gemm1_inputs
+
+    gfr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_gemm1_inputs(w, dev)
+    wb = inp["w13"].numel()
+    n_sets = max(1, -(-(1 << 30) // wb)) if wb < (1 << 29) else 1
+    w_sets = [inp["w13"]] + [inp["w13"].clone() for _ in range(n_sets - 1)]
+    q = torch.zeros((w.M, w.I), dtype=torch.uint8, device=dev).view(inp["out_dtype"])
+    qs = torch.zeros((w.M, w.I // 64, 2), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        gfr.gemm1_swiglu_quant(inp["xin"], w_sets[i % n_sets], inp["scale"], inp["xin_scale"],
+                               inp["group_list"], inp["group_list_type"], inp["transpose_w13"],
+                               inp["out_dtype"], x1_out=q, x1_scale_out=qs)
+
+    ms_per_step, mean_launch_ms = time_steps(step, args, dev)
+    flops, alg_bytes = w.flops(), w.algorithmic_bytes()
+    achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": "effective TFLOP/s (2*M*H*2I/t) + % of binding roofline, upstream gate||up "
+                  "step (SwiGLU + MX quantisation)",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8 (fp8 x fp8 x e8m0 -> f32 -> mx fp8)",
+        "data": "synthetic (seeded; FP8 from N(0,1), E8M0 exponents uniform)",
+        "config": {
+            "workload": f"{w.name}: M={w.M} H={w.H} I={w.I} E={w.E} fp8={w.fp8} "
+                        f"out={w.out_fp8} transpose_w13={w.transpose_w13} "
+                        f"group_list_type={w.group_list_type}",
+            "weight_copies_rotated": n_sets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_mod.recorded_traffic(w.name),
+            "kernel": "gemm1_swiglu_kernel (gfr gate||up grouped MXFP8 GEMM + SwiGLU + MX quant)",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mean_launch_ms": round(mean_launch_ms, 5),
+            "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = gemm1_cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -113,8 +235,11 @@ def main():
     import torch
     import mxfp8_grouped_gemm_group_amd as gfr
     from mxfp8_grouped_gemm_group_amd import traffic as traffic_mod
-    from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_inputs
+    from mxfp8_grouped_gemm_group_amd.workloads import GEMM1_WORKLOADS, WORKLOADS, make_inputs
 
+    if args.workload in GEMM1_WORKLOADS:
+        gemm1_main(args, GEMM1_WORKLOADS[args.workload])
+        return
     gfr.load_library()
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -139,27 +264,7 @@ def main():
             inp["transpose_x2"], deterministic=args.deterministic, workspace=ws,
             split_k=args.split_k)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = total_ms / args.steps
-    mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    ms_per_step, mean_launch_ms = time_steps(step, args, dev)
 
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()

@@ -105,17 +105,18 @@ constexpr int kCoopRows = kTileM * kWavesPerBlock;   // 128
 
 // Rows of one cooperative unit: experts with more than 128 rows use 256-row
 // groups (each wave two 32-row fragments: twice the MFMAs per streamed and
-// per LDS-read weight step), smaller ones 128-row groups.  FP4 units keep one
-// fragment (two would not fit the register file next to FP4's 8 MFMAs per
-// step).
-template <int FMT>
+// per LDS-read weight step), smaller ones 128-row groups.  Units whose
+// fragment has 8 accumulators (FP4 [K,N]; the upstream step with [K,N]
+// weights, gate and up side by side) keep one fragment: two would not fit the
+// register file.  WIDE says whether two-fragment groups are used.
+template <bool WIDE>
 __device__ __forceinline__ int coop_group_rows(int cnt) {
-    return (FMT != 4 && cnt > kCoopRows) ? 2 * kCoopRows : kCoopRows;
+    return (WIDE && cnt > kCoopRows) ? 2 * kCoopRows : kCoopRows;
 }
 
 constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 
-template <int FMT>
+template <bool WIDE>
 __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
                                 int64_t *s_scan) {
     const int tid = threadIdx.x;
@@ -166,7 +167,7 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         }
         run += c[i];
         const int64_t si = cnt >= kCoopMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
-        const int gr = coop_group_rows<FMT>(cnt);
+        const int gr = coop_group_rows<WIDE>(cnt);
         const int64_t li = cnt >= kCoopMinRows ? ((cnt + gr - 1) / gr) * n_tiles : 0;
         items[i] = si | (li << 32);
         isum += items[i];
@@ -473,6 +474,7 @@ __device__ __forceinline__ void epilogue_swiglu(const FusedParams &p, const v16f
     for (int f = 0; f < RF; ++f) {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj) {
+            if (n0 + 32 * jj >= I) continue;   // past I (whole 32-blocks, wave-uniform)
             float sw[16], am[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -547,10 +549,16 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     constexpr bool FP4 = FMT == 4;
     constexpr bool KN4 = FP4 && KN;
     // OP 0: finalize routing (weight columns n0 + tile column).  OP 1: the
-    // upstream step -- the tile's first half of columns comes from the gate
-    // block [n0, n0 + half) and its second half from the up block
-    // [I + n0, I + n0 + half) of the 2I weight columns.
+    // upstream step.  [N,K] weights: the tile's first half of columns comes
+    // from the gate block [n0, n0 + 32) and its second half from the up block
+    // [I + n0, I + n0 + 32) of the 2I weight columns.  [K,N] weights (SPLIT):
+    // every K step is taken twice, as two virtual steps -- first the gate
+    // tile [n0, n0 + 128), then the up tile [I + n0, I + n0 + 128) -- so each
+    // weight row segment read stays a whole 128 bytes; the halves accumulate
+    // into acc[f][0..3] and acc[f][4..7].
     static_assert(OP == 0 || !FP4, "the upstream step is MXFP8 only");
+    constexpr bool SPLIT = OP == 1 && KN;
+    constexpr int kVS = SPLIT ? 2 : 1;      // virtual steps per K step
     constexpr int kHalf = (KN ? kTileN : kTileNNK) / 2;
     const int up0 = OP == 1 ? __builtin_amdgcn_readfirstlane(p.I) : 0;
     constexpr int D = !COOP ? kStages
@@ -576,7 +584,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // (a cooperative wave past the expert's last row has mcount <= 0: its
     // loads have an empty range and return zeros, its epilogue writes nothing)
     if (mcount < 0) mcount = 0;
-    auto wcol = [&](int tc) { return OP == 0 || tc < kHalf ? n0 + tc : up0 + n0 + tc - kHalf; };
+    auto wcol = [&](int tc) {
+        return OP == 0 || SPLIT || tc < kHalf ? n0 + tc : up0 + n0 + tc - kHalf;
+    };
     bool arow_ok[RF];
     int va[RF], vsa[RF];
 #pragma unroll
@@ -595,8 +605,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // Weight-tile load offsets (lane part) and weight-scale offsets.  Columns
     // past N (last partial n-tile) re-read column n0; their results are never
     // written.
-    int vb[KN ? (KN4 ? 2 : 1) : kTileLoads];
-    int vsb[KN4 ? 8 : 4];
+    int vb[KN ? (KN4 || SPLIT ? 2 : 1) : kTileLoads];
+    int vsb[KN4 || SPLIT ? 8 : 4];
     uint32_t tr_addr[KN4 ? 8 : 4] = {};   // [K,N]: per 32-column group, slot-relative
     int sb_shift = 0;
     if constexpr (KN4) {
@@ -630,6 +640,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // (l%8) ^ ((r >> 1) & 3) = (l%8) ^ ((l >> 4) & 3)
         const int chunk_col = wcol(16 * ((lane & 7) ^ ((lane >> 4) & 3)));
         vb[0] = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
+        if constexpr (SPLIT) {   // the up tile: same chunk, I columns further
+            const int up_col = up0 + chunk_col;
+            vb[1] = (lane >> 3) * N + (up_col < N ? up_col : up0 + n0);
+        }
         // transpose reads: lane s of 16-lane group G reads K row
         // 16g + (s >> 1) + (read's K offset), columns 32j + 16(G & 1) + 8(s & 1)
         const int G = lane >> 4, sl = lane & 15, i = sl >> 1, h = sl & 1;
@@ -642,6 +656,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         for (int j = 0; j < 4; ++j) {
             const int col = wcol(32 * j + c);
             vsb[j] = ((col < N ? col : n0) & ~1) * 2;
+            if constexpr (SPLIT) {
+                const int up_col = up0 + col;
+                vsb[4 + j] = ((up_col < N ? up_col : up0 + n0) & ~1) * 2;
+            }
         }
         sb_shift = 8 * (2 * (c & 1) + g);
     } else {
@@ -667,7 +685,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 
     // (the upstream step has no row_index / logit)
     const RowInfo rinfo = OP == 0 ? load_row_info<RF>(p, m0, mcount) : RowInfo{};
-    constexpr int NA = KN4 ? 8 : 4;   // accumulators per row fragment
+    constexpr int NA = KN4 || SPLIT ? 8 : 4;   // accumulators per row fragment
     v16f acc[RF][NA];
 #pragma unroll
     for (int f = 0; f < RF; ++f)
@@ -683,7 +701,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
     StepRegs<kAL, RF, kSB, kSW> regs[D];
 
-    auto issue = [&](int ks, int slot) {
+    // hf: SPLIT's tile of virtual step vs (0 gate, 1 up) = vs & 1, passed as
+    // the unrolled ring index's parity so that it is a compile-time constant
+    // (ks0 * 2 and D are even; for the clamped re-reads past the last step it
+    // may differ, and those are never consumed)
+    auto issue = [&](int vs, int slot, int hf) {
+        const int ks = SPLIT ? vs >> 1 : vs;       // K step of virtual step vs
         const int k0 = ks * kStepA;
         __builtin_amdgcn_sched_barrier(0);
         StepRegs<kAL, RF, kSB, kSW> &r = regs[slot];
@@ -712,8 +735,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                 r.sb[j][0] = v.x;
                 r.sb[j][1] = v.y;
             } else {
-                r.sb[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
-                                                                  KN ? ks * 2 * N : kBlk * ks, 0);
+                r.sb[j][0] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rsb, SPLIT ? vsb[4 * hf + j] : vsb[j], KN ? ks * 2 * N : kBlk * ks, 0);
             }
         }
         // (the instruction's immediate offset would move both addresses, so
@@ -723,8 +746,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             const int u = u0 + uu;
             lds_void_t *dst = (lds_void_t *)(ring + slot * kSlotBytes + u * 1024);
             if (KN)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[KN4 ? (u & 1) : 0],
-                                                         (ks * kStepK + 8 * u) * Nb, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, dst, 16, vb[KN4 ? (u & 1) : SPLIT ? hf : 0], (ks * kStepK + 8 * u) * Nb,
+                    0, 0);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[uu], k0, 0, 0);
         }
@@ -762,7 +786,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
     };
 
-    auto mma = [&](int slot, const BTile &b, bool live, int ks) {
+    auto mma = [&](int slot, const BTile &b, bool live, int vs, int hf) {
+        const int ks = SPLIT ? vs >> 1 : vs;
         StepRegs<kAL, RF, kSB, kSW> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
@@ -788,7 +813,15 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                 for (int j = 0; j < 4; ++j) {
                     const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
                                     b[4 * j + 2].x, b[4 * j + 2].y, b[4 * j + 3].x, b[4 * j + 3].y};
-                    acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
+                    if constexpr (SPLIT) {
+                        if (hf)
+                            acc[f][4 + j] = mfma<FMT, 0>(a, bj, acc[f][4 + j], sa,
+                                                         r.sb[j][0] >> sb_shift);
+                        else
+                            acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
+                    } else {
+                        acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
+                    }
                 }
             } else if constexpr (FP4) {
                 // four 64-K sub-steps s, two 32-column groups j; operand =
@@ -839,11 +872,11 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     constexpr int kOpsPerStep = RF * (kAL + 1) + kSB + kTileLoads;
     static_assert((D - 1) * kOpsPerStep < 64, "vmcnt range");
     static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
-    const int n_steps = ks1 - ks0;
-    auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
+    const int n_steps = (ks1 - ks0) * kVS;        // virtual steps
+    auto step_of = [&](int i) { return ks0 * kVS + (i < n_steps ? i : n_steps - 1); };
 
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(step_of(d), d);
+    for (int d = 0; d < D; ++d) issue(step_of(d), d, d & 1);
     wait_vmcnt<(D - 1) * kOpsPerStep>();
     if (COOP) __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -858,9 +891,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             __builtin_amdgcn_sched_barrier(0);
             read_b((d + 1) % D, bt[(d + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            mma(d, bt[d & 1], i < n_steps, step_of(i));
+            mma(d, bt[d & 1], i < n_steps, step_of(i), d & 1);
             __builtin_amdgcn_sched_barrier(0);
-            issue(step_of(i + D), d);
+            issue(step_of(i + D), d, d & 1);
             lds_wait(bt[(d + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -875,7 +908,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
     }
     if constexpr (OP == 1)
-        epilogue_swiglu<KN ? 4 : 2, RF, NA>(p, acc, m0, mcount, n0);
+        epilogue_swiglu<SPLIT ? 8 : 2, RF, NA>(p, acc, m0, mcount, n0);
     else
         epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
@@ -919,7 +952,7 @@ __device__ __forceinline__ void shared_slice(const FusedParams &p, int64_t wave,
 // round-robin.
 //
 // OP 0 is the finalize-routing operator; OP 1 the upstream step, whose items
-// cover a 64- ([K,N]) or 32-column ([N,K]) block of the I outputs (twice that
+// cover a 128- ([K,N]) or 32-column ([N,K]) block of the I outputs (twice that
 // many weight columns: gate and up) and always the whole K range (its
 // epilogue is not linear, so there is no K split).
 template <int FMT, bool TRANS, int OP>
@@ -933,10 +966,15 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
 
     // columns per item: [N, K] 64, [K, N] 128 (FP8) or 256 (FP4)
     constexpr int kTN = TRANS ? kTileNNK : (FMT == 4 ? 2 * kTileN : kTileN);
-    constexpr int kOutN = OP == 0 ? kTN : kTN / 2;   // output columns per item
+    // output columns per item: the weight columns, or for the upstream step
+    // half of them ([N,K]: gate and up columns in one tile) or all of them
+    // ([K,N]: gate and up tiles streamed in turn)
+    constexpr int kOutN = OP == 0 || !TRANS ? kTN : kTN / 2;
     const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
-    build_work_list<FMT>(p, n_tiles, wl, s_scan);
+    // two-fragment cooperative groups except where a fragment has 8 accumulators
+    constexpr bool kWide = FMT != 4 && !(OP == 1 && !TRANS);
+    build_work_list<kWide>(p, n_tiles, wl, s_scan);
     if (OP == 0 && p.det_total && blockIdx.x == 0 && threadIdx.x == 0)
         *p.det_total = wl.routed_tokens;
 
@@ -995,7 +1033,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
             const int e_pref = __builtin_amdgcn_readfirstlane(s_lpref[e]);
-            const int gr = coop_group_rows<FMT>(e_cnt);
+            const int gr = coop_group_rows<kWide>(e_cnt);
             const int mg_count = (e_cnt + gr - 1) / gr;
             const int64_t local = u - static_cast<int64_t>(e_pref) * S;
             const int mg = static_cast<int>(local % mg_count);
@@ -1008,8 +1046,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            if (FMT != 4 && gr > kCoopRows)
-                routed_item<FMT, !TRANS, true, FMT == 4 ? 1 : 2, OP>(
+            if (kWide && gr > kCoopRows)
+                routed_item<FMT, !TRANS, true, kWide ? 2 : 1, OP>(
                     p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
             else
                 routed_item<FMT, !TRANS, true, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,

@@ -43,6 +43,11 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def kernel_name(workload: str) -> str:
+    """The library kernel a workload's bench run launches."""
+    return "gemm1_swiglu_kernel" if workload.startswith("g1_") else "fused_kernel"
+
+
 def _per_dispatch(run_dir: str, counter: str, name_part: str):
     """Counter value (summed over its dimensions) of every dispatch whose kernel
     name contains name_part, in dispatch order."""
@@ -72,15 +77,16 @@ def compute(run_dir: str, workload: str) -> dict:
     copy_kernel = "copy"   # torch's device copy kernels carry "copy" in their names
     f_copy = _steady(_per_dispatch(os.path.join(run_dir, "copy_fetch"), "FETCH_SIZE", copy_kernel))
     w_copy = _steady(_per_dispatch(os.path.join(run_dir, "copy_write"), "WRITE_SIZE", copy_kernel))
-    f_k = _steady(_per_dispatch(os.path.join(run_dir, f"{workload}_fetch"), "FETCH_SIZE", "fused_kernel"))
-    w_k = _steady(_per_dispatch(os.path.join(run_dir, f"{workload}_write"), "WRITE_SIZE", "fused_kernel"))
+    kname = kernel_name(workload)
+    f_k = _steady(_per_dispatch(os.path.join(run_dir, f"{workload}_fetch"), "FETCH_SIZE", kname))
+    w_k = _steady(_per_dispatch(os.path.join(run_dir, f"{workload}_write"), "WRITE_SIZE", kname))
     f_scale = f_copy * 1024 / GIB      # counter bytes per real byte read
     w_scale = w_copy * 1024 / GIB
     read_b = f_k * 1024 / f_scale
     write_b = w_k * 1024 / w_scale
     return {
         "workload": workload,
-        "kernel": "fused_kernel",
+        "kernel": kname,
         "kernel_source_sha256_16": kernel_hash(),
         "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
         "fetch_scale": f_scale, "write_scale": w_scale,

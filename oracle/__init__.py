@@ -82,6 +82,13 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_mx_group_slack.argtypes = [
             p, p, p, i32, p, p, i32, p, p, i32, i32, i64, i64, i64, i64, i64, p, i64, p]
         lib.oracle_mx_group_slack.restype = ctypes.c_int
+        lib.oracle_w4a8_finalize_routing.argtypes = [
+            p, p, p, p, p,            # x1 x2 scale offset pertoken_scale
+            p, i32, p, p, p,          # group_list type logit row_index shared_input
+            dbl, i64, i64, p,         # shared weight, offset, rows, out_init
+            i64, i64, i64, i64, i64,  # M K N E batch
+            p, i64, p, p]             # rows n_rows res mag
+        lib.oracle_w4a8_finalize_routing.restype = ctypes.c_int
         _lib_handle = lib
     return _lib_handle
 
@@ -218,3 +225,50 @@ def within_tolerance(got, ref, mag, rel=2e-5, abs_=1e-6):
     bound = rel * mag + abs_
     ratio = float(np.max(err / bound)) if err.size else 0.0
     return bool(np.all(err <= bound)), ratio
+
+
+def w4a8_finalize_routing(x1, x2, scale, offset, pertoken_scale, group_list, group_list_type,
+                          logit, row_index, shared_input, shared_input_weight,
+                          shared_input_offset, out_init, rows=None):
+    """The A2/A3 W4A8 variant (oracle_w4a8_finalize_routing in gfr_oracle.c).
+
+    x1 int8 [M, K]; x2 uint8 [E, K, N/2] (two signed 4-bit values per byte
+    along n, element 2j in the low nibble); scale and offset (or None)
+    float32 [E, 1, N]; pertoken_scale float32 [M]; the rest as
+    gmm_finalize_routing.  Returns (out, mag) float64 [len(rows), N]."""
+    x1 = np.ascontiguousarray(x1)
+    if x1.dtype != np.int8:
+        raise TypeError(f"x1 must be int8, got {x1.dtype}")
+    x2 = _u8(x2)
+    sc = np.ascontiguousarray(scale, dtype=np.float32)
+    of = None if offset is None else np.ascontiguousarray(offset, dtype=np.float32)
+    pts = np.ascontiguousarray(pertoken_scale, dtype=np.float32)
+    g = np.ascontiguousarray(group_list, dtype=np.int64)
+    ri = np.ascontiguousarray(row_index, dtype=np.int64)
+    init = np.ascontiguousarray(out_init, dtype=np.float32)
+    M, K = x1.shape
+    E, N = x2.shape[0], x2.shape[2] * 2
+    assert x2.shape[1] == K and sc.shape == (E, 1, N) and pts.shape == (M,)
+    assert of is None or of.shape == (E, 1, N)
+    batch = init.shape[0]
+    lg = None if logit is None else np.ascontiguousarray(logit, dtype=np.float32)
+    sh = None if shared_input is None else np.ascontiguousarray(shared_input, dtype=np.uint16)
+    R = 0 if sh is None else sh.shape[0]
+    if rows is None:
+        rows_arr, n_rows = None, batch
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows_arr.shape[0]
+    res = np.zeros((n_rows, N), np.float64)
+    mag = np.zeros((n_rows, N), np.float64)
+    rc = _lib().oracle_w4a8_finalize_routing(
+        x1.ctypes.data, x2.ctypes.data, sc.ctypes.data, None if of is None else of.ctypes.data,
+        pts.ctypes.data, g.ctypes.data, int(group_list_type),
+        None if lg is None else lg.ctypes.data, ri.ctypes.data,
+        None if sh is None else sh.ctypes.data, float(shared_input_weight),
+        int(shared_input_offset), R, init.ctypes.data, M, K, N, E, batch,
+        None if rows_arr is None else rows_arr.ctypes.data, n_rows,
+        res.ctypes.data, mag.ctypes.data)
+    if rc:
+        raise OracleError(rc)
+    return res, mag

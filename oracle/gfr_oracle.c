@@ -27,6 +27,9 @@
  * summation error (about K * 2^-53 relative), which is negligible against the
  * FP32 tolerance the GPU path is held to.
  *
+ * The end of this file adds the A2/A3 W4A8 variant of [P3] (INT8 x INT4 with
+ * FP32 per-channel and per-token scales) with the same routing.
+ *
  * Alongside out, the oracle returns mag = |out_init| + sum |w_t * term| +
  * |shared term| per element: the sum of the magnitudes of every term that
  * enters that element.  The GPU tolerance is expressed against it.
@@ -470,5 +473,132 @@ done:
     free(start);
     free(end);
     free(expert_of);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * The A2/A3 W4A8 variant ([P3] A2/A3 parameter notes and pseudo-quant notes):
+ * INT8 x1, INT4 weights, a fused per-channel FP32 scale, an FP32 per-token
+ * scale, an optional asymmetric offset, then the same routing and shared
+ * term as the MX operator.  Formula 1 of [P3] with these operands:
+ *
+ *   y[t, n] = pertoken_scale[t] * ( scale[e, n] * sum_k x1[t, k] * w[e, k, n]
+ *                                   + offset[e, n] * sum_k x1[t, k] )
+ *   out[row_index[t], n] += logit[t] * y[t, n]
+ *
+ * (offset = antiquantOffset * scale, the asymmetric form: dequantised weight
+ * (w + antiquantOffset) * scale; absent for the symmetric form.)
+ *
+ * Layouts: x1 [M, K] int8; x2 [E, K, N/2] bytes, two signed 4-bit values per
+ * byte along n, element 2j in the low nibble of byte j (the reading of the
+ * "(e, k, n/8) INT32" packing, nibbles in little-endian order); scale and
+ * offset [E, 1, N] float32 (one group along K); pertoken_scale [M] float32;
+ * the rest as oracle_gmm_finalize_routing.  The integer sums are exact
+ * (int64); the rest is double precision.  mag accumulates |init| +
+ * |logit * pts| * (|scale| * sum |x w| + |offset| * sum |x|) + |shared|.
+ * ------------------------------------------------------------------------- */
+
+/* Signed value of a 4-bit two's complement code. */
+static int int4_value(uint8_t c)
+{
+    return (c & 8) ? (int)(c & 15) - 16 : (int)(c & 15);
+}
+
+int oracle_w4a8_finalize_routing(
+    const int8_t *x1, const uint8_t *x2, const float *scale, const float *offset,
+    const float *pertoken_scale, const int64_t *group_list, int group_list_type,
+    const float *logit, const int64_t *row_index, const uint16_t *shared_input,
+    double shared_input_weight, int64_t shared_input_offset, int64_t shared_rows,
+    const float *out_init, int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+    const int64_t *rows, int64_t n_rows, double *res_out, double *mag_out)
+{
+    if (M < 0 || K <= 0 || N < 0 || N % 2 != 0 || E <= 0 || batch < 0 || n_rows < 0)
+        return ORACLE_BAD_ARG;
+    if (rows == NULL && n_rows != batch)
+        return ORACLE_BAD_ARG;
+    if (shared_input != NULL &&
+        (shared_input_offset < 0 || shared_rows < 0 ||
+         shared_input_offset + shared_rows > batch))
+        return ORACLE_BAD_SHARED_RANGE;
+    int64_t *start = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t *end = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t *expert_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    int64_t *dot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    int64_t *adot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    int rc = ORACLE_OK;
+    if (!start || !end || !expert_of || !dot || !adot) {
+        rc = ORACLE_NO_MEMORY;
+        goto done;
+    }
+    rc = oracle_expert_ranges(group_list, E, group_list_type, M, start, end);
+    if (rc != ORACLE_OK)
+        goto done;
+    for (int64_t t = 0; t < M; ++t)
+        expert_of[t] = -1;
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t t = start[e]; t < end[e]; ++t)
+            expert_of[t] = e;
+    for (int64_t t = 0; t < M; ++t)
+        if (expert_of[t] >= 0 && (row_index[t] < 0 || row_index[t] >= batch)) {
+            rc = ORACLE_BAD_ROW_INDEX;
+            goto done;
+        }
+
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t b = rows ? rows[i] : i;
+        if (b < 0 || b >= batch) {
+            rc = ORACLE_BAD_ARG;
+            goto done;
+        }
+        double *res = res_out + i * N;
+        double *mag = mag_out + i * N;
+        for (int64_t n = 0; n < N; ++n) {
+            res[n] = (double)out_init[b * N + n];
+            mag[n] = fabs(res[n]);
+        }
+        for (int64_t t = 0; t < M; ++t) {
+            const int64_t e = expert_of[t];
+            if (e < 0 || row_index[t] != b)
+                continue;
+            const double w = (logit ? (double)logit[t] : 1.0) * (double)pertoken_scale[t];
+            int64_t xsum = 0, xabs = 0;
+            for (int64_t n = 0; n < N; ++n)
+                dot[n] = adot[n] = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t xv = x1[t * K + k];
+                xsum += xv;
+                xabs += xv < 0 ? -xv : xv;
+                const uint8_t *wrow = x2 + (e * K + k) * (N / 2);   /* row k of expert e */
+                for (int64_t n = 0; n < N; ++n) {
+                    const uint8_t byte = wrow[n / 2];
+                    const int64_t p = xv * int4_value((n & 1) ? (uint8_t)(byte >> 4) : byte);
+                    dot[n] += p;
+                    adot[n] += p < 0 ? -p : p;
+                }
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                const double s = (double)scale[e * N + n];
+                const double o = offset ? (double)offset[e * N + n] : 0.0;
+                res[n] += w * (s * (double)dot[n] + o * (double)xsum);
+                mag[n] += fabs(w) * (fabs(s) * (double)adot[n] + fabs(o) * (double)xabs);
+            }
+        }
+        if (shared_input && b >= shared_input_offset &&
+            b < shared_input_offset + shared_rows) {
+            const int64_t r = b - shared_input_offset;
+            for (int64_t n = 0; n < N; ++n) {
+                const double v = shared_input_weight *
+                                 oracle_decode_bf16(shared_input[r * N + n]);
+                res[n] += v;
+                mag[n] += fabs(v);
+            }
+        }
+    }
+done:
+    free(start);
+    free(end);
+    free(expert_of);
+    free(dot);
+    free(adot);
     return rc;
 }

@@ -215,6 +215,52 @@ int gfr_gemm1_swiglu_quant(const void *xin, const void *w13, const uint8_t *scal
                            int transpose_w13, int fp8_kind, int out_kind, int64_t M, int64_t H,
                            int64_t I, int64_t E, void *stream, const gfr_options *opts);
 
+/*
+ * gfr_w4a8_finalize_routing — the A2/A3 W4A8 variant of the operator ([P3]
+ * A2/A3 parameter notes: INT8 x1, INT4 x2, INT64-typed fused scale (e, 1, n),
+ * FP32 offset (e, 1, n), FP32 perTokenScale (m); pseudo-quant notes: scale is
+ * the offline fusion of per-channel and per-group scales, offset the
+ * asymmetric term antiquantOffset * scale; formula 1 for the product).  For
+ * every expert e and token t in its group_list range:
+ *
+ *   y[t, n] = pertoken_scale[t] * ( scale[e, n] * sum_k x1[t, k] * w[e, k, n]
+ *                                   + offset[e, n] * sum_k x1[t, k] )
+ *   out[row_index[t], n] += logit[t] * y[t, n]
+ *   out[off + r, n]      += shared_input_weight * shared_input[r, n]
+ *
+ *  x1              int8 [M, K].
+ *  x2              signed 4-bit weights [E, K, N/2] bytes: two per byte along
+ *                  n, element 2j in the low nibble of byte j (the pages'
+ *                  (e, k, n/8) INT32 packing read as little-endian nibbles).
+ *  scale           float32 [E, 1, N]: the fused per-channel scale (the pages
+ *                  type it INT64; its value is taken here as FP32).
+ *  offset          float32 [E, 1, N], or NULL for symmetric weights.
+ *  pertoken_scale  float32 [M].
+ *  group_list, group_list_type, logit, row_index, shared_input (bf16 [R, N]),
+ *  shared_input_weight, shared_input_offset, out (float32 [batch, N], in/out),
+ *  M, K, N, E, batch, shared_rows, stream: as gmm_finalize_routing.
+ *  opts            as gmm_finalize_routing_ex (deterministic mode, workspace
+ *                  from gfr_workspace_size, status word, K split);
+ *                  scale_per_expert must be 0 (the scale always has an expert
+ *                  axis).
+ *
+ * The pages' bias input (8 * w * scale summed over k) restores a term that
+ * their kernel's INT4 decomposition of the activations drops; the integer
+ * products here are exact, so it has no counterpart.  Integer sums are exact;
+ * the scaling is FP32.
+ *
+ * Limits (GFR_ERR_UNSUPPORTED): K % 128 != 0, K > 65536, N % 32 != 0, E
+ * outside [1, 1024], M or batch >= 2^31.  x1 and x2 must be 16-byte aligned,
+ * scale and offset 8-byte aligned.  Returns a gfr_status.
+ */
+int gfr_w4a8_finalize_routing(const int8_t *x1, const uint8_t *x2, const float *scale,
+                              const float *offset, const float *pertoken_scale,
+                              const int64_t *group_list, int group_list_type, const float *logit,
+                              const int64_t *row_index, const uint16_t *shared_input,
+                              float shared_input_weight, int64_t shared_input_offset, float *out,
+                              int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                              int64_t shared_rows, void *stream, const gfr_options *opts);
+
 /* Static, NUL-terminated description of a gfr_status. */
 const char *gfr_status_string(int status);
 

@@ -61,6 +61,10 @@ def load_library() -> ctypes.CDLL:
             ctypes.c_void_p] * 2 + [ctypes.c_int] * 3 + [ctypes.c_int64] * 4 + [
             ctypes.c_void_p, ctypes.POINTER(GfrOptions)]
         lib.gfr_gemm1_swiglu_quant.restype = ctypes.c_int
+        lib.gfr_w4a8_finalize_routing.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] + [
+            ctypes.c_void_p] * 3 + [ctypes.c_float, ctypes.c_int64, ctypes.c_void_p] + [
+            ctypes.c_int64] * 6 + [ctypes.c_void_p, ctypes.POINTER(GfrOptions)]
+        lib.gfr_w4a8_finalize_routing.restype = ctypes.c_int
         lib.gfr_status_string.argtypes = [ctypes.c_int]
         lib.gfr_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -222,3 +226,62 @@ def gemm1_swiglu_quant(xin, w13, scale, xin_scale, group_list, group_list_type,
     if rc:
         raise GfrError(rc, status_string(rc))
     return x1_out, x1_scale_out
+
+
+def w4a8_finalize_routing(x1, x2, scale, offset, pertoken_scale, group_list, group_list_type,
+                          logit, row_index, shared_input, shared_input_weight,
+                          shared_input_offset, out, *, deterministic=False, workspace=None,
+                          status=None, split_k=0, stream=None):
+    """The W4A8 variant (include/gfr.h, gfr_w4a8_finalize_routing): x1 int8
+    [M, K]; x2 uint8 [E, K, N/2] (two signed 4-bit weights per byte along n,
+    element 2j in the low nibble); scale and offset (or None) float32
+    [E, 1, N]; pertoken_scale float32 [M]; the rest as gmm_finalize_routing.
+    Updates out in place and returns it."""
+    lib = load_library()
+    _need(x1.dtype == torch.int8 and x1.dim() == 2, "x1 must be int8 [M, K]")
+    _need(x2.dtype == torch.uint8 and x2.dim() == 3, "x2 must be uint8 [E, K, N/2]")
+    M, K = x1.shape
+    E = x2.shape[0]
+    _need(x2.shape[1] == K, "x2 [E, K, N/2] does not match K")
+    N = 2 * x2.shape[2]
+    _need(scale.dtype == torch.float32 and tuple(scale.shape) == (E, 1, N), "bad scale")
+    _need(offset is None or (offset.dtype == torch.float32 and tuple(offset.shape) == (E, 1, N)),
+          "bad offset")
+    _need(pertoken_scale.dtype == torch.float32 and tuple(pertoken_scale.shape) == (M,),
+          "bad pertoken_scale")
+    _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
+    _need(row_index.dtype == torch.int64 and tuple(row_index.shape) == (M,), "bad row_index")
+    if logit is not None:
+        _need(logit.dtype == torch.float32 and tuple(logit.shape) == (M,), "bad logit")
+    _need(out.dtype == torch.float32 and out.dim() == 2 and out.shape[1] == N, "bad out")
+    batch = out.shape[0]
+    R = 0
+    if shared_input is not None:
+        _need(shared_input.dtype == torch.bfloat16 and shared_input.dim() == 2
+              and shared_input.shape[1] == N, "bad shared_input")
+        R = shared_input.shape[0]
+    dev = out.device
+    for t in (x1, x2, scale, offset, pertoken_scale, group_list, row_index, out, logit,
+              shared_input, workspace, status):
+        if t is not None:
+            _need(t.is_cuda and t.device == dev, "all tensors must be on out's CUDA device")
+            _need(t.is_contiguous(), "all tensors must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ws_bytes = 0
+    if deterministic:
+        need = workspace_size(M, K, N, E, batch, True)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    opts = GfrOptions(int(bool(deterministic)), _ptr(workspace), ws_bytes, _ptr(status),
+                      int(split_k), 0)
+    with torch.cuda.device(dev):
+        rc = lib.gfr_w4a8_finalize_routing(
+            _ptr(x1), _ptr(x2), _ptr(scale), _ptr(offset), _ptr(pertoken_scale),
+            _ptr(group_list), int(group_list_type), _ptr(logit), _ptr(row_index),
+            _ptr(shared_input), float(shared_input_weight), int(shared_input_offset), _ptr(out),
+            M, K, N, E, batch, R, ctypes.c_void_p(stream), ctypes.byref(opts))
+    if rc:
+        raise GfrError(rc, status_string(rc))
+    return out

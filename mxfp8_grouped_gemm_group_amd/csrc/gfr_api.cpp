@@ -62,6 +62,35 @@ int validate(const void *x1, const void *x2, const uint8_t *scale, const uint8_t
     return GFR_OK;
 }
 
+// Launch the finalize-routing path for a filled parameter block: one fused
+// launch (atomic mode) or prep + fused + fixed-order reduce (deterministic).
+int dispatch_finalize(gfr::FusedParams &p, int transpose_x2, int kind, int64_t M, int64_t N,
+                      int64_t batch, hipStream_t s, const gfr_options *opts) {
+    if (opts && opts->deterministic) {
+        const gfr::DetLayout d = gfr::det_layout(M, N, batch);
+        char *ws = static_cast<char *>(opts->workspace);
+        p.wbuf = reinterpret_cast<float *>(ws + d.wbuf);
+        p.det_total = reinterpret_cast<int32_t *>(ws + d.total_tokens);
+        if (gfr::launch_deterministic_prep(p, opts->workspace, s) != hipSuccess) return GFR_ERR_HIP;
+        if (gfr::launch_fused(p, transpose_x2, kind, s) != hipSuccess) return GFR_ERR_HIP;
+        if (gfr::launch_deterministic_reduce(p, opts->workspace, s) != hipSuccess)
+            return GFR_ERR_HIP;
+        return GFR_OK;
+    }
+    if (gfr::launch_fused(p, transpose_x2, kind, s) != hipSuccess) return GFR_ERR_HIP;
+    return GFR_OK;
+}
+
+// Deterministic-mode workspace and alignment checks (shared by both entries).
+int check_det(const gfr_options *opts, const float *out, int64_t M, int64_t N, int64_t batch) {
+    if (!(opts && opts->deterministic)) return GFR_OK;
+    const gfr::DetLayout d = gfr::det_layout(M, N, batch);
+    if (!opts->workspace || opts->workspace_bytes < d.total) return GFR_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(opts->workspace, 256)) return GFR_ERR_BAD_ALIGNMENT;
+    if (!aligned(out, 16)) return GFR_ERR_BAD_ALIGNMENT;   // float4 row reduction
+    return GFR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,16 +132,10 @@ int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale
                       E, batch, shared_rows);
     if (rc != GFR_OK) return rc;
     if (N == 0 || batch == 0) return GFR_OK;  // empty output: nothing to do
-    const bool det = opts && opts->deterministic;
     const int per_expert = opts ? opts->scale_per_expert : 0;
     if (per_expert != 0 && per_expert != 1) return GFR_ERR_BAD_ARG;
-    if (det) {
-        const gfr::DetLayout d = gfr::det_layout(M, N, batch);
-        if (!opts->workspace || opts->workspace_bytes < d.total)
-            return GFR_ERR_WORKSPACE_TOO_SMALL;
-        if (!aligned(opts->workspace, 256)) return GFR_ERR_BAD_ALIGNMENT;
-        if (!aligned(out, 16)) return GFR_ERR_BAD_ALIGNMENT;   // float4 row reduction
-    }
+    rc = check_det(opts, out, M, N, batch);
+    if (rc != GFR_OK) return rc;
     if (!shared_input) shared_rows = 0;
 
     gfr::FusedParams p{};
@@ -137,21 +160,67 @@ int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale
     p.group_list_type = group_list_type;
     p.split_k = opts ? opts->split_k : 0;
     p.scale_e_stride = per_expert ? (K / 32) * N : 0;   // ceil(K/64) * N * 2 bytes
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dispatch_finalize(p, transpose_x2, fp8_kind, M, N, batch,
+                             static_cast<hipStream_t>(stream), opts);
+}
 
-    if (det) {
-        const gfr::DetLayout d = gfr::det_layout(M, N, batch);
-        char *ws = static_cast<char *>(opts->workspace);
-        p.wbuf = reinterpret_cast<float *>(ws + d.wbuf);
-        p.det_total = reinterpret_cast<int32_t *>(ws + d.total_tokens);
-        if (gfr::launch_deterministic_prep(p, opts->workspace, s) != hipSuccess) return GFR_ERR_HIP;
-        if (gfr::launch_fused(p, transpose_x2, fp8_kind, s) != hipSuccess) return GFR_ERR_HIP;
-        if (gfr::launch_deterministic_reduce(p, opts->workspace, s) != hipSuccess)
-            return GFR_ERR_HIP;
-        return GFR_OK;
+int gfr_w4a8_finalize_routing(const int8_t *x1, const uint8_t *x2, const float *scale,
+                              const float *offset, const float *pertoken_scale,
+                              const int64_t *group_list, int group_list_type, const float *logit,
+                              const int64_t *row_index, const uint16_t *shared_input,
+                              float shared_input_weight, int64_t shared_input_offset, float *out,
+                              int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                              int64_t shared_rows, void *stream, const gfr_options *opts) {
+    int rc = check_sizes(M, K, N, E, batch);
+    if (rc != GFR_OK) return rc;
+    if (group_list_type != GFR_GROUP_LIST_CUMSUM && group_list_type != GFR_GROUP_LIST_COUNT)
+        return GFR_ERR_BAD_ARG;
+    // 16-byte weight rows (N/2 bytes); 16 * |sum of K products| < 2^31
+    if (N % 32 != 0 || K > 65536) return GFR_ERR_UNSUPPORTED;
+    const bool routed = M > 0 && N > 0 && batch > 0;
+    if (routed && (!x1 || !x2 || !scale || !pertoken_scale || !group_list || !row_index))
+        return GFR_ERR_NULL_ARG;
+    if (N > 0 && batch > 0 && !out) return GFR_ERR_NULL_ARG;
+    if (shared_input) {
+        if (shared_rows < 0) return GFR_ERR_BAD_SHAPE;
+        if (shared_input_offset < 0 || shared_input_offset + shared_rows > batch)
+            return GFR_ERR_BAD_OFFSET;
+        if (!aligned(shared_input, 16)) return GFR_ERR_BAD_ALIGNMENT;
     }
-    if (gfr::launch_fused(p, transpose_x2, fp8_kind, s) != hipSuccess) return GFR_ERR_HIP;
-    return GFR_OK;
+    if (routed && (!aligned(x1, 16) || !aligned(x2, 16) || !aligned(scale, 8) ||
+                   !aligned(offset, 8) || !aligned(pertoken_scale, 4)))
+        return GFR_ERR_BAD_ALIGNMENT;
+    if (out && !aligned(out, 4)) return GFR_ERR_BAD_ALIGNMENT;
+    if (N == 0 || batch == 0) return GFR_OK;
+    if (opts && opts->scale_per_expert != 0) return GFR_ERR_BAD_ARG;   // scale is [E, 1, N]
+    rc = check_det(opts, out, M, N, batch);
+    if (rc != GFR_OK) return rc;
+    if (!shared_input) shared_rows = 0;
+
+    gfr::FusedParams p{};
+    p.x1 = reinterpret_cast<const uint8_t *>(x1);
+    p.x2 = x2;
+    p.w_scale = scale;
+    p.w_offset = offset;
+    p.pts_f = pertoken_scale;
+    p.group_list = group_list;
+    p.logit = logit;
+    p.row_index = row_index;
+    p.shared = shared_rows > 0 ? shared_input : nullptr;
+    p.shared_w = shared_input_weight;
+    p.shared_off = static_cast<int32_t>(shared_input_offset);
+    p.shared_rows = static_cast<int32_t>(shared_rows);
+    p.out = out;
+    p.status = opts ? opts->status_dev : nullptr;
+    p.M = static_cast<int32_t>(M);
+    p.K = static_cast<int32_t>(K);
+    p.N = static_cast<int32_t>(N);
+    p.E = static_cast<int32_t>(E);
+    p.batch = static_cast<int32_t>(batch);
+    p.group_list_type = group_list_type;
+    p.split_k = opts ? opts->split_k : 0;
+    return dispatch_finalize(p, 0, gfr::kKindW4A8, M, N, batch, static_cast<hipStream_t>(stream),
+                             opts);
 }
 
 int gmm_finalize_routing(const void *x1, const void *x2, const uint8_t *scale,

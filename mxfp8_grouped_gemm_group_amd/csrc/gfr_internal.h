@@ -49,7 +49,14 @@ struct FusedParams {
     uint8_t *qs_out;           // [M, I/64, 2] E8M0 block scales
     int32_t I;
     int32_t out_kind;          // 0 E4M3FN, 1 E5M2
+    // W4A8 variant: x1 int8, x2 int4 pairs; FP32 scales
+    const float *w_scale;      // [E, 1, N] fused per-channel scale
+    const float *w_offset;     // [E, 1, N] asymmetric term, or null
+    const float *pts_f;        // [M] per-token scale
 };
+
+// Internal element kind of the W4A8 variant (launch_fused's fp8_kind).
+constexpr int kKindW4A8 = 8;
 
 // Deterministic-mode workspace layout (all offsets 256-byte aligned):
 //   wbuf          float [M, N]     weighted matmul rows

@@ -34,6 +34,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // Small helpers
@@ -372,7 +373,8 @@ struct RowInfo {
     bool live;    // lane < 32 and the row is one of the expert's tokens
 };
 
-template <int RF>
+// PTS (W4A8): the row weight also carries the FP32 per-token scale.
+template <int RF, bool PTS = false>
 __device__ __forceinline__ RowInfo load_row_info(const FusedParams &p, int m0, int mcount) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     constexpr int kRows = kTileM * RF;
@@ -385,6 +387,10 @@ __device__ __forceinline__ RowInfo load_row_info(const FusedParams &p, int m0, i
         ri.w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lane, 0, 0));
     } else {
         ri.w = 1.0f;
+    }
+    if constexpr (PTS) {
+        const rsrc_t rp = make_rsrc(p.pts_f + m0, static_cast<int64_t>(cnt) * 4);
+        ri.w *= __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, 4 * lane, 0, 0));
     }
     return ri;
 }
@@ -431,6 +437,76 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs
                 unsafeAtomicAdd(p.out + static_cast<int64_t>(dst) * p.N + col, v);
         }
     }
+    }
+}
+
+// W4A8 epilogue.  acc[f][j] / acc[f][4 + j] hold 16 * the exact integer
+// products of the odd / even weight columns n0 + 2(32j + c) + {1, 0}; rsum
+// the lane's share of its row's x1 sum (K halves g = 0, 1 in lanes c, c + 32).
+//   y = (logit * pts) * (scale[e, n] * P + offset[e, n] * sum_k x1)
+// scattered like the MX operator's rows.
+// Scale and offset of this lane's column pairs (2m, 2m + 1), loaded when the
+// item starts: used first inside the per-row branches next to atomics, a load
+// still in flight there would cost a full vmcnt drain per row.
+struct ColScales {
+    float2 sc[4], of[4];
+};
+
+__device__ __forceinline__ ColScales load_col_scales(const FusedParams &p, int e, int n0) {
+    const int c = threadIdx.x & 31;
+    const int N = p.N;
+    ColScales cs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + 2 * (32 * j + c);
+        const int64_t at = static_cast<int64_t>(e) * N + (col < N ? col : n0);
+        cs.sc[j] = *reinterpret_cast<const float2 *>(p.w_scale + at);
+        cs.of[j] = p.w_offset ? *reinterpret_cast<const float2 *>(p.w_offset + at)
+                              : float2{0.f, 0.f};
+    }
+    return cs;
+}
+
+template <int RF>
+__device__ __forceinline__ void epilogue_w4a8(const FusedParams &p, const v16i (&acc)[RF][8],
+                                              const int (&rsum)[RF], const ColScales &cs, int m0,
+                                              int n0, bool store_rows, RowInfo ri) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+    const int N = p.N;
+    const int my_dst = row_dst(p, ri);
+    const float2 (&sc)[4] = cs.sc;
+    const float2 (&of)[4] = cs.of;
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+        const int rs = rsum[f] + __shfl_xor(rsum[f], 32);   // row 32f + c, whole K range
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rl = 8 * (r >> 2) + 4 * g + (r & 3);
+            const int row = 32 * f + rl;
+            const int dst = __shfl(my_dst, row);
+            const float w = __shfl(ri.w, row);
+            const float S = static_cast<float>(__shfl(rs, rl));
+            if (dst < 0) continue;
+            const int t = m0 + row;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + 2 * (32 * j + c);
+                if (col >= N) continue;
+                const float pe = static_cast<float>(acc[f][4 + j][r] >> 4);   // exact
+                const float po = static_cast<float>(acc[f][j][r] >> 4);
+                const float ve = (sc[j].x * pe + of[j].x * S) * w;
+                const float vo = (sc[j].y * po + of[j].y * S) * w;
+                if (store_rows) {
+                    *reinterpret_cast<float2 *>(p.wbuf + static_cast<int64_t>(t) * N + col) =
+                        float2{ve, vo};
+                } else {
+                    float *o = p.out + static_cast<int64_t>(dst) * N + col;
+                    unsafeAtomicAdd(o, ve);
+                    unsafeAtomicAdd(o + 1, vo);
+                }
+            }
+        }
     }
 }
 
@@ -548,6 +624,18 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // of 128 bytes), eight MFMAs per step.
     constexpr bool FP4 = FMT == 4;
     constexpr bool KN4 = FP4 && KN;
+    // FMT 8, the W4A8 variant: INT8 x1 and signed INT4 [K, N] weights packed
+    // two per byte along N.  Its slot is FP8's (64 K rows of 128 bytes, here
+    // 256 columns) and its operands come out of LDS the same way, as
+    // K-contiguous bytes of a byte column 2j|2j+1.  v_mfma_i32_32x32x32_i8
+    // multiplies them twice: with byte & 0xF0 (= 16 * the odd column's
+    // value) and with (byte << 4) & 0xF0 (= 16 * the even column's value),
+    // both exact; acc[f][j] holds the odd columns, acc[f][4 + j] the even ones.
+    // Lane (c, g) supplies K bytes [16g, 16g + 16) of each 32-K half to both
+    // operands: the product pairs A and B bytes by position, so any K order
+    // shared by the two is exact.
+    constexpr bool I8 = FMT == 8;
+    static_assert(!I8 || (KN && OP == 0), "W4A8: [K, N] weights, finalize routing");
     // OP 0: finalize routing (weight columns n0 + tile column).  OP 1: the
     // upstream step.  [N,K] weights: the tile's first half of columns comes
     // from the gate block [n0, n0 + 32) and its second half from the up block
@@ -579,7 +667,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
     const int Kb = FP4 ? K / 2 : K;    // bytes of one x1 row / one [N, K] weight column
-    const int Nb = FP4 ? N / 2 : N;    // bytes of one [K, N] weight row
+    const int Nb = FP4 || I8 ? N / 2 : N;    // bytes of one [K, N] weight row
     // x1 rows of this tile; padding rows read row 0 and are zeroed before use
     // (a cooperative wave past the expert's last row has mcount <= 0: its
     // loads have an empty range and return zeros, its epilogue writes nothing)
@@ -598,7 +686,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
     const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * Kb, static_cast<int64_t>(mcount) * Kb);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
-    const rsrc_t rb = make_rsrc(p.x2 + static_cast<int64_t>(e) * Kb * N, static_cast<int64_t>(Kb) * N);
+    const int64_t wbytes = KN ? static_cast<int64_t>(K) * Nb : static_cast<int64_t>(N) * Kb;
+    const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     const int u0 = COOP ? w * kTileLoads : 0;   // first tile load this wave issues
 
@@ -634,6 +723,16 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             vsb[j] = ((col < N ? col : n0) & ~1) * 2;
         }
         sb_shift = 8 * (2 * (c & 1) + g);
+    } else if (KN && I8) {
+        // as for FP8 [K, N] below, in bytes: the tile's 128 byte columns are
+        // weight columns [n0, n0 + 256)
+        const int n0b = n0 / 2;
+        const int cb = n0b + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+        vb[0] = (lane >> 3) * Nb + (cb < Nb ? cb : n0b);
+        const int G = lane >> 4, sl = lane & 15, i = sl >> 1, h = sl & 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            tr_addr[j] = (16 * g + i) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((i >> 1) & 3)) + 8 * h;
     } else if (KN) {
         // load u, lane l: K row r = 8u + l/8 (row offset in soffset); it fills
         // physical chunk l%8 of the slot row, which holds logical chunk
@@ -684,22 +783,27 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
 
     // (the upstream step has no row_index / logit)
-    const RowInfo rinfo = OP == 0 ? load_row_info<RF>(p, m0, mcount) : RowInfo{};
-    constexpr int NA = KN4 || SPLIT ? 8 : 4;   // accumulators per row fragment
-    v16f acc[RF][NA];
+    const RowInfo rinfo = OP == 0 ? load_row_info<RF, I8>(p, m0, mcount) : RowInfo{};
+    constexpr int NA = KN4 || SPLIT || I8 ? 8 : 4;   // accumulators per row fragment
+    using Acc = std::conditional_t<I8, v16i, v16f>;
+    Acc acc[RF][NA];
 #pragma unroll
     for (int f = 0; f < RF; ++f)
 #pragma unroll
-        for (int j = 0; j < NA; ++j) acc[f][j] = v16f{};
+        for (int j = 0; j < NA; ++j) acc[f][j] = Acc{};
+    int rsum[RF] = {};   // W4A8: sum of this lane's x1 bytes (its row, its K halves)
+    ColScales cscale;
+    if constexpr (I8) cscale = load_col_scales(p, e, n0);
     // bytes of an x1 row per step: FP8 [K,N] 64, FP4 [K,N] 32, [N,K] 128 (the
     // [N,K] weight column moves the same 128 bytes)
     constexpr int kStepA = KN ? (FP4 ? kStepK / 2 : kStepK) : kStepKNK;
     constexpr int kAL = KN ? (FP4 ? 1 : 2) : 4;      // x1 loads per step
-    constexpr int kSB = KN4 ? 8 : KN ? 4 : 2;        // weight-scale loads per step
+    constexpr int kSA = I8 ? 0 : 1;                  // x1-scale loads per step and fragment
+    constexpr int kSB = I8 ? 0 : KN4 ? 8 : KN ? 4 : 2;   // weight-scale loads per step
     constexpr int kSW = FP4 && !KN ? 2 : 1;          // dwords per scale load
     // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4 (FP8) or 8 (FP4)
     constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
-    StepRegs<kAL, RF, kSB, kSW> regs[D];
+    StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> regs[D];
 
     // hf: SPLIT's tile of virtual step vs (0 gate, 1 up) = vs & 1, passed as
     // the unrolled ring index's parity so that it is a compile-time constant
@@ -709,7 +813,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         const int ks = SPLIT ? vs >> 1 : vs;       // K step of virtual step vs
         const int k0 = ks * kStepA;
         __builtin_amdgcn_sched_barrier(0);
-        StepRegs<kAL, RF, kSB, kSW> &r = regs[slot];
+        StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
 #pragma unroll
         for (int f = 0; f < RF; ++f)
 #pragma unroll
@@ -718,7 +822,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // x1 scale bytes of the step: [K,N] (2 ks + g) & 3 of the dword at
         // (2 ks) & ~3; [N,K] the step's kBlk bytes at kBlk ks
 #pragma unroll
-        for (int f = 0; f < RF; ++f) {
+        for (int f = 0; f < RF * kSA; ++f) {
             if constexpr (kSW == 2) {
                 const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[f], kBlk * ks, 0);
                 r.sa[f][0] = v.x;
@@ -788,13 +892,32 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 
     auto mma = [&](int slot, const BTile &b, bool live, int vs, int hf) {
         const int ks = SPLIT ? vs >> 1 : vs;
-        StepRegs<kAL, RF, kSB, kSW> &r = regs[slot];
+        StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
             const bool on = arow_ok[f] && live;
-            if constexpr (KN4) {
+            if constexpr (I8) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {   // the two 32-K halves of the step
+                    const v4i a = on ? r.a[f][h2] : v4i{};
+                    rsum[f] = __builtin_amdgcn_sdot4(a.x, 0x01010101, rsum[f], false);
+                    rsum[f] = __builtin_amdgcn_sdot4(a.y, 0x01010101, rsum[f], false);
+                    rsum[f] = __builtin_amdgcn_sdot4(a.z, 0x01010101, rsum[f], false);
+                    rsum[f] = __builtin_amdgcn_sdot4(a.w, 0x01010101, rsum[f], false);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const v4i bw = {b[4 * j + 2 * h2].x, b[4 * j + 2 * h2].y,
+                                        b[4 * j + 2 * h2 + 1].x, b[4 * j + 2 * h2 + 1].y};
+                        const v4i m = {static_cast<int>(0xF0F0F0F0u), static_cast<int>(0xF0F0F0F0u),
+                                       static_cast<int>(0xF0F0F0F0u), static_cast<int>(0xF0F0F0F0u)};
+                        acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bw & m, acc[f][j], 0, 0, 0);
+                        acc[f][4 + j] =
+                            __builtin_amdgcn_mfma_i32_32x32x32_i8(a, (bw << 4) & m, acc[f][4 + j], 0, 0, 0);
+                    }
+                }
+            } else if constexpr (KN4) {
                 // one 64-K step, eight 32-column groups; 16-byte operands
                 const v4i z = {0, 0, 0, 0};
                 const v8i a = on ? cat(r.a[f][0], z) : v8i{};
@@ -869,7 +992,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     //   runs step i's MFMAs (operands read in the previous iteration);
     //   refills step i's slot and registers with step i + D;
     //   waits for the LDS reads of step i + 1.
-    constexpr int kOpsPerStep = RF * (kAL + 1) + kSB + kTileLoads;
+    constexpr int kOpsPerStep = RF * (kAL + kSA) + kSB + kTileLoads;
     static_assert((D - 1) * kOpsPerStep < 64, "vmcnt range");
     static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
     const int n_steps = (ks1 - ks0) * kVS;        // virtual steps
@@ -909,6 +1032,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
     if constexpr (OP == 1)
         epilogue_swiglu<SPLIT ? 8 : 2, RF, NA>(p, acc, m0, mcount, n0);
+    else if constexpr (I8)
+        epilogue_w4a8<RF>(p, acc, rsum, cscale, m0, n0, store_rows, rinfo);
     else
         epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
@@ -965,7 +1090,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock * kRingBytes];
 
     // columns per item: [N, K] 64, [K, N] 128 (FP8) or 256 (FP4)
-    constexpr int kTN = TRANS ? kTileNNK : (FMT == 4 ? 2 * kTileN : kTileN);
+    constexpr int kTN = TRANS ? kTileNNK : (FMT == 4 || FMT == 8 ? 2 * kTileN : kTileN);
     // output columns per item: the weight columns, or for the upstream step
     // half of them ([N,K]: gate and up columns in one tile) or all of them
     // ([K,N]: gate and up tiles streamed in turn)
@@ -973,7 +1098,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
     // two-fragment cooperative groups except where a fragment has 8 accumulators
-    constexpr bool kWide = FMT != 4 && !(OP == 1 && !TRANS);
+    constexpr bool kWide = FMT != 4 && FMT != 8 && !(OP == 1 && !TRANS);
     build_work_list<kWide>(p, n_tiles, wl, s_scan);
     if (OP == 0 && p.det_total && blockIdx.x == 0 && threadIdx.x == 0)
         *p.det_total = wl.routed_tokens;
@@ -1047,7 +1172,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             if (kWide && gr > kCoopRows)
-                routed_item<FMT, !TRANS, true, kWide ? 2 : 1, OP>(
+                routed_item<FMT, !TRANS, true, (kWide ? 2 : 1), OP>(
                     p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
             else
                 routed_item<FMT, !TRANS, true, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
@@ -1283,6 +1408,8 @@ hipError_t launch_gemm1(const FusedParams &p, int transpose_w13, int fp8_kind,
 
 hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
                         hipStream_t stream) {
+    if (fp8_kind == kKindW4A8)
+        return launch_fused_t<8, false>(p, stream);
     if (fp8_kind == GFR_FP4_E2M1)
         return transpose_x2 ? launch_fused_t<4, true>(p, stream) : launch_fused_t<4, false>(p, stream);
     if (fp8_kind == GFR_FP8_E4M3FN)

@@ -29,7 +29,7 @@ import torch
 
 FP8_DTYPES = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2,
               "e2m1": torch.float4_e2m1fn_x2}
-FP8_KIND = {"e4m3fn": 0, "e5m2": 1, "e2m1": 2}
+FP8_KIND = {"e4m3fn": 0, "e5m2": 1, "e2m1": 2, "w4a8": 8}
 
 
 @dataclass(frozen=True)
@@ -56,6 +56,7 @@ class Workload:
     seed: int = 0
     topk: int = 0                        # informational (M = batch * topk)
     scale_per_expert: bool = False       # weight scales with a leading expert axis
+    w4a8_offset: bool = True             # W4A8 ("w4a8"): asymmetric offset present
 
     @property
     def fp8_kind(self) -> int:
@@ -84,9 +85,13 @@ class Workload:
         M_r = int(c.sum())
         K, N = self.K, self.N
         kb32 = 2 * ((K + 63) // 64)
-        eb = 0.5 if self.fp8 == "e2m1" else 1   # bytes per element of x1 / x2
-        b = int(eb * (active * K * N + M_r * K))
-        b += M_r * kb32 + N * kb32 * (active if self.scale_per_expert else 1)
+        if self.fp8 == "w4a8":   # int8 x1, int4 x2, FP32 scale (+ offset) and per-token scale
+            b = active * K * N // 2 + M_r * K
+            b += 4 * N * active * (2 if self.w4a8_offset else 1) + 4 * M_r
+        else:
+            eb = 0.5 if self.fp8 == "e2m1" else 1   # bytes per element of x1 / x2
+            b = int(eb * (active * K * N + M_r * K))
+            b += M_r * kb32 + N * kb32 * (active if self.scale_per_expert else 1)
         b += (4 * M_r if self.logit != "none" else 0) + 8 * M_r + 8 * self.E
         b += 8 * self.batch * N + 2 * self.R * N
         return b
@@ -175,11 +180,21 @@ C1_FP4 = _reg(replace(C1, name="c1_fp4", fp8="e2m1", seed=1048))
 C3_FP4 = _reg(replace(C3, name="c3_fp4", fp8="e2m1", seed=1049))
 C4_FP4 = _reg(replace(C4, name="c4_fp4", fp8="e2m1", seed=1050))
 
+# The A2/A3 W4A8 variant ([P3] A2/A3 notes: INT8 x1 with k 2048, INT4 x2 with
+# n 7168, e up to 256): small ragged cases and the page's shape with a
+# skewed routing of 4096 tokens (batch 512, topk 8).
+W4A8_SMALL = _reg(replace(SMALL_N, name="w4a8_small", fp8="w4a8", seed=1061))
+W4A8_SMALL_BIG = _reg(replace(SMALL_BIG_N, name="w4a8_small_big", fp8="w4a8", K=640,
+                              w4a8_offset=False, seed=1062))
+W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=256,
+                        fp8="w4a8", groups=("zipf", 1.2), group_list_type=1, logit="softmax",
+                        row_index="perm", seed=1063))
+
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
-              SMALL_BIG_N_FP4, C3_FP4):
+              SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))
 
@@ -286,6 +301,21 @@ def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
         sc_shape = (E,) + sc_shape
     sc = (127 + rng.integers(lo, hi + 1, size=sc_shape)).astype(np.uint8)
 
+    d = dict(x1=x1, x2=x2, scale=_t(sc, device), pertoken_scale=_t(pts, device),
+             fp8_kind=w.fp8_kind,
+             transpose_x2=bool(w.transpose_x2))
+    d.update(_routing_inputs(w, rng, device))
+    return d
+
+
+def _t(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def _routing_inputs(w: Workload, rng, device) -> dict:
+    """group_list, row_index, logit, shared input and out's initial value
+    (drawn after the operands, in this order)."""
+    M, N, B = w.M, w.N, w.batch
     counts = _counts(w)
     group_list = make_group_list(counts, w.group_list_type)
 
@@ -326,15 +356,47 @@ def make_inputs(w: Workload, device: Union[str, torch.device] = "cpu") -> dict:
     else:
         init = np.zeros((B, N), np.float32)
 
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    t = lambda a: _t(a, device)
     return dict(
-        x1=x1, x2=x2, scale=t(sc), pertoken_scale=t(pts),
         group_list=t(group_list), group_list_type=w.group_list_type,
         logit=None if logit is None else t(logit), row_index=t(row_index),
         shared_input=shared, shared_input_weight=float(w.shared_weight),
         shared_input_offset=int(w.shared_offset) if R > 0 else 0,
-        out=t(init), transpose_x2=bool(w.transpose_x2), fp8_kind=w.fp8_kind,
+        out=t(init),
     )
+
+
+def make_w4a8_inputs(w: Workload, device="cpu") -> dict:
+    """Inputs of the W4A8 variant: x1 int8 [M, K] (uniform over the int8
+    range; exact variant: [-8, 7]); x2 uint8 [E, K, N/2] (uniform bytes, i.e.
+    uniform signed 4-bit pairs); scale float32 [E, 1, N] uniform in
+    [0.001, 0.01] (exact: 2^-4); offset [E, 1, N] uniform in [-0.01, 0.01]
+    (exact: 0, +-2^-5) or None; pertoken_scale float32 [M] uniform in
+    [0.5, 2] (exact: 1 or 0.5); routing, shared input and out as make_inputs."""
+    assert w.fp8 == "w4a8"
+    device = torch.device(device)
+    rng = np.random.default_rng(w.seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    M, K, N, E = w.M, w.K, w.N, w.E
+    lo, hi = (-8, 8) if w.exact else (-128, 128)
+    x1 = torch.randint(lo, hi, (M, K), generator=gen, device=device, dtype=torch.int8)
+    x2 = torch.empty((E, K, N // 2), dtype=torch.uint8, device=device)
+    for e in range(E):
+        x2[e] = torch.randint(0, 256, (K, N // 2), generator=gen, device=device,
+                              dtype=torch.uint8)
+    if w.exact:
+        sc = np.full((E, 1, N), 2.0 ** -4, np.float32)
+        of = rng.choice(np.array([0.0, 2.0 ** -5, -2.0 ** -5], np.float32), size=(E, 1, N))
+        pts = rng.choice(np.array([1.0, 0.5], np.float32), size=M)
+    else:
+        sc = rng.uniform(0.001, 0.01, size=(E, 1, N)).astype(np.float32)
+        of = rng.uniform(-0.01, 0.01, size=(E, 1, N)).astype(np.float32)
+        pts = rng.uniform(0.5, 2.0, size=M).astype(np.float32)
+    d = dict(x1=x1, x2=x2, scale=_t(sc, device),
+             offset=_t(of, device) if w.w4a8_offset else None, pertoken_scale=_t(pts, device))
+    d.update(_routing_inputs(w, rng, device))
+    return d
 
 
 def as_numpy(inputs: dict) -> dict:

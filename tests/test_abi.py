@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     lib = gfr.load_library()
     names = _declared_functions()
     assert {"gmm_finalize_routing", "gmm_finalize_routing_ex", "gfr_workspace_size",
-            "gfr_status_string", "gfr_gemm1_swiglu_quant"} <= names
+            "gfr_status_string", "gfr_gemm1_swiglu_quant", "gfr_w4a8_finalize_routing"} <= names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -134,3 +134,38 @@ def test_gemm1_host_validation(over, code):
 def test_gemm1_scale_per_expert_flag_is_validated():
     opts = GfrOptions(0, None, 0, None, 0, 2)
     assert _call_gemm1(opts=ctypes.byref(opts)) == 7
+
+
+def _call_w4a8(**over):
+    """gfr_w4a8_finalize_routing with fake pointers; only failing or no-op
+    argument combinations are used: nothing is launched."""
+    lib = gfr.load_library()
+    fake = 0x10000
+    a = dict(x1=fake, x2=fake, scale=fake, offset=None, pts=fake, gl=fake, gtype=1, logit=fake,
+             ri=fake, shared=fake, sw=1.0, soff=0, out=fake, M=4096, K=2048, N=7168, E=256,
+             batch=512, R=512, stream=None, opts=None)
+    a.update(over)
+    return lib.gfr_w4a8_finalize_routing(
+        a["x1"], a["x2"], a["scale"], a["offset"], a["pts"], a["gl"], a["gtype"], a["logit"],
+        a["ri"], a["shared"], a["sw"], a["soff"], a["out"], a["M"], a["K"], a["N"], a["E"],
+        a["batch"], a["R"], a["stream"], a["opts"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x1=None), 1), (dict(x2=None), 1), (dict(scale=None), 1), (dict(pts=None), 1),
+    (dict(gl=None), 1), (dict(ri=None), 1), (dict(out=None), 1),
+    (dict(M=-1), 2), (dict(K=0), 2), (dict(E=0), 2),
+    (dict(soff=1), 3), (dict(R=513), 3),
+    (dict(K=2000), 4), (dict(K=131072), 4), (dict(N=7184), 4), (dict(E=1025), 4),
+    (dict(x1=0x10008), 5), (dict(x2=0x10004), 5), (dict(scale=0x10004), 5),
+    (dict(offset=0x10004), 5), (dict(pts=0x10002), 5), (dict(shared=0x10002), 5),
+    (dict(gtype=2), 7),
+    (dict(N=0), 0), (dict(batch=0, R=0, shared=None), 0),
+])
+def test_w4a8_host_validation(over, code):
+    assert _call_w4a8(**over) == code
+
+
+def test_w4a8_options_are_validated():
+    assert _call_w4a8(opts=ctypes.byref(GfrOptions(0, None, 0, None, 0, 1))) == 7
+    assert _call_w4a8(opts=ctypes.byref(GfrOptions(1, None, 0, None, 0, 0))) == 6

@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MXFP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA
 
 
 def parse():
@@ -75,11 +76,28 @@ def copy_calibration(args):
 def cpu_baseline(w, inp, budget_s):
     """Time the oracle on a growing seeded sample of output rows."""
     import numpy as np
+    import torch
     import oracle
     from mxfp8_grouped_gemm_group_amd.workloads import as_numpy
 
-    h = as_numpy(inp)
-    ri = h["row_index"]
+    if w.fp8 == "w4a8":
+        c = lambda t: None if t is None else t.cpu().numpy()
+        sh = inp["shared_input"]
+        sh = None if sh is None else sh.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        args = (c(inp["x1"]), c(inp["x2"]), c(inp["scale"]), c(inp["offset"]),
+                c(inp["pertoken_scale"]), c(inp["group_list"]), inp["group_list_type"],
+                c(inp["logit"]), c(inp["row_index"]), sh, inp["shared_input_weight"],
+                inp["shared_input_offset"], c(inp["out"]))
+        run = lambda rows: oracle.w4a8_finalize_routing(*args, rows=rows)
+        ri = args[8]
+    else:
+        h = as_numpy(inp)
+        run = lambda rows: oracle.gmm_finalize_routing(
+            h["x1"], h["x2"], h["scale"], h["pertoken_scale"], h["group_list"],
+            h["group_list_type"], h["logit"], h["row_index"], h["shared_input"],
+            h["shared_input_weight"], h["shared_input_offset"], h["out_init"],
+            h["transpose_x2"], h["fp8_kind"], rows=rows)
+        ri = h["row_index"]
     total_tokens = int(w.counts().sum())
     routed = ri[:total_tokens]
     rng = np.random.default_rng(12345)
@@ -90,11 +108,7 @@ def cpu_baseline(w, inp, budget_s):
         if rows.size == 0:
             break
         t0 = time.perf_counter()
-        oracle.gmm_finalize_routing(
-            h["x1"], h["x2"], h["scale"], h["pertoken_scale"], h["group_list"],
-            h["group_list_type"], h["logit"], h["row_index"], h["shared_input"],
-            h["shared_input_weight"], h["shared_input_offset"], h["out_init"],
-            h["transpose_x2"], h["fp8_kind"], rows=rows)
+        run(rows)
         spent += time.perf_counter() - t0
         rows_done += rows.size
         tok_done += int(np.isin(routed, rows).sum())
@@ -102,7 +116,8 @@ def cpu_baseline(w, inp, budget_s):
             break
         n = max(1, int(rows_done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
     flops = 2.0 * tok_done * w.K * w.N
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": flops / spent / 1e12, "unit": "TOP/s" if w.fp8 == "w4a8" else "TFLOP/s",
+            "cores": 1, "kind": "oracle",
             "sample": f"{rows_done} of {w.batch} output rows ({tok_done} routed tokens, all "
                       f"{w.N} columns) of workload {w.name}; {spent:.1f} s single-threaded"}
 
@@ -235,7 +250,8 @@ def main():
     import torch
     import mxfp8_grouped_gemm_group_amd as gfr
     from mxfp8_grouped_gemm_group_amd import traffic as traffic_mod
-    from mxfp8_grouped_gemm_group_amd.workloads import GEMM1_WORKLOADS, WORKLOADS, make_inputs
+    from mxfp8_grouped_gemm_group_amd.workloads import (GEMM1_WORKLOADS, WORKLOADS, make_inputs,
+                                                        make_w4a8_inputs)
 
     if args.workload in GEMM1_WORKLOADS:
         gemm1_main(args, GEMM1_WORKLOADS[args.workload])
@@ -244,7 +260,8 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = make_inputs(w, dev)
+    w4a8 = w.fp8 == "w4a8"
+    inp = make_w4a8_inputs(w, dev) if w4a8 else make_inputs(w, dev)
     # Rotate weight copies so the 256 MB last-level cache never holds the
     # next step's weights (cold HBM every step).
     x2_bytes = inp["x2"].numel()
@@ -257,6 +274,14 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     def step(i):
+        if w4a8:
+            gfr.w4a8_finalize_routing(
+                inp["x1"], x2_sets[i % n_sets], inp["scale"], inp["offset"],
+                inp["pertoken_scale"], inp["group_list"], inp["group_list_type"], inp["logit"],
+                inp["row_index"], inp["shared_input"], inp["shared_input_weight"],
+                inp["shared_input_offset"], out, deterministic=args.deterministic,
+                workspace=ws, split_k=args.split_k)
+            return
         gfr.gmm_finalize_routing(
             inp["x1"], x2_sets[i % n_sets], inp["scale"], inp["pertoken_scale"],
             inp["group_list"], inp["group_list_type"], inp["logit"], inp["row_index"],
@@ -279,7 +304,7 @@ def main():
     line = {
         "metric": "effective TFLOP/s (2*M*K*N/t) + % of binding roofline, M=768 K=8192 N=4096 E=32",
         "value": round(tflops, 2),
-        "unit": "TFLOP/s",
+        "unit": "TOP/s" if w4a8 else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -287,9 +312,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("mxfp4 (e2m1 x e2m1 x e8m0 -> f32)" if w.fp8 == "e2m1"
+        "dtype": ("w4a8 (int8 x int4 -> i32, f32 scales)" if w4a8
+                  else "mxfp4 (e2m1 x e2m1 x e8m0 -> f32)" if w.fp8 == "e2m1"
                   else "mxfp8 (fp8 x fp8 x e8m0 -> f32)"),
-        "data": (f"synthetic (seeded; {'E2M1' if w.fp8 == 'e2m1' else 'FP8'} from N(0,1), "
+        "data": ("synthetic (seeded; int8 and int4 uniform, FP32 scales uniform)" if w4a8 else
+                 f"synthetic (seeded; {'E2M1' if w.fp8 == 'e2m1' else 'FP8'} from N(0,1), "
                  "E8M0 exponents uniform)"),
         "config": {
             "workload": f"{w.name}: M={w.M} K={w.K} N={w.N} E={w.E} batch={w.batch} "
@@ -310,7 +337,8 @@ def main():
             "algorithmic_bytes_per_launch": alg_bytes,
             "mean_launch_ms": round(mean_launch_ms, 5),
             "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 /
-                               (MXFP4_PEAK_TFLOPS if w.fp8 == "e2m1" else MXFP8_PEAK_TFLOPS), 4),
+                               (MXFP4_PEAK_TFLOPS if w.fp8 == "e2m1" else
+                                INT8_PEAK_TOPS if w4a8 else MXFP8_PEAK_TFLOPS), 4),
         },
         "cpu_baseline": None,
     }

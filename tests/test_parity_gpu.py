@@ -91,7 +91,9 @@ def slack_for(inp, rows=None):
                                   "small_n_pe_exact", "small_big_t_pe_exact", "small_t_fp4",
                                   "small_big_t_fp4", "small_t_fp4_exact",
                                   "small_big_t_fp4_exact", "small_n_fp4", "small_big_n_fp4",
-                                  "small_n_fp4_exact", "small_big_n_fp4_exact"])
+                                  "small_n_fp4_exact", "small_big_n_fp4_exact",
+                                  "small_t_k768", "small_big_t_k768", "small_t_k768_exact",
+                                  "small_big_t_k768_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]
@@ -121,7 +123,8 @@ def test_full_shapes_sampled(name):
 
 
 @pytest.mark.parametrize("name", ["c5", "c5_exact", "small_n", "small_t", "small_big_n",
-                                  "small_big_t_exact", "small_t_fp4", "small_big_n_fp4"])
+                                  "small_big_t_exact", "small_t_fp4", "small_big_n_fp4",
+                                  "small_big_t_k768"])
 def test_deterministic_mode(name):
     """Deterministic mode: bitwise repeatable, within tolerance of the oracle
     (bit-exact on integer data)."""

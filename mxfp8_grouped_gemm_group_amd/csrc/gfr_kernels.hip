@@ -611,7 +611,12 @@ static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
                   kCoopStagesKN4 * kSlotBytes <= kWavesPerBlock * kRingBytes,
               "cooperative ring fits the block's LDS");
 
-template <int FMT, bool KN, bool COOP, int RF, int OP>
+// One 32-bit element k (uniform, 0..3; larger values read element 3) of w.
+__device__ __forceinline__ uint32_t pick(const v4i &w, int k) {
+    return static_cast<uint32_t>(k <= 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w);
+}
+
+template <int FMT, bool KN, bool COOP, int RF, int OP, bool WS = false>
 __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                             int ks0, int ks1, bool store_rows, char *ring, int w) {
     static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
@@ -798,8 +803,20 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // [N,K] weight column moves the same 128 bytes)
     constexpr int kStepA = KN ? (FP4 ? kStepK / 2 : kStepK) : kStepKNK;
     constexpr int kAL = KN ? (FP4 ? 1 : 2) : 4;      // x1 loads per step
-    constexpr int kSA = I8 ? 0 : 1;                  // x1-scale loads per step and fragment
-    constexpr int kSB = I8 ? 0 : KN4 ? 8 : KN ? 4 : 2;   // weight-scale loads per step
+    // WS (FP8 [N, K], 4-slot ring, K >= 512): the x1 and weight scales are
+    // loaded once per window of four steps, one 16-byte load per x1 row and
+    // per weight column (the four steps' dwords) instead of a 4-byte gather
+    // per step: each load instruction touches 32 rows, so this is 4x fewer
+    // scattered cache-line accesses.  The window load goes first in the load
+    // group of the window's first step (item-relative steps 4m, a multiple of
+    // the ring depth), into the "next" register set, which becomes "current"
+    // after the window's last step; a window that would run past the row's
+    // end starts earlier (still 16 bytes inside the row) and the steps' dword
+    // index is shifted by the difference.
+    static_assert(!WS || (!KN && !FP4 && !I8 && D == 4), "windowed scales: FP8 [N,K], 4 slots");
+    constexpr int kSA = I8 || WS ? 0 : 1;            // x1-scale loads per step and fragment
+    constexpr int kSB = I8 || WS ? 0 : KN4 ? 8 : KN ? 4 : 2;   // weight-scale loads per step
+    constexpr int kXW = WS ? RF + 2 : 0;             // loads per window
     constexpr int kSW = FP4 && !KN ? 2 : 1;          // dwords per scale load
     // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4 (FP8) or 8 (FP4)
     constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
@@ -809,10 +826,27 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // the unrolled ring index's parity so that it is a compile-time constant
     // (ks0 * 2 and D are even; for the clamped re-reads past the last step it
     // may differ, and those are never consumed)
-    auto issue = [&](int vs, int slot, int hf) {
+    v4i wsa[2][RF], wsb[2][2];   // WS: scale windows, [0] current, [1] next
+    int wdl[2] = {0, 0};         // WS: dword shift of a window moved back from the row end
+    const int k_row = K / kStepKNK;   // 128-K steps of a whole row (its scale bytes / 4)
+    auto wload = [&](int vs, int set) {   // the window starting at step vs
+        const int start = vs < k_row - 4 ? vs : k_row - 4;
+        wdl[set] = vs - start;
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+            wsa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + 4 * start, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            wsb[set][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+    };
+
+    auto issue = [&](int vs, int slot, int hf, bool wstart) {
         const int ks = SPLIT ? vs >> 1 : vs;       // K step of virtual step vs
         const int k0 = ks * kStepA;
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (WS) {
+            if (wstart) wload(vs, 1);
+        }
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
 #pragma unroll
         for (int f = 0; f < RF; ++f)
@@ -890,7 +924,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
     };
 
-    auto mma = [&](int slot, const BTile &b, bool live, int vs, int hf) {
+    auto mma = [&](int slot, const BTile &b, bool live, int vs, int hf, int wpos) {
         const int ks = SPLIT ? vs >> 1 : vs;
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
@@ -966,6 +1000,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             } else {
                 // two 64-K halves s, two 32-column groups j; the scale of
                 // 32-block 4 ks + 2 s + g is byte 2 s + g of each scale dword
+                uint32_t sa = r.sa[f][0], sb[2] = {r.sb[0][0], r.sb[1][0]};
+                if constexpr (WS) {
+                    sa = pick(wsa[0][f], wpos + wdl[0]);
+                    sb[0] = pick(wsb[0][0], wpos + wdl[0]);
+                    sb[1] = pick(wsb[0][1], wpos + wdl[0]);
+                }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const v8i a = on ? cat(r.a[f][2 * s2], r.a[f][2 * s2 + 1]) : v8i{};
@@ -973,7 +1013,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         acc[f][j] = mfma<FMT, 0>(a, cat(b[2 * (2 * s2) + j], b[2 * (2 * s2 + 1) + j]),
-                                                 acc[f][j], r.sa[f][0] >> shf, r.sb[j][0] >> shf);
+                                                 acc[f][j], sa >> shf, sb[j] >> shf);
                 }
             }
         }
@@ -992,14 +1032,18 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     //   runs step i's MFMAs (operands read in the previous iteration);
     //   refills step i's slot and registers with step i + D;
     //   waits for the LDS reads of step i + 1.
+    // WS adds the kXW window loads before the group of every item-relative
+    // step 4m >= 4 (issued in iterations with d = 0): the wait in iteration
+    // d = 1 or 2 has one such group among the two later ones.
     constexpr int kOpsPerStep = RF * (kAL + kSA) + kSB + kTileLoads;
-    static_assert((D - 1) * kOpsPerStep < 64, "vmcnt range");
+    static_assert((D - 1) * kOpsPerStep < 64 && (D - 2) * kOpsPerStep + kXW < 64, "vmcnt range");
     static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
     const int n_steps = (ks1 - ks0) * kVS;        // virtual steps
     auto step_of = [&](int i) { return ks0 * kVS + (i < n_steps ? i : n_steps - 1); };
 
+    if constexpr (WS) wload(step_of(0), 0);   // older than every step's loads
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(step_of(d), d, d & 1);
+    for (int d = 0; d < D; ++d) issue(step_of(d), d, d & 1, false);
     wait_vmcnt<(D - 1) * kOpsPerStep>();
     if (COOP) __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -1009,15 +1053,27 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int i = i0 + d;
-            wait_vmcnt<(D - 2) * kOpsPerStep>();
+            if (WS && (d == 1 || d == 2))
+                wait_vmcnt<(D - 2) * kOpsPerStep + kXW>();
+            else
+                wait_vmcnt<(D - 2) * kOpsPerStep>();
             if (COOP) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             read_b((d + 1) % D, bt[(d + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            mma(d, bt[d & 1], i < n_steps, step_of(i), d & 1);
+            mma(d, bt[d & 1], i < n_steps, step_of(i), d & 1, d);
             __builtin_amdgcn_sched_barrier(0);
-            issue(step_of(i + D), d, d & 1);
+            issue(step_of(i + D), d, d & 1, d == 0);
             lds_wait(bt[(d + 1) & 1]);
+            if constexpr (WS) {
+                if (d == 3) {   // the next window becomes current
+#pragma unroll
+                    for (int f = 0; f < RF; ++f) wsa[0][f] = wsa[1][f];
+                    wsb[0][0] = wsb[1][0];
+                    wsb[0][1] = wsb[1][1];
+                    wdl[0] = wdl[1];
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -1104,6 +1160,10 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         *p.det_total = wl.routed_tokens;
 
     const bool store_rows = OP == 0 && p.wbuf != nullptr;
+    // FP8 [N, K]: windowed scale loads in the 4-slot-ring items (whole 16-byte
+    // windows need rows of at least 16 scale bytes, K >= 512)
+    constexpr bool kWS = TRANS && FMT != 4 && FMT != 8;
+    const bool ws_ok = kWS && p.K >= 4 * kStepKNK;
     // K elements per step: 64 ([K,N]), 128 ([N,K] FP8), 256 ([N,K] FP4): one
     // step always moves 8 KB of the weight tile
     const int k_steps = p.K / (!TRANS ? kStepK : FMT == 4 ? 2 * kStepKNK : kStepKNK);
@@ -1171,9 +1231,17 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            if (kWide && gr > kCoopRows)
+            if (kWide && gr > kCoopRows) {
+                if constexpr (kWS) {
+                    if (ws_ok) {
+                        routed_item<FMT, !TRANS, true, 2, OP, true>(
+                            p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
+                        continue;
+                    }
+                }
                 routed_item<FMT, !TRANS, true, (kWide ? 2 : 1), OP>(
                     p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
+            }
             else
                 routed_item<FMT, !TRANS, true, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
                                                       store_rows, s_ring, w);
@@ -1196,6 +1264,13 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
+            if constexpr (kWS) {
+                if (ws_ok) {
+                    routed_item<FMT, !TRANS, false, 1, OP, true>(p, e, m0, mcount, nt * kOutN,
+                                                                 ks0, ks1, store_rows, own, w);
+                    continue;
+                }
+            }
             routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
                                                    store_rows, own, w);
         }

@@ -803,20 +803,22 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // [N,K] weight column moves the same 128 bytes)
     constexpr int kStepA = KN ? (FP4 ? kStepK / 2 : kStepK) : kStepKNK;
     constexpr int kAL = KN ? (FP4 ? 1 : 2) : 4;      // x1 loads per step
-    // WS (FP8 [N, K], 4-slot ring, K >= 512): the x1 and weight scales are
-    // loaded once per window of four steps, one 16-byte load per x1 row and
-    // per weight column (the four steps' dwords) instead of a 4-byte gather
-    // per step: each load instruction touches 32 rows, so this is 4x fewer
-    // scattered cache-line accesses.  The window load goes first in the load
+    // WS ([N, K], 4-slot ring; K >= 512 for FP8, >= 1024 for FP4): the x1
+    // and weight scales are loaded once per window of four steps, 16 bytes
+    // per x1 row and per weight column (FP8: the four steps' dwords; FP4: two
+    // loads, the four steps' qwords) instead of a gather per step: each load
+    // instruction touches 32 rows, so this is 4x fewer scattered cache-line
+    // accesses.  The window load goes first in the load
     // group of the window's first step (item-relative steps 4m, a multiple of
     // the ring depth), into the "next" register set, which becomes "current"
     // after the window's last step; a window that would run past the row's
     // end starts earlier (still 16 bytes inside the row) and the steps' dword
     // index is shifted by the difference.
-    static_assert(!WS || (!KN && !FP4 && !I8 && D == 4), "windowed scales: FP8 [N,K], 4 slots");
+    static_assert(!WS || (!KN && !I8 && D == 4), "windowed scales: [N,K], 4 slots");
+    constexpr int kWL = FP4 ? 2 : 1;                 // 16-byte loads per row per window
     constexpr int kSA = I8 || WS ? 0 : 1;            // x1-scale loads per step and fragment
     constexpr int kSB = I8 || WS ? 0 : KN4 ? 8 : KN ? 4 : 2;   // weight-scale loads per step
-    constexpr int kXW = WS ? RF + 2 : 0;             // loads per window
+    constexpr int kXW = WS ? kWL * (RF + 2) : 0;     // loads per window
     constexpr int kSW = FP4 && !KN ? 2 : 1;          // dwords per scale load
     // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4 (FP8) or 8 (FP4)
     constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
@@ -826,18 +828,31 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // the unrolled ring index's parity so that it is a compile-time constant
     // (ks0 * 2 and D are even; for the clamped re-reads past the last step it
     // may differ, and those are never consumed)
-    v4i wsa[2][RF], wsb[2][2];   // WS: scale windows, [0] current, [1] next
-    int wdl[2] = {0, 0};         // WS: dword shift of a window moved back from the row end
-    const int k_row = K / kStepKNK;   // 128-K steps of a whole row (its scale bytes / 4)
+    v4i wsa[2][RF][kWL], wsb[2][2][kWL];   // WS: scale windows, [0] current, [1] next
+    int wdl[2] = {0, 0};   // WS: step shift of a window moved back from the row end
+    // steps of a whole row; each takes kBlk scale bytes of it
+    const int k_row = K / (FP4 ? 2 * kStepKNK : kStepKNK);
     auto wload = [&](int vs, int set) {   // the window starting at step vs
         const int start = vs < k_row - 4 ? vs : k_row - 4;
         wdl[set] = vs - start;
 #pragma unroll
-        for (int f = 0; f < RF; ++f)
-            wsa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + 4 * start, 0, 0);
+        for (int q = 0; q < kWL; ++q) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            wsb[set][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+            for (int f = 0; f < RF; ++f)
+                wsa[set][f][q] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + kBlk * start + 16 * q, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                wsb[set][j][q] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + kBlk * start + 16 * q, 0, 0);
+        }
+    };
+    // dword k (uniform) of a window: FP8 one per step, FP4 two per step
+    auto wpick = [&](const v4i (&w)[kWL], int k) {
+        if constexpr (kWL == 2)
+            return k < 4 ? pick(w[0], k) : pick(w[1], k - 4);
+        else
+            return pick(w[0], k);
     };
 
     auto issue = [&](int vs, int slot, int hf, bool wstart) {
@@ -981,6 +996,17 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                     }
                 }
             } else if constexpr (FP4) {
+                uint32_t sa2[2] = {r.sa[f][0], r.sa[f][1]};
+                uint32_t sb2[2][2] = {{r.sb[0][0], r.sb[0][1]}, {r.sb[1][0], r.sb[1][1]}};
+                if constexpr (WS) {
+                    const int k = 2 * (wpos + wdl[0]);   // the step's qword in the window
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        sa2[h] = wpick(wsa[0][f], k + h);
+                        sb2[0][h] = wpick(wsb[0][0], k + h);
+                        sb2[1][h] = wpick(wsb[0][1], k + h);
+                    }
+                }
                 // four 64-K sub-steps s, two 32-column groups j; operand =
                 // 16 bytes (chunk 2s + g of the lane's row / column); scale of
                 // 32-block 8 ks + 2 s + g = byte 2 s + g of the step's 8; odd
@@ -995,16 +1021,16 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                     for (int j = 0; j < 2; ++j)
                         acc[f][j + 2 * (s4 & 1)] =
                             mfma<FMT, 0>(a, cat(b[2 * s4 + j], z), acc[f][j + 2 * (s4 & 1)],
-                                         r.sa[f][s4 >> 1] >> shf, r.sb[j][s4 >> 1] >> shf);
+                                         sa2[s4 >> 1] >> shf, sb2[j][s4 >> 1] >> shf);
                 }
             } else {
                 // two 64-K halves s, two 32-column groups j; the scale of
                 // 32-block 4 ks + 2 s + g is byte 2 s + g of each scale dword
                 uint32_t sa = r.sa[f][0], sb[2] = {r.sb[0][0], r.sb[1][0]};
                 if constexpr (WS) {
-                    sa = pick(wsa[0][f], wpos + wdl[0]);
-                    sb[0] = pick(wsb[0][0], wpos + wdl[0]);
-                    sb[1] = pick(wsb[0][1], wpos + wdl[0]);
+                    sa = wpick(wsa[0][f], wpos + wdl[0]);
+                    sb[0] = wpick(wsb[0][0], wpos + wdl[0]);
+                    sb[1] = wpick(wsb[0][1], wpos + wdl[0]);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
@@ -1068,9 +1094,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             if constexpr (WS) {
                 if (d == 3) {   // the next window becomes current
 #pragma unroll
-                    for (int f = 0; f < RF; ++f) wsa[0][f] = wsa[1][f];
-                    wsb[0][0] = wsb[1][0];
-                    wsb[0][1] = wsb[1][1];
+                    for (int q = 0; q < kWL; ++q) {
+#pragma unroll
+                        for (int f = 0; f < RF; ++f) wsa[0][f][q] = wsa[1][f][q];
+                        wsb[0][0][q] = wsb[1][0][q];
+                        wsb[0][1][q] = wsb[1][1][q];
+                    }
                     wdl[0] = wdl[1];
                 }
             }
@@ -1160,10 +1189,10 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         *p.det_total = wl.routed_tokens;
 
     const bool store_rows = OP == 0 && p.wbuf != nullptr;
-    // FP8 [N, K]: windowed scale loads in the 4-slot-ring items (whole 16-byte
-    // windows need rows of at least 16 scale bytes, K >= 512)
-    constexpr bool kWS = TRANS && FMT != 4 && FMT != 8;
-    const bool ws_ok = kWS && p.K >= 4 * kStepKNK;
+    // [N, K]: windowed scale loads in the 4-slot-ring items (a window is four
+    // steps of a row's scale bytes: K >= 512 for FP8, >= 1024 for FP4)
+    constexpr bool kWS = TRANS && FMT != 8;
+    const bool ws_ok = kWS && p.K >= 4 * (FMT == 4 ? 2 * kStepKNK : kStepKNK);
     // K elements per step: 64 ([K,N]), 128 ([N,K] FP8), 256 ([N,K] FP4): one
     // step always moves 8 KB of the weight tile
     const int k_steps = p.K / (!TRANS ? kStepK : FMT == 4 ? 2 * kStepKNK : kStepKNK);

@@ -172,6 +172,8 @@ C5_PE = _reg(replace(C5, name="c5_pe", scale_per_expert=True, seed=1035))
 SMALL_T_FP4 = _reg(replace(SMALL_T, name="small_t_fp4", fp8="e2m1", K=768, seed=1041))
 SMALL_BIG_T_FP4 = _reg(replace(SMALL_BIG_T, name="small_big_t_fp4", fp8="e2m1", K=768,
                                seed=1042))
+SMALL_T_FP4_K1280 = _reg(replace(SMALL_T, name="small_t_fp4_k1280", fp8="e2m1", K=1280,
+                                 seed=1051))
 C2_FP4 = _reg(replace(C2, name="c2_fp4", fp8="e2m1", seed=1043))
 C3_FP4T = _reg(replace(C3, name="c3_fp4t", fp8="e2m1", transpose_x2=True, seed=1044))
 C5_FP4 = _reg(replace(C5, name="c5_fp4", fp8="e2m1", seed=1045))
@@ -197,7 +199,7 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_T_K768,
-              SMALL_BIG_T_K768, SMALL_N_PE,
+              SMALL_BIG_T_K768, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,

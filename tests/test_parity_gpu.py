@@ -93,7 +93,8 @@ def slack_for(inp, rows=None):
                                   "small_big_t_fp4_exact", "small_n_fp4", "small_big_n_fp4",
                                   "small_n_fp4_exact", "small_big_n_fp4_exact",
                                   "small_t_k768", "small_big_t_k768", "small_t_k768_exact",
-                                  "small_big_t_k768_exact"])
+                                  "small_big_t_k768_exact", "small_t_fp4_k1280",
+                                  "small_t_fp4_k1280_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]

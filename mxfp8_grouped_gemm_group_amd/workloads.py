@@ -158,6 +158,10 @@ SMALL_BIG_T = _reg(Workload("small_big_t", batch=86, M=516, K=640, N=352, E=4, f
 # The small [N, K] cases again with K = 768 (six 128-K steps instead of five)
 SMALL_T_K768 = _reg(replace(SMALL_T, name="small_t_k768", K=768, seed=1025))
 SMALL_BIG_T_K768 = _reg(replace(SMALL_BIG_T, name="small_big_t_k768", K=768, seed=1026))
+# ... K = 512 (exactly one four-step scale window per row) and K = 384 (rows too
+# short for a window: per-step scale loads)
+SMALL_T_K512 = _reg(replace(SMALL_T, name="small_t_k512", K=512, seed=1027))
+SMALL_T_K384 = _reg(replace(SMALL_T, name="small_t_k384", K=384, seed=1028))
 
 # Per-expert weight scales (a leading expert axis on scale; CANN V3 Atlas 350
 # scale notes).
@@ -199,7 +203,7 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_T_K768,
-              SMALL_BIG_T_K768, SMALL_T_FP4_K1280, SMALL_N_PE,
+              SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,

@@ -94,7 +94,8 @@ def slack_for(inp, rows=None):
                                   "small_n_fp4_exact", "small_big_n_fp4_exact",
                                   "small_t_k768", "small_big_t_k768", "small_t_k768_exact",
                                   "small_big_t_k768_exact", "small_t_fp4_k1280",
-                                  "small_t_fp4_k1280_exact"])
+                                  "small_t_fp4_k1280_exact", "small_t_k512", "small_t_k384",
+                                  "small_t_k512_exact", "small_t_k384_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]

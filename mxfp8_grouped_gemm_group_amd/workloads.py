@@ -155,6 +155,18 @@ SMALL_BIG_T = _reg(Workload("small_big_t", batch=86, M=516, K=640, N=352, E=4, f
                             transpose_x2=True, groups=(141, 5, 300, 70), group_list_type=0,
                             exp_range=(-4, 4), row_index="perm", seed=1024))
 
+# An expert with more than four 256-row groups (1300 rows: six groups, the last
+# with 20 rows), so the cooperative units' order has a short last band of row
+# groups, beside an empty expert and a 128-row group (77 rows).
+SMALL_HUGE_N = _reg(Workload("small_huge_n", batch=200, M=1377, K=256, N=320, E=3,
+                             fp8="e4m3fn", groups=(1300, 0, 77), group_list_type=1,
+                             exp_range=(-4, 4), row_index="perm", shared_rows=40,
+                             shared_weight=0.75, shared_offset=100, seed=1029))
+SMALL_HUGE_T = _reg(Workload("small_huge_t", batch=200, M=1377, K=512, N=352, E=3,
+                             fp8="e5m2", transpose_x2=True, groups=(77, 1300, 0),
+                             group_list_type=0, exp_range=(-4, 4), row_index="perm",
+                             out_init="normal", seed=1030))
+
 # The small [N, K] cases again with K = 768 (six 128-K steps instead of five)
 SMALL_T_K768 = _reg(replace(SMALL_T, name="small_t_k768", K=768, seed=1025))
 SMALL_BIG_T_K768 = _reg(replace(SMALL_BIG_T, name="small_big_t_k768", K=768, seed=1026))
@@ -202,7 +214,8 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
-for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_T_K768,
+for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_HUGE_N,
+              SMALL_HUGE_T, SMALL_T_K768,
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):

@@ -95,7 +95,9 @@ def slack_for(inp, rows=None):
                                   "small_t_k768", "small_big_t_k768", "small_t_k768_exact",
                                   "small_big_t_k768_exact", "small_t_fp4_k1280",
                                   "small_t_fp4_k1280_exact", "small_t_k512", "small_t_k384",
-                                  "small_t_k512_exact", "small_t_k384_exact"])
+                                  "small_t_k512_exact", "small_t_k384_exact",
+                                  "small_huge_n", "small_huge_t", "small_huge_n_exact",
+                                  "small_huge_t_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]
@@ -126,7 +128,7 @@ def test_full_shapes_sampled(name):
 
 @pytest.mark.parametrize("name", ["c5", "c5_exact", "small_n", "small_t", "small_big_n",
                                   "small_big_t_exact", "small_t_fp4", "small_big_n_fp4",
-                                  "small_big_t_k768"])
+                                  "small_big_t_k768", "small_huge_t", "small_huge_n_exact"])
 def test_deterministic_mode(name):
     """Deterministic mode: bitwise repeatable, within tolerance of the oracle
     (bit-exact on integer data)."""

@@ -1186,11 +1186,11 @@ __device__ __forceinline__ void shared_slice(const FusedParams &p, int64_t wave,
 
 // One block per CU (the weight rings fill most of the 160 KB of LDS).
 //
-// Work is dealt in block units.  First come the cooperative units of the
-// large experts (expert, 128-row group, 128-column tile, K split); then the
-// wave items of the small experts (expert, 32-row tile, 128-column tile, K
-// split), four consecutive ones per unit, one per wave.  Blocks take units
-// round-robin.
+// Work is dealt in block units: the cooperative units of the large experts
+// (expert, 128- or 256-row group, column tile, K split) and the wave items of
+// the small experts (expert, 32-row tile, column tile, K split), four
+// consecutive ones per unit, one per wave.  Each kind is dealt to the blocks
+// round-robin, and every block alternates between its units of the two kinds.
 //
 // OP 0 is the finalize-routing operator; OP 1 the upstream step, whose items
 // cover a 128- ([K,N]) or 32-column ([N,K]) block of the I outputs (twice that
@@ -1262,15 +1262,23 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     const int64_t wave_units = units - coop_units;
     const int64_t waves = static_cast<int64_t>(blocks) * kWavesPerBlock;
 
-    for (int64_t uu = 0;; ++uu) {
-        int64_t u = xcd_block + uu * blocks;        // cooperative phase
-        if (u >= coop_units) {
-            // wave phase: this block's k-th wave unit is blockIdx.x + k * blocks
-            const int64_t first_wave = uu - (coop_units - xcd_block + blocks - 1) / blocks;
-            const int64_t v = blockIdx.x + first_wave * blocks;
-            if (v >= wave_units) break;
-            u = coop_units + v;
-        }
+    // This block's cooperative units are xcd_block + k * blocks, its wave
+    // units blockIdx.x + k * blocks.  It alternates between the two kinds
+    // (even blocks start with a cooperative unit, odd ones with a wave unit)
+    // until one kind runs out: cooperative units hardly use HBM (their
+    // weights are shared through L2) and wave units stream it, so mixing
+    // them keeps HBM busy while the cooperative work proceeds (c5 2412 ->
+    // 2369 µs, c5_fp4 1732 -> 1619, c4 516 -> 506 against all cooperative
+    // units first).
+    const int64_t n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;
+    const int64_t n_wave =
+        wave_units > blockIdx.x ? (wave_units - blockIdx.x + blocks - 1) / blocks : 0;
+    int64_t i_coop = 0, i_wave = 0;
+    for (int64_t uu = 0; uu < n_coop + n_wave; ++uu) {
+        const bool take_coop = i_wave >= n_wave ||
+                               (i_coop < n_coop && ((uu + blockIdx.x) & 1) == 0);
+        const int64_t u = take_coop ? xcd_block + (i_coop++) * blocks
+                                    : coop_units + blockIdx.x + (i_wave++) * blocks;
         __syncthreads();   // the previous unit's waves are done with the LDS
         if (u < coop_units) {
             const int q = static_cast<int>(u / S);

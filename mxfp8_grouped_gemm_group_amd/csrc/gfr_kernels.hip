@@ -92,10 +92,12 @@ struct WorkList {
     int *start;   // [E]   first token of expert e
     int *cnt;     // [E]   tokens of expert e
     int *spref;   // [E+1] prefix of per-expert wave items (one K split)
-    int *lpref;   // [E+1] prefix of per-expert cooperative block items
+    int *lpref;   // [n_ce+1] prefix of cooperative block items, experts in `perm` order
+    int *perm;    // [n_ce]  cooperative experts, most rows per cooperative group first
     int routed_tokens;  // sum of counts
     int sitems;         // spref[E]
-    int litems;         // lpref[E]
+    int litems;         // lpref[n_ce]
+    int n_ce;           // experts with cooperative units
 };
 
 // Experts with at least this many tokens are processed by cooperative block
@@ -162,11 +164,13 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
     // (each total stays below 2^31: the host bounds (M/32 + E) * ceil(N/128)).
     int64_t isum = 0;
     int64_t items[kPerThread];
+    int ccnt[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
         int cnt = c[i];
         if (run + cnt > p.M) { bad = true; cnt = run < p.M ? static_cast<int>(p.M - run) : 0; }
+        ccnt[i] = cnt;
         if (e < p.E) {
             wl.start[e] = static_cast<int>(run < p.M ? run : p.M);
             wl.cnt[e] = cnt;
@@ -196,7 +200,69 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
     wl.routed_tokens = static_cast<int>(total_tokens < p.M ? total_tokens : p.M);
     wl.sitems = static_cast<int>(total_items & 0xffffffff);
     wl.litems = static_cast<int>(total_items >> 32);
+    wl.n_ce = 0;
     if (bad && blockIdx.x == 0) flag(p.status, GFR_DEV_BAD_GROUP_LIST);
+    __syncthreads();
+    if (wl.litems == 0) return;
+    if (!WIDE) {
+        // one-fragment units: cooperative experts in index order (their cost
+        // does not follow the rows per group the same way; measured)
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int e = tid * kPerThread + i;
+            if (e < p.E) wl.perm[e] = e;
+        }
+        wl.n_ce = p.E;
+        __syncthreads();
+        return;
+    }
+
+    // Cooperative experts in the order their units are dealt: more rows per
+    // cooperative group first (a unit's time grows with its live rows: their
+    // x1 loads), ties by expert index.  Each cooperative expert's rank is the
+    // number of cooperative experts ordered before it; lpref is rebuilt as
+    // the prefix of cooperative units over that order.
+    int16_t *s_key = reinterpret_cast<int16_t *>(s_scan);   // 2 KB, free after the scans
+    static_assert(kMaxExperts * sizeof(int16_t) <= kBlockThreads * sizeof(int64_t), "keys fit");
+    int key[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int e = tid * kPerThread + i;
+        const bool coop = e < p.E && (items[i] >> 32) > 0;
+        key[i] = coop ? min(ccnt[i], coop_group_rows<WIDE>(ccnt[i])) : 0;
+        s_key[e] = static_cast<int16_t>(key[i]);
+    }
+    __syncthreads();
+    int rank[kPerThread] = {};
+    int n_ce = 0;
+    for (int e2 = 0; e2 < p.E; ++e2) {
+        const int k2 = s_key[e2];
+        n_ce += k2 > 0;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+            rank[i] += (k2 > key[i]) || (k2 == key[i] && e2 < tid * kPerThread + i);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+        if (key[i] > 0) wl.perm[rank[i]] = tid * kPerThread + i;
+    __syncthreads();
+    int64_t lv[kPerThread];
+    int64_t lsum = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int r = tid * kPerThread + i;
+        lv[i] = r < n_ce ? wl.lpref[wl.perm[r] + 1] - wl.lpref[wl.perm[r]] : 0;
+        lsum += lv[i];
+    }
+    int64_t ltotal = 0;
+    int64_t lpre = block_exclusive_scan<int64_t>(lsum, s_scan, ltotal);   // ends synchronised
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int r = tid * kPerThread + i;
+        if (r <= n_ce) wl.lpref[r] = static_cast<int>(lpre);
+        lpre += lv[i];
+    }
+    wl.n_ce = n_ce;
     __syncthreads();
 }
 
@@ -1202,6 +1268,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_spref[kMaxExperts + 1];
     __shared__ int s_lpref[kMaxExperts + 1];
+    __shared__ int s_perm[kMaxExperts];
     __shared__ int64_t s_scan[kBlockThreads];
     __shared__ __attribute__((aligned(16))) char s_ring[kWavesPerBlock * kRingBytes];
 
@@ -1212,7 +1279,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // ([K,N]: gate and up tiles streamed in turn)
     constexpr int kOutN = OP == 0 || !TRANS ? kTN : kTN / 2;
     const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
-    WorkList wl{s_start, s_cnt, s_spref, s_lpref, 0, 0, 0};
+    WorkList wl{s_start, s_cnt, s_spref, s_lpref, s_perm, 0, 0, 0, 0};
     // two-fragment cooperative groups except where a fragment has 8 accumulators
     constexpr bool kWide = FMT != 4 && FMT != 8 && !(OP == 1 && !TRANS);
     build_work_list<kWide>(p, n_tiles, wl, s_scan);
@@ -1259,33 +1326,61 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     const int64_t xcd_block =
         (blocks % 8 == 0) ? static_cast<int64_t>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
                           : blockIdx.x;
-    const int64_t wave_units = units - coop_units;
     const int64_t waves = static_cast<int64_t>(blocks) * kWavesPerBlock;
 
-    // This block's cooperative units are xcd_block + k * blocks, its wave
-    // units blockIdx.x + k * blocks.  It alternates between the two kinds
-    // (even blocks start with a cooperative unit, odd ones with a wave unit)
-    // until one kind runs out: cooperative units hardly use HBM (their
-    // weights are shared through L2) and wave units stream it, so mixing
-    // them keeps HBM busy while the cooperative work proceeds (c5 2412 ->
-    // 2369 µs, c5_fp4 1732 -> 1619, c4 516 -> 506 against all cooperative
-    // units first).
-    const int64_t n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;
-    const int64_t n_wave =
-        wave_units > blockIdx.x ? (wave_units - blockIdx.x + blocks - 1) / blocks : 0;
+    // The deal.  With two-fragment cooperative units present, units g = 0,
+    // 1, ... (the cooperative units in the order of the work list, experts
+    // with the most rows per group first, then the wave units) go to ranks in
+    // snake order -- round k = g / blocks runs over the ranks forward when k
+    // is even and backward when it is odd -- so that every rank gets costly
+    // and cheap units alike (a cooperative unit's time grows with its live
+    // rows: c4 523 -> 501 µs, c5 2355 -> 2278).  Ranks are XCD-grouped
+    // (consecutive ranks on one XCD, so consecutive cooperative units share
+    // an L2).  Otherwise (one-fragment cooperative units, where the snake
+    // measured slower, or none) the cooperative units go round-robin over the
+    // XCD-grouped ranks and the wave units round-robin in plain block order
+    // (measured fastest for pure streaming).
+    // A block alternates between its cooperative and its wave units (even
+    // blocks start with a cooperative unit, odd ones with a wave unit):
+    // cooperative units hardly use HBM (their weights are shared through L2)
+    // and wave units stream it, so mixing them keeps HBM busy while the
+    // cooperative work proceeds (c5 2412 -> 2369 µs, c5_fp4 1732 -> 1619,
+    // c4 516 -> 506 against all cooperative units first).
+    const bool snake = kWide && coop_units > 0;
+    auto g_of = [&](int64_t k) {
+        return k * blocks + ((k & 1) ? blocks - 1 - xcd_block : xcd_block);
+    };
+    int64_t n_coop = 0, n_wave = 0;
+    if (snake) {
+        // this rank's rounds: the cooperative ones, then the wave ones (g
+        // grows with k)
+        for (int64_t k = 0; k * blocks < units; ++k) {
+            const int64_t g = g_of(k);
+            n_coop += g < coop_units;
+            n_wave += g >= coop_units && g < units;
+        }
+    } else {
+        const int64_t wave_units = units - coop_units;
+        n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;
+        n_wave = wave_units > blockIdx.x ? (wave_units - blockIdx.x + blocks - 1) / blocks : 0;
+    }
+    auto coop_unit = [&](int64_t i) { return snake ? g_of(i) : xcd_block + i * blocks; };
+    auto wave_unit = [&](int64_t j) {
+        return snake ? g_of(n_coop + j) : coop_units + blockIdx.x + j * blocks;
+    };
     int64_t i_coop = 0, i_wave = 0;
     for (int64_t uu = 0; uu < n_coop + n_wave; ++uu) {
         const bool take_coop = i_wave >= n_wave ||
                                (i_coop < n_coop && ((uu + blockIdx.x) & 1) == 0);
-        const int64_t u = take_coop ? xcd_block + (i_coop++) * blocks
-                                    : coop_units + blockIdx.x + (i_wave++) * blocks;
+        const int64_t u = take_coop ? coop_unit(i_coop++) : wave_unit(i_wave++);
         __syncthreads();   // the previous unit's waves are done with the LDS
         if (u < coop_units) {
             const int q = static_cast<int>(u / S);
-            const int e = __builtin_amdgcn_readfirstlane(find_expert(s_lpref, p.E, q));
+            const int rk = __builtin_amdgcn_readfirstlane(find_expert(s_lpref, wl.n_ce, q));
+            const int e = __builtin_amdgcn_readfirstlane(s_perm[rk]);
             const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
-            const int e_pref = __builtin_amdgcn_readfirstlane(s_lpref[e]);
+            const int e_pref = __builtin_amdgcn_readfirstlane(s_lpref[rk]);
             const int gr = coop_group_rows<kWide>(e_cnt);
             const int mg_count = (e_cnt + gr - 1) / gr;
             // Units of one expert, K split s outermost, then bands of

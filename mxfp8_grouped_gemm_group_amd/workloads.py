@@ -167,6 +167,19 @@ SMALL_HUGE_T = _reg(Workload("small_huge_t", batch=200, M=1377, K=512, N=352, E=
                              group_list_type=0, exp_range=(-4, 4), row_index="perm",
                              out_init="normal", seed=1030))
 
+# Many cooperative experts, several with the same rows per group (ties in the
+# cost order), beside small and empty experts: more cooperative units than
+# workgroups, so the snake deal runs over several rounds.
+_MANY = (130, 256, 200, 130, 64, 90, 300, 256, 129, 0, 180, 64, 128, 257, 200, 40,
+         130, 75, 5, 256, 0, 200, 99, 64, 31, 512, 130, 1, 140, 256)
+SMALL_MANY_N = _reg(Workload("small_many_n", batch=600, M=sum(_MANY), K=256, N=512,
+                             E=len(_MANY), fp8="e4m3fn", groups=_MANY, group_list_type=1,
+                             exp_range=(-4, 4), row_index="perm", seed=1036))
+SMALL_MANY_T = _reg(Workload("small_many_t", batch=600, M=sum(_MANY), K=512, N=320,
+                             E=len(_MANY), fp8="e5m2", transpose_x2=True, groups=_MANY,
+                             group_list_type=0, exp_range=(-4, 4), row_index="perm",
+                             out_init="normal", seed=1037))
+
 # The small [N, K] cases again with K = 768 (six 128-K steps instead of five)
 SMALL_T_K768 = _reg(replace(SMALL_T, name="small_t_k768", K=768, seed=1025))
 SMALL_BIG_T_K768 = _reg(replace(SMALL_BIG_T, name="small_big_t_k768", K=768, seed=1026))
@@ -215,7 +228,7 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_HUGE_N,
-              SMALL_HUGE_T, SMALL_T_K768,
+              SMALL_HUGE_T, SMALL_MANY_N, SMALL_MANY_T, SMALL_T_K768,
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):

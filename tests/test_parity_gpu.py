@@ -65,6 +65,8 @@ def assert_parity(got, ref, mag, exact=False, what="", slack=None):
     if ok:
         return
     assert slack is not None, f"{what}: worst ratio {worst}"
+    if callable(slack):   # computed only when the plain tolerance is exceeded
+        slack = slack()
     err = np.abs(got - ref)
     bound = REL * mag + ABS + slack
     worst2 = float(np.max(err / bound))
@@ -97,7 +99,8 @@ def slack_for(inp, rows=None):
                                   "small_t_fp4_k1280_exact", "small_t_k512", "small_t_k384",
                                   "small_t_k512_exact", "small_t_k384_exact",
                                   "small_huge_n", "small_huge_t", "small_huge_n_exact",
-                                  "small_huge_t_exact"])
+                                  "small_huge_t_exact", "small_many_n", "small_many_t",
+                                  "small_many_n_exact", "small_many_t_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]
@@ -105,7 +108,7 @@ def test_small_full(name, split_k):
     inp = make_inputs(w, DEV)
     got = run_gpu(inp, split_k=split_k)
     ref, mag = run_oracle(inp)
-    assert_parity(got, ref, mag, exact=w.exact, what=name, slack=slack_for(inp))
+    assert_parity(got, ref, mag, exact=w.exact, what=name, slack=lambda: slack_for(inp))
 
 
 # ---------------------------------------------------------------------------
@@ -143,7 +146,7 @@ def test_deterministic_mode(name):
     got = a if rows is None else a[torch.as_tensor(rows, device=DEV)]
     stress = name.startswith("small")
     assert_parity(got, ref, mag, exact=w.exact, what=name + " det",
-                  slack=slack_for(inp, rows) if stress else None)
+                  slack=(lambda: slack_for(inp, rows)) if stress else None)
 
 
 # ---------------------------------------------------------------------------
@@ -166,7 +169,7 @@ def test_logit_and_shared_absent():
     inp["shared_input"] = None
     got = run_gpu(inp)
     ref, mag = run_oracle(inp)
-    assert_parity(got, ref, mag, what="no logit / no shared", slack=slack_for(inp))
+    assert_parity(got, ref, mag, what="no logit / no shared", slack=lambda: slack_for(inp))
 
 
 def test_empty_groups_and_no_tokens():
@@ -211,7 +214,7 @@ def test_device_status_bits():
     lg[40] = 0
     ref, mag = run_oracle(dict(inp, logit=lg))
     assert_parity(got, ref, mag, what="bad row_index skipped",
-                  slack=slack_for(dict(inp, logit=lg)))
+                  slack=lambda: slack_for(dict(inp, logit=lg)))
 
     status.zero_()
     g = inp["group_list"].clone()

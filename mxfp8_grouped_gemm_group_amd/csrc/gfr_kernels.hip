@@ -65,22 +65,30 @@ __device__ __forceinline__ void flag(int32_t *status, int32_t bit) {
     if (status) atomicOr(status, bit);
 }
 
-// Exclusive block-wide prefix sum (Hillis-Steele in LDS).
+// Exclusive block-wide prefix sum: a shuffle scan within each wave, then the
+// wave totals through LDS (two barriers in all).
 template <class T>
 __device__ T block_exclusive_scan(T v, T *s_scan, T &total) {
     const int tid = threadIdx.x;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kBlockThreads; off <<= 1) {
-        const T add = tid >= off ? s_scan[tid - off] : T(0);
-        __syncthreads();
-        s_scan[tid] += add;
-        __syncthreads();
+    const int lane = tid & (kWaveSize - 1), wv = tid / kWaveSize;
+    T x = v;
+#pragma unroll
+    for (int off = 1; off < kWaveSize; off <<= 1) {
+        const T y = __shfl_up(x, off, kWaveSize);
+        if (lane >= off) x += y;
     }
-    const T incl = s_scan[tid];
-    total = s_scan[kBlockThreads - 1];
+    if (lane == kWaveSize - 1) s_scan[wv] = x;
     __syncthreads();
-    return incl - v;
+    T before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        const T t = s_scan[i];
+        before += i < wv ? t : T(0);
+        all += t;
+    }
+    total = all;
+    __syncthreads();   // s_scan may be reused after return
+    return before + x - v;
 }
 
 // ---------------------------------------------------------------------------

@@ -802,7 +802,11 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // instruction), into a per-wave ring after the block's weight ring; the
     // 16-byte chunks of row r are XOR-swizzled by (r >> 1) & 3 and the
     // operands come out with ds_read_b128, one step ahead, like the weights.
-    constexpr bool kXL = KN && COOP && RF == 2 && !FP4 && !I8 && OP == 0;
+    // FP8 [N, K] two-fragment cooperative units stage the first 64 bytes of
+    // each row's 128-byte step the same way (the whole step would need 128 KB
+    // of x1 slots); the second 64 bytes stay register loads (kXLH).
+    constexpr bool kXLH = !KN && COOP && RF == 2 && !FP4 && !I8 && OP == 0;
+    constexpr bool kXL = (KN && COOP && RF == 2 && !FP4 && !I8 && OP == 0) || kXLH;
     constexpr int kXSlotBytes = 2 * kTileM * kStepK;      // 64 rows x 64 bytes
     char *const xring = ring + D * kSlotBytes + w * D * kXSlotBytes;
     static_assert(!kXL || D * kSlotBytes + kWavesPerBlock * D * kXSlotBytes <=
@@ -1028,11 +1032,19 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
         if constexpr (kXL) {
-            static_assert(!kXL || RF * kAL == 4, "four x1 loads per step, as in registers");
+            static_assert(!kXL || RF * kAL == (kXLH ? 8 : 4),
+                          "as many x1 loads per step as in registers");
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 lds_void_t *dst = (lds_void_t *)(xring + slot * kXSlotBytes + u * 1024);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vx[u], k0, 0, 0);
+            }
+            if constexpr (kXLH) {   // the step's second 64 bytes: registers
+#pragma unroll
+                for (int f = 0; f < RF; ++f)
+#pragma unroll
+                    for (int q = 2; q < 4; ++q)
+                        r.a[f][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[f], k0 + 32 * q, 0);
             }
         } else {
 #pragma unroll
@@ -1208,7 +1220,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const v8i a = on ? cat(r.a[f][2 * s2], r.a[f][2 * s2 + 1]) : v8i{};
+                    v8i a = on ? cat(r.a[f][2 * s2], r.a[f][2 * s2 + 1]) : v8i{};
+                    if constexpr (kXLH) {   // the first 64-K half came through LDS
+                        if (s2 == 0) a = on ? cat(ax[2 * f], ax[2 * f + 1]) : v8i{};
+                    }
                     const int shf = 8 * (2 * s2 + g);
 #pragma unroll
                     for (int j = 0; j < 2; ++j)

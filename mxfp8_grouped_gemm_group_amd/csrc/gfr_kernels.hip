@@ -424,6 +424,16 @@ __device__ __forceinline__ void lds_issue_x(uint32_t a0, uint32_t a1, v4i (&t)[4
         : "memory");
 }
 
+// ... one fragment: the reads at a0 and a1 only (t[2], t[3] untouched).
+__device__ __forceinline__ void lds_issue_x1(uint32_t a0, uint32_t a1, v4i (&t)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3"
+        : "=&v"(t[0]), "=&v"(t[1])
+        : "v"(a0), "v"(a1)
+        : "memory");
+}
+
 __device__ __forceinline__ void lds_wait(v4i (&t)[4]) {
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
@@ -802,12 +812,14 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // instruction), into a per-wave ring after the block's weight ring; the
     // 16-byte chunks of row r are XOR-swizzled by (r >> 1) & 3 and the
     // operands come out with ds_read_b128, one step ahead, like the weights.
-    // FP8 [N, K] two-fragment cooperative units stage the first 64 bytes of
-    // each row's 128-byte step the same way (the whole step would need 128 KB
-    // of x1 slots); the second 64 bytes stay register loads (kXLH).
-    constexpr bool kXLH = !KN && COOP && RF == 2 && !FP4 && !I8 && OP == 0;
-    constexpr bool kXL = (KN && COOP && RF == 2 && !FP4 && !I8 && OP == 0) || kXLH;
-    constexpr int kXSlotBytes = 2 * kTileM * kStepK;      // 64 rows x 64 bytes
+    // FP8 [N, K] cooperative units stage the first 64 bytes of each row's
+    // 128-byte step the same way (whole steps would need 128 KB of x1 slots);
+    // the second 64 bytes stay register loads (kXLH).  One-fragment units
+    // (32 rows per wave, 8-slot weight ring) do the same with 2 KB slots.
+    constexpr bool kXLH = !KN && COOP && !FP4 && !I8 && OP == 0;
+    constexpr bool kXL = (KN && COOP && !FP4 && !I8 && OP == 0) || kXLH;
+    constexpr int kXLoads = 2 * RF;                       // 16-row x1 loads per step
+    constexpr int kXSlotBytes = RF * kTileM * kStepK;     // 32 or 64 rows x 64 bytes
     char *const xring = ring + D * kSlotBytes + w * D * kXSlotBytes;
     static_assert(!kXL || D * kSlotBytes + kWavesPerBlock * D * kXSlotBytes <=
                               kWavesPerBlock * kRingBytes,
@@ -816,7 +828,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     uint32_t xa[2] = {0, 0};    // slot-relative operand addresses, K halves 0 and 1
     if constexpr (kXL) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kXLoads; ++u) {
             const int r = 16 * u + (lane >> 2);
             vx[u] = r * Kb + 16 * ((lane & 3) ^ ((r >> 1) & 3));
         }
@@ -1032,10 +1044,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
         if constexpr (kXL) {
-            static_assert(!kXL || RF * kAL == (kXLH ? 8 : 4),
+            static_assert(!kXL || RF * kAL == (kXLH ? 2 : 1) * kXLoads,
                           "as many x1 loads per step as in registers");
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kXLoads; ++u) {
                 lds_void_t *dst = (lds_void_t *)(xring + slot * kXSlotBytes + u * 1024);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vx[u], k0, 0, 0);
             }
@@ -1086,7 +1098,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     v4i at[2][4];   // kXL: x1 operands of a step (fragment f, K half q at 2 f + q)
     auto read_a = [&](int slot, v4i (&a)[4]) {
         const uint32_t base = lds_addr(xring + slot * kXSlotBytes);
-        lds_issue_x(base + xa[0], base + xa[1], a);
+        if constexpr (RF == 2)
+            lds_issue_x(base + xa[0], base + xa[1], a);
+        else
+            lds_issue_x1(base + xa[0], base + xa[1], a);
     };
     // [N,K] reads: 64-K half s, 16-byte half h of the lane's 32 operand bytes
     // = logical chunk 4s + 2h + g of column 32j + c (column c's slot row at

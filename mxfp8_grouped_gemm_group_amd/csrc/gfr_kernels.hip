@@ -127,10 +127,10 @@ __device__ __forceinline__ int coop_group_rows(int cnt) {
 
 constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 
-// Row groups per band in the order cooperative units are taken (c5-like
-// routing measured 1.7 % faster with 4 than with the whole expert as one
-// band; 2 and 8 in between).
-constexpr int kCoopBand = 4;
+// Row groups per band in the order cooperative units are taken.  With x1
+// through LDS, c5 measured 2177 µs with 2, 2182 with 1, 2198 with 4, 2228
+// with 8 and 2250 with 16 (c4 within 1 % for 2 to 16, 2 % slower with 1).
+constexpr int kCoopBand = 2;
 
 template <bool WIDE>
 __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,

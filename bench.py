@@ -10,8 +10,13 @@ value      = effective TFLOP/s = 2*M*K*N / (time per step)
 roofline   = the fused kernel against the HBM roofline (its algorithmic bytes
              per launch / its mean launch time, timed with events on the launch
              stream), the binding roof for every configuration here
+             (mean, median and minimum of the per-launch event times are
+             reported; frac_per_step is the same bytes over the whole-run
+             time per step, launch gaps included)
 cpu_baseline = the CPU oracle on a bounded sample of output rows of the same
-             workload (single-threaded C, double precision)
+             workload (plain C in double precision, output rows spread over
+             the host's OpenMP threads; cores = threads used, host_cores =
+             os.cpu_count())
 
 ``--workload g1_*`` measures the upstream step of the FFN instead
 (gfr_gemm1_swiglu_quant: gate||up grouped matmul, SwiGLU, MX quantisation;
@@ -102,7 +107,8 @@ def cpu_baseline(w, inp, budget_s):
     routed = ri[:total_tokens]
     rng = np.random.default_rng(12345)
     order = rng.permutation(w.batch)
-    n, spent, rows_done, tok_done = 1, 0.0, 0, 0
+    threads = oracle.num_threads()
+    n, spent, rows_done, tok_done = threads, 0.0, 0, 0
     while True:
         rows = order[rows_done:rows_done + n]
         if rows.size == 0:
@@ -114,18 +120,19 @@ def cpu_baseline(w, inp, budget_s):
         tok_done += int(np.isin(routed, rows).sum())
         if spent >= budget_s:
             break
-        n = max(1, int(rows_done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
+        n = max(threads, int(rows_done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
     flops = 2.0 * tok_done * w.K * w.N
     return {"value": flops / spent / 1e12, "unit": "TOP/s" if w.fp8 == "w4a8" else "TFLOP/s",
-            "cores": 1, "kind": "oracle",
+            "cores": threads, "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": f"{rows_done} of {w.batch} output rows ({tok_done} routed tokens, all "
-                      f"{w.N} columns) of workload {w.name}; {spent:.1f} s single-threaded"}
+                      f"{w.N} columns) of workload {w.name}; {spent:.1f} s on {threads} threads "
+                      "(one output row per thread at a time)"}
 
 
 def time_steps(step, args, dev):
     """Warm up, then time exactly args.steps calls: whole-run events plus one
     event pair per call, all on the launch stream.  Returns (ms_per_step,
-    mean_launch_ms)."""
+    per-launch times in ms)."""
     import torch
     for i in range(args.warmup):
         step(i)
@@ -144,14 +151,25 @@ def time_steps(step, args, dev):
     t_end.record(stream)
     torch.cuda.synchronize()
     per_launch_ms = [a.elapsed_time(b) for a, b in ev]
-    return t_start.elapsed_time(t_end) / args.steps, sum(per_launch_ms) / len(per_launch_ms)
+    return t_start.elapsed_time(t_end) / args.steps, per_launch_ms
+
+
+def launch_stats(per_launch_ms):
+    """Mean, median and minimum of the per-launch event times (ms)."""
+    v = sorted(per_launch_ms)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"mean_launch_ms": round(sum(v) / n, 5), "median_launch_ms": round(med, 5),
+            "min_launch_ms": round(v[0], 5)}
 
 
 def gemm1_cpu_baseline(w, inp, budget_s):
     """Time the upstream-step oracle on a growing seeded sample of tokens."""
     import numpy as np
     import torch
+    import oracle
     from oracle import gemm1 as og
+    threads = oracle.num_threads()
     u8 = lambda x: x.detach().contiguous().view(torch.uint8).cpu().numpy()
     h = [u8(inp["xin"]), u8(inp["w13"]), u8(inp["scale"]), u8(inp["xin_scale"]),
          inp["group_list"].cpu().numpy()]
@@ -159,7 +177,7 @@ def gemm1_cpu_baseline(w, inp, budget_s):
     okind = 0 if w.out_fp8 == "e4m3fn" else 1
     routed = np.flatnonzero(og.routed_tokens(h[4], w.group_list_type, w.M))
     order = np.random.default_rng(12345).permutation(routed)
-    n, spent, done = 1, 0.0, 0
+    n, spent, done = threads, 0.0, 0
     while done < order.size:
         rows = order[done:done + n]
         t0 = time.perf_counter()
@@ -168,11 +186,13 @@ def gemm1_cpu_baseline(w, inp, budget_s):
         done += rows.size
         if spent >= budget_s:
             break
-        n = max(1, int(done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
+        n = max(threads, int(done * (budget_s - spent) / max(spent, 1e-9) / 2)) if spent > 0.5 else n * 2
     flops = 2.0 * done * w.H * 2 * w.I
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": f"{done} of {routed.size} routed tokens (all {w.I} outputs) of workload "
-                      f"{w.name}; {spent:.1f} s single-threaded"}
+                      f"{w.name}; {spent:.1f} s on {threads} threads (the gate||up matmul "
+                      "one token row per thread at a time; SwiGLU and quantisation in numpy)"}
 
 
 def gemm1_main(args, w):
@@ -196,7 +216,9 @@ def gemm1_main(args, w):
                                inp["group_list"], inp["group_list_type"], inp["transpose_w13"],
                                inp["out_dtype"], x1_out=q, x1_scale_out=qs)
 
-    ms_per_step, mean_launch_ms = time_steps(step, args, dev)
+    ms_per_step, per_launch = time_steps(step, args, dev)
+    st = launch_stats(per_launch)
+    mean_launch_ms = st["mean_launch_ms"]
     flops, alg_bytes = w.flops(), w.algorithmic_bytes()
     achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
     line = {
@@ -228,7 +250,8 @@ def gemm1_main(args, w):
             "traffic": traffic_mod.recorded_traffic(w.name),
             "kernel": "gemm1_swiglu_kernel (gfr gate||up grouped MXFP8 GEMM + SwiGLU + MX quant)",
             "algorithmic_bytes_per_launch": alg_bytes,
-            "mean_launch_ms": round(mean_launch_ms, 5),
+            **st,
+            "frac_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
         },
         "cpu_baseline": None,
@@ -289,7 +312,9 @@ def main():
             inp["transpose_x2"], deterministic=args.deterministic, workspace=ws,
             split_k=args.split_k)
 
-    ms_per_step, mean_launch_ms = time_steps(step, args, dev)
+    ms_per_step, per_launch = time_steps(step, args, dev)
+    st = launch_stats(per_launch)
+    mean_launch_ms = st["mean_launch_ms"]
 
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()
@@ -335,7 +360,8 @@ def main():
             "traffic": traffic,
             "kernel": "fused_kernel (gfr grouped MXFP8 GEMM + finalize routing)",
             "algorithmic_bytes_per_launch": alg_bytes,
-            "mean_launch_ms": round(mean_launch_ms, 5),
+            **st,
+            "frac_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 /
                                (MXFP4_PEAK_TFLOPS if w.fp8 == "e2m1" else
                                 INT8_PEAK_TOPS if w4a8 else MXFP8_PEAK_TFLOPS), 4),

@@ -456,19 +456,6 @@ def as_numpy(inputs: dict) -> dict:
     return d
 
 
-def sample_rows(w: Workload, n: int, seed: int = 0) -> np.ndarray:
-    """A seeded sample of output rows plus the shared range's edge rows."""
-    rng = np.random.default_rng(10_000 + w.seed + seed)
-    rows = set(rng.choice(w.batch, size=min(n, w.batch), replace=False).tolist())
-    if w.R > 0:
-        for r in (w.shared_offset - 1, w.shared_offset, w.shared_offset + w.R - 1,
-                  w.shared_offset + w.R):
-            if 0 <= r < w.batch:
-                rows.add(r)
-    rows.update({0, w.batch - 1})
-    return np.array(sorted(rows), np.int64)
-
-
 # --------------------------------------------------------------------------
 # The upstream step of the MoE FFN (gate||up grouped matmul, SwiGLU, MX
 # quantisation; gfr_gemm1_swiglu_quant).  Shapes: the LLaDA2.0-mini grouped

@@ -41,11 +41,12 @@ class OracleError(RuntimeError):
 
 
 def build() -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    """Compile the oracle with gcc (plain -O2, no fast-math; OpenMP spreads
+    independent output rows over threads, each row computed whole by one)."""
     tmp = _LIB + ".tmp"
     subprocess.check_call(
         ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
-         "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+         "-fno-fast-math", "-fopenmp", _SRC, "-o", tmp, "-lm"])
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -89,8 +90,15 @@ def _lib() -> ctypes.CDLL:
             i64, i64, i64, i64, i64,  # M K N E batch
             p, i64, p, p]             # rows n_rows res mag
         lib.oracle_w4a8_finalize_routing.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         _lib_handle = lib
     return _lib_handle
+
+
+def num_threads() -> int:
+    """Threads the oracle's output-row loop runs on (OMP_NUM_THREADS, else all cores)."""
+    return int(_lib().oracle_num_threads())
 
 
 def decode(kind: str, code: int) -> float:

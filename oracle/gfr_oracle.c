@@ -30,6 +30,10 @@
  * The end of this file adds the A2/A3 W4A8 variant of [P3] (INT8 x INT4 with
  * FP32 per-channel and per-token scales) with the same routing.
  *
+ * Output rows are independent and are spread over OpenMP threads; each row
+ * is computed whole, in the order written below, by one thread, so the result
+ * is the same for any thread count.
+ *
  * Alongside out, the oracle returns mag = |out_init| + sum |w_t * term| +
  * |shared term| per element: the sum of the magnitudes of every term that
  * enters that element.  The GPU tolerance is expressed against it.
@@ -38,6 +42,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* Error codes returned by oracle_gmm_finalize_routing. */
 #define ORACLE_OK 0
@@ -262,10 +269,9 @@ int oracle_gmm_finalize_routing(
     int64_t *start = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
     int64_t *end = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
     int64_t *expert_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
-    double *acc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
-    double *absacc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     int rc = ORACLE_OK;
-    if (!start || !end || !expert_of || !acc || !absacc) {
+    int no_memory = 0;
+    if (!start || !end || !expert_of) {
         rc = ORACLE_NO_MEMORY;
         goto done;
     }
@@ -287,99 +293,129 @@ int oracle_gmm_finalize_routing(
             rc = ORACLE_BAD_ROW_INDEX;
             goto done;
         }
-
     for (int64_t i = 0; i < n_rows; ++i) {
         const int64_t b = rows ? rows[i] : i;
         if (b < 0 || b >= batch) {
             rc = ORACLE_BAD_ARG;
             goto done;
         }
-        double *res = res_out + i * N;
-        double *mag = mag_out + i * N;
+    }
 
-        /* out starts from its initial value ([P1] §3.1: out is the initial value). */
-        for (int64_t n = 0; n < N; ++n) {
-            res[n] = (double)out_init[b * N + n];
-            mag[n] = fabs(res[n]);
+    /* Output rows are independent: each is computed whole by one thread, in
+     * the order below, so the result does not depend on the thread count. */
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *absacc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (!acc || !absacc) {
+#pragma omp atomic write
+            no_memory = 1;
         }
-
-        /* Routed experts: every token scattered to row b, ascending t
-         * ([P1] §2.2 stages 1-3; [P3] formula 2). */
-        for (int64_t t = 0; t < M; ++t) {
-            const int64_t e = expert_of[t];
-            if (e < 0 || row_index[t] != b)
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            if (!acc || !absacc)
                 continue;
-            const double w = logit ? (double)logit[t] : 1.0;
+            const int64_t b = rows ? rows[i] : i;
+            double *res = res_out + i * N;
+            double *mag = mag_out + i * N;
 
+            /* out starts from its initial value ([P1] §3.1: out is the initial value). */
             for (int64_t n = 0; n < N; ++n) {
-                acc[n] = 0.0;
-                absacc[n] = 0.0;
+                res[n] = (double)out_init[b * N + n];
+                mag[n] = fabs(res[n]);
             }
 
-            /* Stage 1: the scaled matmul row, summed over k in ascending order
-             * for each n.  The loop nest is ordered for the memory layout only;
-             * each element's sum is the same sequence either way. */
-            const uint8_t *ps_row = pertoken_scale + t * KB * 2;
-            const uint8_t *sc = scale + (scale_per_expert ? e * KB * N * 2 : 0);
-            const uint8_t *x1_row = x1 + t * row_bytes(K, fp8_kind);
-            if (!transpose_x2) {
-                for (int64_t k = 0; k < K; ++k) {
-                    /* row k of expert e's [K, N] weight */
-                    const uint8_t *w2 = x2 + (e * K + k) * row_bytes(N, fp8_kind);
-                    const double a = fp8v[code_at(x1_row, k, fp8_kind)] *
-                                     e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
-                    for (int64_t n = 0; n < N; ++n) {
-                        const double bw = fp8v[code_at(w2, n, fp8_kind)] *
-                                          e8m0v[sc[((k / 64) * N + n) * 2 + (k / 32) % 2]];
-                        const double term = a * bw;
-                        acc[n] += term;
-                        absacc[n] += fabs(term);
-                    }
-                }
-            } else {
+            /* Routed experts: every token scattered to row b, ascending t
+             * ([P1] §2.2 stages 1-3; [P3] formula 2). */
+            for (int64_t t = 0; t < M; ++t) {
+                const int64_t e = expert_of[t];
+                if (e < 0 || row_index[t] != b)
+                    continue;
+                const double w = logit ? (double)logit[t] : 1.0;
+
                 for (int64_t n = 0; n < N; ++n) {
-                    /* row n of expert e's [N, K] weight */
-                    const uint8_t *w2 = x2 + (e * N + n) * row_bytes(K, fp8_kind);
+                    acc[n] = 0.0;
+                    absacc[n] = 0.0;
+                }
+
+                /* Stage 1: the scaled matmul row, summed over k in ascending
+                 * order for each n.  The loop nest is ordered for the memory
+                 * layout only; each element's sum is the same sequence either
+                 * way. */
+                const uint8_t *ps_row = pertoken_scale + t * KB * 2;
+                const uint8_t *sc = scale + (scale_per_expert ? e * KB * N * 2 : 0);
+                const uint8_t *x1_row = x1 + t * row_bytes(K, fp8_kind);
+                if (!transpose_x2) {
                     for (int64_t k = 0; k < K; ++k) {
+                        /* row k of expert e's [K, N] weight */
+                        const uint8_t *w2 = x2 + (e * K + k) * row_bytes(N, fp8_kind);
                         const double a = fp8v[code_at(x1_row, k, fp8_kind)] *
                                          e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
-                        const double bw = fp8v[code_at(w2, k, fp8_kind)] *
-                                          e8m0v[sc[(n * KB + k / 64) * 2 + (k / 32) % 2]];
-                        const double term = a * bw;
-                        acc[n] += term;
-                        absacc[n] += fabs(term);
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double bw = fp8v[code_at(w2, n, fp8_kind)] *
+                                              e8m0v[sc[((k / 64) * N + n) * 2 + (k / 32) % 2]];
+                            const double term = a * bw;
+                            acc[n] += term;
+                            absacc[n] += fabs(term);
+                        }
                     }
+                } else {
+                    for (int64_t n = 0; n < N; ++n) {
+                        /* row n of expert e's [N, K] weight */
+                        const uint8_t *w2 = x2 + (e * N + n) * row_bytes(K, fp8_kind);
+                        for (int64_t k = 0; k < K; ++k) {
+                            const double a = fp8v[code_at(x1_row, k, fp8_kind)] *
+                                             e8m0v[ps_row[(k / 64) * 2 + (k / 32) % 2]];
+                            const double bw = fp8v[code_at(w2, k, fp8_kind)] *
+                                              e8m0v[sc[(n * KB + k / 64) * 2 + (k / 32) % 2]];
+                            const double term = a * bw;
+                            acc[n] += term;
+                            absacc[n] += fabs(term);
+                        }
+                    }
+                }
+
+                /* Stages 2-3: weight by logit, add into row b. */
+                for (int64_t n = 0; n < N; ++n) {
+                    res[n] += w * acc[n];
+                    mag[n] += fabs(w) * absacc[n];
                 }
             }
 
-            /* Stages 2-3: weight by logit, add into row b. */
-            for (int64_t n = 0; n < N; ++n) {
-                res[n] += w * acc[n];
-                mag[n] += fabs(w) * absacc[n];
+            /* Stage 4: shared expert into rows [off, off + R) ([P1] §2.1,
+             * §5.3; [P3] formula 3). */
+            if (shared_input && b >= shared_input_offset &&
+                b < shared_input_offset + shared_rows) {
+                const int64_t r = b - shared_input_offset;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double v = shared_input_weight *
+                                     oracle_decode_bf16(shared_input[r * N + n]);
+                    res[n] += v;
+                    mag[n] += fabs(v);
+                }
             }
         }
-
-        /* Stage 4: shared expert into rows [off, off + R) ([P1] §2.1, §5.3;
-         * [P3] formula 3). */
-        if (shared_input && b >= shared_input_offset &&
-            b < shared_input_offset + shared_rows) {
-            const int64_t r = b - shared_input_offset;
-            for (int64_t n = 0; n < N; ++n) {
-                const double v = shared_input_weight *
-                                 oracle_decode_bf16(shared_input[r * N + n]);
-                res[n] += v;
-                mag[n] += fabs(v);
-            }
-        }
+        free(acc);
+        free(absacc);
     }
+    if (no_memory)
+        rc = ORACLE_NO_MEMORY;
 
 done:
     free(start);
     free(end);
     free(expert_of);
-    free(acc);
-    free(absacc);
     return rc;
+}
+
+/* Threads the row loops above run on (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* ---------------------------------------------------------------------------
@@ -523,10 +559,9 @@ int oracle_w4a8_finalize_routing(
     int64_t *start = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
     int64_t *end = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
     int64_t *expert_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
-    int64_t *dot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
-    int64_t *adot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
     int rc = ORACLE_OK;
-    if (!start || !end || !expert_of || !dot || !adot) {
+    int no_memory = 0;
+    if (!start || !end || !expert_of) {
         rc = ORACLE_NO_MEMORY;
         goto done;
     }
@@ -543,62 +578,80 @@ int oracle_w4a8_finalize_routing(
             rc = ORACLE_BAD_ROW_INDEX;
             goto done;
         }
-
     for (int64_t i = 0; i < n_rows; ++i) {
         const int64_t b = rows ? rows[i] : i;
         if (b < 0 || b >= batch) {
             rc = ORACLE_BAD_ARG;
             goto done;
         }
-        double *res = res_out + i * N;
-        double *mag = mag_out + i * N;
-        for (int64_t n = 0; n < N; ++n) {
-            res[n] = (double)out_init[b * N + n];
-            mag[n] = fabs(res[n]);
+    }
+
+    /* One output row per thread at a time, as in oracle_gmm_finalize_routing. */
+#pragma omp parallel
+    {
+        int64_t *dot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+        int64_t *adot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+        if (!dot || !adot) {
+#pragma omp atomic write
+            no_memory = 1;
         }
-        for (int64_t t = 0; t < M; ++t) {
-            const int64_t e = expert_of[t];
-            if (e < 0 || row_index[t] != b)
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            if (!dot || !adot)
                 continue;
-            const double w = (logit ? (double)logit[t] : 1.0) * (double)pertoken_scale[t];
-            int64_t xsum = 0, xabs = 0;
-            for (int64_t n = 0; n < N; ++n)
-                dot[n] = adot[n] = 0;
-            for (int64_t k = 0; k < K; ++k) {
-                const int64_t xv = x1[t * K + k];
-                xsum += xv;
-                xabs += xv < 0 ? -xv : xv;
-                const uint8_t *wrow = x2 + (e * K + k) * (N / 2);   /* row k of expert e */
+            const int64_t b = rows ? rows[i] : i;
+            double *res = res_out + i * N;
+            double *mag = mag_out + i * N;
+            for (int64_t n = 0; n < N; ++n) {
+                res[n] = (double)out_init[b * N + n];
+                mag[n] = fabs(res[n]);
+            }
+            for (int64_t t = 0; t < M; ++t) {
+                const int64_t e = expert_of[t];
+                if (e < 0 || row_index[t] != b)
+                    continue;
+                const double w = (logit ? (double)logit[t] : 1.0) * (double)pertoken_scale[t];
+                int64_t xsum = 0, xabs = 0;
+                for (int64_t n = 0; n < N; ++n)
+                    dot[n] = adot[n] = 0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t xv = x1[t * K + k];
+                    xsum += xv;
+                    xabs += xv < 0 ? -xv : xv;
+                    const uint8_t *wrow = x2 + (e * K + k) * (N / 2);   /* row k of expert e */
+                    for (int64_t n = 0; n < N; ++n) {
+                        const uint8_t byte = wrow[n / 2];
+                        const int64_t p = xv * int4_value((n & 1) ? (uint8_t)(byte >> 4) : byte);
+                        dot[n] += p;
+                        adot[n] += p < 0 ? -p : p;
+                    }
+                }
                 for (int64_t n = 0; n < N; ++n) {
-                    const uint8_t byte = wrow[n / 2];
-                    const int64_t p = xv * int4_value((n & 1) ? (uint8_t)(byte >> 4) : byte);
-                    dot[n] += p;
-                    adot[n] += p < 0 ? -p : p;
+                    const double s = (double)scale[e * N + n];
+                    const double o = offset ? (double)offset[e * N + n] : 0.0;
+                    res[n] += w * (s * (double)dot[n] + o * (double)xsum);
+                    mag[n] += fabs(w) * (fabs(s) * (double)adot[n] + fabs(o) * (double)xabs);
                 }
             }
-            for (int64_t n = 0; n < N; ++n) {
-                const double s = (double)scale[e * N + n];
-                const double o = offset ? (double)offset[e * N + n] : 0.0;
-                res[n] += w * (s * (double)dot[n] + o * (double)xsum);
-                mag[n] += fabs(w) * (fabs(s) * (double)adot[n] + fabs(o) * (double)xabs);
+            if (shared_input && b >= shared_input_offset &&
+                b < shared_input_offset + shared_rows) {
+                const int64_t r = b - shared_input_offset;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double v = shared_input_weight *
+                                     oracle_decode_bf16(shared_input[r * N + n]);
+                    res[n] += v;
+                    mag[n] += fabs(v);
+                }
             }
         }
-        if (shared_input && b >= shared_input_offset &&
-            b < shared_input_offset + shared_rows) {
-            const int64_t r = b - shared_input_offset;
-            for (int64_t n = 0; n < N; ++n) {
-                const double v = shared_input_weight *
-                                 oracle_decode_bf16(shared_input[r * N + n]);
-                res[n] += v;
-                mag[n] += fabs(v);
-            }
-        }
+        free(dot);
+        free(adot);
     }
+    if (no_memory)
+        rc = ORACLE_NO_MEMORY;
 done:
     free(start);
     free(end);
     free(expert_of);
-    free(dot);
-    free(adot);
     return rc;
 }

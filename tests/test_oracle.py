@@ -505,3 +505,29 @@ def test_mx_group_slack_analytic():
     want_g1 = 3 * 2.0 ** -22            # E = -9, q = 2^-22, each term 2^-9 > q
     assert got.shape == (1, 1)
     assert got[0, 0] == 0.5 * (want_g0 + want_g1)
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("kind", [0, 1])
+def test_truncation_patterns_oracle_side(kind, transpose):
+    """The crafted sums of tests/test_mfma_truncation_gpu.py on the CPU: the
+    oracle gives each exact sum (powers of two: exact in double), and its
+    truncation bound covers the value a run-truncating unit returns, while the
+    plain bar does not for the six patterns whose small terms are dropped."""
+    from tests.test_mfma_truncation_gpu import N, T, _inputs
+    from mxfp8_grouped_gemm_group_amd.workloads import as_numpy
+    inp, pats, S = _inputs(kind, transpose, device="cpu")
+    h = as_numpy(inp)
+    ref, mag = oracle.gmm_finalize_routing(
+        h["x1"], h["x2"], h["scale"], h["pertoken_scale"], h["group_list"], 1, None,
+        h["row_index"], None, 0.0, 0, h["out_init"], transpose, kind)
+    exact = np.array([pats[n][3] for n in range(N)])
+    model = np.array([pats[n][2] for n in range(N)])
+    assert np.array_equal(ref[0], exact)
+    assert np.array_equal(ref[1], (32.0 + T) * 2.0 ** -5 * 2.0 ** S[:, 0])
+    slack = oracle.mx_group_slack(h["x1"], h["x2"], h["scale"], h["pertoken_scale"],
+                                  h["group_list"], 1, None, h["row_index"], transpose, kind, 2)
+    err = np.abs(model - ref[0])
+    bar = 2e-5 * mag[0] + 1e-6
+    assert np.all(err <= bar + slack[0])
+    assert int(np.sum(err > bar)) == 6

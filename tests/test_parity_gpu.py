@@ -2,36 +2,52 @@
 
 Bar: |gpu - oracle| <= 2e-5 * mag + 1e-6 per element, where mag is the sum of
 the magnitudes of every term entering the element.  Integer-valued variants
-must match bit for bit.  Small cases are compared on every element; the full
-benchmark shapes on a seeded sample of output rows (all columns, every token
-routed to them) plus the shared range's edge rows.
+must match bit for bit.  Small cases, every shape of the c1-c3 benchmark sizes
+and the pages' test shapes are compared on every element; c4 and c5 on the
+rows tests/coverage.py selects (seeded random rows plus rows that reach every
+cooperative row group and the ragged tails), all columns, every token routed
+to them.
 
-The benchmark configurations and the pages' test shapes are held to that bar
-strictly.  The gfx950 block-scaled MFMA sums each run of 8 consecutive K
-products with 13 bits below the largest one (truncating the rest), so data
-with a wide dynamic range inside such a run can exceed it; the synthetic
-stress cases (small_*, wide E8M0 exponent ranges, E5M2 subnormals) are held to
-the bar plus the oracle's bound on that truncation (oracle.mx_group_slack).
+Every case is held to that bar strictly, except the cases named in
+SLACK_CASES.  The gfx950 block-scaled MFMA sums each run of 8 consecutive K
+products aligned to the largest one and truncates 13 bits below it
+(tests/test_mfma_truncation_gpu.py pins that behaviour through the library),
+so data with a wide dynamic range inside such a run can exceed the bar.  For
+the named synthetic stress cases (wide E8M0 exponent ranges, E5M2
+subnormals) the bar gains the oracle's bound on that truncation
+(oracle.mx_group_slack), and the number of elements that needed it is capped
+and printed.  MXFP4 products never lose bits to it (an E2M1 product has at
+most 4 significant bits and the 8 products of a run span less than 2^8), so no
+MXFP4 case is named.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, as_numpy, make_inputs, sample_rows
+from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, as_numpy, make_inputs
+from tests.coverage import coverage_rows
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 REL, ABS = 2e-5, 1e-6
 
+# Cases measured to exceed the plain bar through the MFMA's in-group
+# truncation: name -> the most elements allowed over the plain bar (twice the
+# most seen in any K split or mode, since the FP32 summation order of atomics
+# varies between runs).  Measured on the MI355X: small_t 3 of 36864 elements
+# (E5M2, E8M0 exponents +-6, K 640) in every K split and in deterministic
+# mode, small_t_k384 2 of 36864, small_many_n 5 of 307200 (E4M3FN, +-4); every
+# other case, each MXFP4 one at under 1 % of the bar, stays within it.  No
+# other case may exceed it.
+SLACK_CASES = {"small_t": 6, "small_t_k384": 4, "small_many_n": 10}
+
 
 def _gfr():
     import mxfp8_grouped_gemm_group_amd as gfr
     gfr.load_library()
     return gfr
-
-
 def run_gpu(inp, out=None, **kw):
     gfr = _gfr()
     out = inp["out"].clone() if out is None else out
@@ -53,10 +69,14 @@ def run_oracle(inp, rows=None, **over):
         h["transpose_x2"], h["fp8_kind"], rows=rows)
 
 
-def assert_parity(got, ref, mag, exact=False, what="", slack=None):
+def assert_parity(got, ref, mag, exact=False, what="", case=None, slack=None):
+    """Element-wise acceptance.  ``case`` names the workload; only cases in
+    SLACK_CASES may use ``slack`` (the truncation bound, or a callable giving
+    it), and then on at most SLACK_CASES[case] elements."""
     got = got.detach().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else got
     if exact:
         bad = np.argwhere(got != ref)
+        print(f"{what}: {bad.shape[0]} of {got.size} elements differ (exact)", flush=True)
         assert bad.size == 0, f"{what}: {len(bad)} elements differ, first {bad[:3].tolist()}"
         return
     ok, worst = oracle.within_tolerance(got, ref, mag, REL, ABS)
@@ -64,7 +84,10 @@ def assert_parity(got, ref, mag, exact=False, what="", slack=None):
     print(f"{what}: worst err/bound = {worst:.3g} ({n_over} of {got.size} over)", flush=True)
     if ok:
         return
-    assert slack is not None, f"{what}: worst ratio {worst}"
+    assert case in SLACK_CASES and slack is not None, \
+        f"{what}: {n_over} elements over the bar, worst ratio {worst}"
+    assert n_over <= SLACK_CASES[case], \
+        f"{what}: {n_over} elements over the bar, more than the {SLACK_CASES[case]} allowed"
     if callable(slack):   # computed only when the plain tolerance is exceeded
         slack = slack()
     err = np.abs(got - ref)
@@ -108,23 +131,39 @@ def test_small_full(name, split_k):
     inp = make_inputs(w, DEV)
     got = run_gpu(inp, split_k=split_k)
     ref, mag = run_oracle(inp)
-    assert_parity(got, ref, mag, exact=w.exact, what=name, slack=lambda: slack_for(inp))
+    assert_parity(got, ref, mag, exact=w.exact, what=f"{name} split_k={split_k}", case=name,
+                  slack=lambda: slack_for(inp))
 
 
 # ---------------------------------------------------------------------------
-# Benchmark shapes (sampled rows) and the pages' test shapes.
+# The c1-c3 benchmark shapes (and their MXFP4, per-expert-scale and integer
+# variants) and the pages' test shapes: every element.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["c1_exact", "c2_exact", "c3_exact", "c4_exact", "c5_exact",
-                                  "c1", "c2", "c3", "c4", "c5",
-                                  "p1_tc_a", "p1_tc_b", "p2_ragged", "c3_pe", "c5_pe",
-                                  "c2_fp4", "c3_fp4t", "c3_fp4t_exact", "c5_fp4",
-                                  "c1_fp4", "c3_fp4", "c3_fp4_exact", "c4_fp4"])
-def test_full_shapes_sampled(name):
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c1_exact", "c2_exact", "c3_exact",
+                                  "c3_pe", "c1_fp4", "c2_fp4", "c3_fp4", "c3_fp4_exact",
+                                  "c3_fp4t", "c3_fp4t_exact", "p1_tc_a", "p1_tc_b",
+                                  "p2_ragged"])
+def test_full_shapes_every_element(name):
     w = WORKLOADS[name]
-    print(f"case {name}", flush=True)
+    print(f"case {name} (every element)", flush=True)
     inp = make_inputs(w, DEV)
     got = run_gpu(inp)
-    rows = sample_rows(w, 12)
+    ref, mag = run_oracle(inp)
+    assert_parity(got, ref, mag, exact=w.exact, what=name)
+
+
+# ---------------------------------------------------------------------------
+# c4 and c5 (and variants): the coverage rows, every column.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c4", "c5", "c4_exact", "c5_exact", "c5_pe", "c4_fp4",
+                                  "c5_fp4"])
+def test_large_shapes_coverage_rows(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w, DEV)
+    rows = coverage_rows(w, inp["row_index"].cpu().numpy())
+    print(f"case {name} ({rows.size} of {w.batch} rows)", flush=True)
+    assert rows.size >= 16 + 2
+    got = run_gpu(inp)
     ref, mag = run_oracle(inp, rows=rows)
     assert_parity(got[torch.as_tensor(rows, device=DEV)], ref, mag, exact=w.exact, what=name)
 
@@ -141,12 +180,11 @@ def test_deterministic_mode(name):
     a = run_gpu(inp, deterministic=True)
     b = run_gpu(inp, deterministic=True)
     assert torch.equal(a, b)
-    rows = sample_rows(w, 12) if w.M > 1000 else None
+    rows = coverage_rows(w, inp["row_index"].cpu().numpy()) if w.M > 2000 else None
     ref, mag = run_oracle(inp, rows=rows)
     got = a if rows is None else a[torch.as_tensor(rows, device=DEV)]
-    stress = name.startswith("small")
-    assert_parity(got, ref, mag, exact=w.exact, what=name + " det",
-                  slack=(lambda: slack_for(inp, rows)) if stress else None)
+    assert_parity(got, ref, mag, exact=w.exact, what=name + " det", case=name,
+                  slack=lambda: slack_for(inp, rows))
 
 
 # ---------------------------------------------------------------------------
@@ -169,7 +207,8 @@ def test_logit_and_shared_absent():
     inp["shared_input"] = None
     got = run_gpu(inp)
     ref, mag = run_oracle(inp)
-    assert_parity(got, ref, mag, what="no logit / no shared", slack=lambda: slack_for(inp))
+    assert_parity(got, ref, mag, what="small_t no logit / no shared", case="small_t",
+                  slack=lambda: slack_for(inp))
 
 
 def test_empty_groups_and_no_tokens():
@@ -213,7 +252,7 @@ def test_device_status_bits():
     lg = inp["logit"].clone()
     lg[40] = 0
     ref, mag = run_oracle(dict(inp, logit=lg))
-    assert_parity(got, ref, mag, what="bad row_index skipped",
+    assert_parity(got, ref, mag, what="small_n bad row_index skipped", case="small_n",
                   slack=lambda: slack_for(dict(inp, logit=lg)))
 
     status.zero_()
@@ -230,3 +269,16 @@ def test_group_list_type_equivalence_bitwise_exact():
     g = torch.cumsum(inp["group_list"], 0)
     b = run_gpu(dict(inp, group_list=g, group_list_type=0))
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_row_index_int32_equals_int64_bitwise_exact(deterministic):
+    """row_index may be int32 through the descriptor ABI ([P1] §5.4 passes it
+    as int32): integer-exact data gives the same bits as int64 in both modes."""
+    for name in ("small_n_exact", "small_big_t_exact"):
+        w = WORKLOADS[name]
+        inp = make_inputs(w, DEV)
+        a = run_gpu(inp, deterministic=deterministic)
+        b = run_gpu(dict(inp, row_index=inp["row_index"].to(torch.int32)),
+                    deterministic=deterministic)
+        assert torch.equal(a, b), name

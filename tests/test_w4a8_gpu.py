@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_w4a8_inputs, sample_rows
+from mxfp8_grouped_gemm_group_amd.workloads import WORKLOADS, make_w4a8_inputs
+from tests.coverage import coverage_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -69,12 +70,12 @@ def test_w4a8_small_full(name, split_k):
 
 
 @pytest.mark.parametrize("name", ["w4a8_p3", "w4a8_p3_exact"])
-def test_w4a8_full_shape_sampled(name):
+def test_w4a8_full_shape_coverage_rows(name):
     w = WORKLOADS[name]
-    print(f"case {name}", flush=True)
     inp = make_w4a8_inputs(w, DEV)
+    rows = coverage_rows(w, inp["row_index"].cpu().numpy())
+    print(f"case {name} ({rows.size} of {w.batch} rows)", flush=True)
     got = run_gpu(inp)
-    rows = sample_rows(w, 14)
     ref, mag = run_oracle(inp, rows)
     check(got[rows], ref, mag, w.exact, name)
 

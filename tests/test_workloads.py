@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from mxfp8_grouped_gemm_group_amd.workloads import (GEMM1_WORKLOADS, WORKLOADS, as_numpy,
-                                                    make_gemm1_inputs, make_inputs, sample_rows)
+                                                    make_gemm1_inputs, make_inputs)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "p1_tc_a", "p1_tc_b",
@@ -59,11 +59,29 @@ def test_make_inputs_shapes_and_determinism(name):
         assert torch.equal(v, v.round()) and v.abs().max() <= 2
 
 
-def test_sample_rows_cover_shared_edges():
-    w = WORKLOADS["c4"]
-    r = sample_rows(w, 16)
-    for e in (127, 128, 383, 384, 0, 511):
-        assert e in r
+@pytest.mark.parametrize("name", ["c4", "c5", "w4a8_p3"])
+def test_coverage_rows_reach_every_cooperative_group(name):
+    from tests.coverage import COOP_MIN_ROWS, GROUP_STEP, coverage_rows
+    w = WORKLOADS[name]
+    ri = np.random.default_rng(5).permutation(np.tile(np.arange(w.batch), -(-w.M // w.batch)))[:w.M]
+    rows = coverage_rows(w, ri)
+    assert np.all(np.diff(rows) > 0) and rows[0] >= 0 and rows[-1] < w.batch
+    assert rows.size >= 18 and {0, w.batch - 1} <= set(rows.tolist())
+    if w.R > 0:
+        for e in (w.shared_offset - 1, w.shared_offset, w.shared_offset + w.R - 1,
+                  w.shared_offset + w.R):
+            assert not 0 <= e < w.batch or e in rows
+    sel = np.isin(ri, rows)
+    c = w.counts()
+    s = np.concatenate([[0], np.cumsum(c)[:-1]])
+    n_coop = 0
+    for e in range(w.E):
+        if c[e] >= COOP_MIN_ROWS:
+            n_coop += 1
+            for g0 in range(0, c[e], GROUP_STEP):
+                assert sel[s[e] + g0: s[e] + min(c[e], g0 + GROUP_STEP)].any(), (e, g0)
+            assert sel[s[e] + c[e] - 1]
+    assert n_coop > 0
 
 
 @pytest.mark.parametrize("name", ["g1_small", "g1_small_t", "g1_big", "g1_big_t_pe",

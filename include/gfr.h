@@ -22,9 +22,22 @@
  * pair of axes, and element j of the pair for 64-block b covers
  * k in [64b + 32j, 64b + 32j + 32).
  *
+ * Two layers of entry points:
+ *  - the tensor-descriptor calls (gmm_finalize_routing, gmm_finalize_routing_ex,
+ *    gfr_workspace_size, gfr_w4a8_finalize_routing, gfr_gemm1_swiglu_quant)
+ *    take every tensor as a gfr_tensor and derive all sizes from the shapes;
+ *    each descriptor's dtype, rank and shape is checked against the others on
+ *    the host before anything is enqueued (GFR_ERR_BAD_DTYPE / _BAD_RANK /
+ *    _BAD_SHAPE), as [P3]'s first phase validates the parameters;
+ *  - the raw calls (*_raw) take device pointers plus the sizes M, K, N, E,
+ *    batch, R and trust them: each buffer must hold at least the bytes its
+ *    documented shape implies at those sizes, or the kernels read or write
+ *    past it.  The descriptor calls check exactly that and then call them.
+ *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major storage
  *    owned by the caller; the library never allocates, frees or retains them.
+ *    Descriptors themselves are read on the host during the call only.
  *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is the
  *    null stream).  Nothing is synchronised and no device memory is read on the
  *    host: group_list is consumed on the device.
@@ -59,8 +72,39 @@ enum gfr_status {
                                     workspace not 256-byte aligned */
     GFR_ERR_WORKSPACE_TOO_SMALL = 6,
     GFR_ERR_BAD_ARG = 7,         /* unknown enum value (fp8_kind, group_list_type) */
-    GFR_ERR_HIP = 8              /* a HIP runtime call failed */
+    GFR_ERR_HIP = 8,             /* a HIP runtime call failed */
+    GFR_ERR_BAD_DTYPE = 9,       /* a descriptor's dtype is not one its argument takes,
+                                    or x1 / x2 do not match fp8_kind */
+    GFR_ERR_BAD_RANK = 10        /* a descriptor's ndim is not its argument's rank */
 };
+
+/* Element types of a gfr_tensor.  Packed types hold two 4-bit elements per
+ * byte along the last axis (element 2j in the low nibble of byte j); their
+ * descriptor's last extent counts bytes. */
+enum gfr_dtype {
+    GFR_DT_FP8_E4M3FN = 0,
+    GFR_DT_FP8_E5M2 = 1,
+    GFR_DT_FP4_E2M1X2 = 2,   /* MXFP4 elements, packed */
+    GFR_DT_E8M0 = 3,         /* E8M0 scale codes, one byte each */
+    GFR_DT_U8 = 4,           /* raw bytes: accepted wherever E8M0 codes are */
+    GFR_DT_BF16 = 5,
+    GFR_DT_F32 = 6,
+    GFR_DT_I64 = 7,
+    GFR_DT_I32 = 8,
+    GFR_DT_I8 = 9,
+    GFR_DT_INT4X2 = 10       /* signed 4-bit (two's complement) elements, packed */
+};
+
+/* A tensor argument: device pointer to contiguous row-major storage of
+ * shape[0] x ... x shape[ndim - 1] elements of dtype (1 <= ndim <= 4; the
+ * unused extents are ignored).  data may be NULL only when the tensor holds
+ * no element. */
+typedef struct gfr_tensor {
+    void *data;
+    int32_t dtype;
+    int32_t ndim;
+    int64_t shape[4];
+} gfr_tensor;
 
 /* Element formats of x1 and x2 ([P1] §3.1: FP8 E4M3FN or E5M2; [P3] Atlas
  * 350 MX notes: the MXFP4 variant, FP4 E2M1 elements stored two per byte
@@ -98,70 +142,81 @@ typedef struct gfr_options {
     /* 0: scale is shared by all experts (3-D, [P1] §3.1).  1: scale carries a
      * leading expert axis ([P3] Atlas 350 scale notes: (e, n, ceil(k/64), 2)
      * when transpose_x2, by the same reading (e, ceil(k/64), n, 2)
-     * otherwise); expert e's rows use slice e. */
+     * otherwise); expert e's rows use slice e.  The descriptor calls take
+     * this from the rank of scale (4-D: per expert); a nonzero value there
+     * requires a 4-D scale (GFR_ERR_BAD_RANK). */
     int scale_per_expert;
 } gfr_options;
 
+/* ======================================================================== *
+ * Tensor-descriptor calls                                                  *
+ * ======================================================================== */
+
 /*
- * gmm_finalize_routing — the fused operator ([P1] §2.1–2.2; [P3] formulas).
+ * gmm_finalize_routing — the fused operator ([P1] §2.1–2.2; [P3] formulas),
+ * in [P1]'s parameter order.  Sizes come from the descriptors (elements):
  *
- *  x1              [M, K] FP8 (fp8_kind), routed tokens sorted by expert.
- *  x2              [E, K, N] FP8, or [E, N, K] when transpose_x2 != 0.
- *  scale           E8M0 bytes, [ceil(K/64), N, 2], or [N, ceil(K/64), 2] when
- *                  transpose_x2 != 0; shared by all experts ([P1] §3.1), or
- *                  with a leading [E] axis (gfr_options.scale_per_expert).
- *  pertoken_scale  E8M0 bytes, [M, ceil(K/64), 2].
- *  group_list      int64 [E], format per group_list_type.
- *  logit           float32 [M], or NULL for weight 1 ([P1] §5.1 has_logit).
- *  row_index       int64 [M], destination row of each token, in [0, batch).
- *  shared_input    bfloat16 [shared_rows, N], or NULL (no shared expert).
+ *  x1              [M, K] of dtype FP8_E4M3FN / FP8_E5M2 / FP4_E2M1X2 (then
+ *                  [M, K/2] bytes), routed tokens sorted by expert.
+ *  x2              [E, K, N], or [E, N, K] when transpose_x2 != 0, of x1's
+ *                  dtype (FP4_E2M1X2: the last extent halved, packed along it).
+ *  scale           E8M0 (or U8) [ceil(K/64), N, 2], or [N, ceil(K/64), 2]
+ *                  when transpose_x2 != 0; shared by all experts ([P1] §3.1),
+ *                  or 4-D with a leading E extent (per expert, [P3]).
+ *  pertoken_scale  E8M0 (or U8) [M, ceil(K/64), 2].
+ *  group_list      I64 [E], format per group_list_type.
+ *  logit           F32 [M], or NULL (descriptor or data) for weight 1 ([P1]
+ *                  §5.1 has_logit).
+ *  row_index       I64 or I32 [M]: destination row of each token, in
+ *                  [0, batch) ([P1] §3.1 int64; §5.4 passes int32).
+ *  shared_input    BF16 [R, N], or NULL (no shared expert).
  *  shared_input_weight, shared_input_offset: shared rows land in
- *                  out[offset, offset + shared_rows); offset >= 0 and
- *                  offset + shared_rows <= batch.
- *  out             float32 [batch, N]; read as the initial value and updated
- *                  in place ([P1] §3.1, §5.4).
- *  transpose_x2    0 or 1 (scale layout follows it, [P3] Atlas 350 notes).
- *  fp8_kind        gfr_fp8_kind of both x1 and x2.  With GFR_FP4_E2M1, x1 is
- *                  [M, K/2] bytes and x2 [E, N, K/2] bytes (transposed, packed
- *                  along K) or [E, K, N/2] bytes (packed along N); M, K, N stay
- *                  element counts.
- *  M, K, N, E, batch, shared_rows: sizes.  M = 0 leaves only the shared term;
- *                  N = 0 or batch = 0 is a no-op ([P3] empty-tensor notes).
+ *                  out[offset, offset + R); offset >= 0 and offset + R <= batch
+ *                  ([P3] Atlas 350 notes).
+ *  out             F32 [batch, N]; read as the initial value and updated in
+ *                  place ([P1] §3.1, §5.4).
+ *  transpose_x2    0 or 1 (the weight-scale layout follows it, [P3]).
+ *  fp8_kind        gfr_fp8_kind; must name x1's and x2's dtype.
  *  stream          hipStream_t.
  *
- * Implementation limits (GFR_ERR_UNSUPPORTED): K % 128 != 0, N % 16 != 0,
- * E outside [1, 1024], M or batch >= 2^31; for GFR_FP4_E2M1 also K % 256 != 0
- * with transpose_x2 == 1, N % 32 != 0 with transpose_x2 == 0.  x1, x2 and
- * scale must be 16-byte aligned (GFR_ERR_BAD_ALIGNMENT).  Atomic mode needs no
- * workspace.
+ * M = 0 leaves only the shared term; N = 0 or batch = 0 is a no-op ([P3]
+ * empty-tensor notes).  Errors: GFR_ERR_NULL_ARG (a required descriptor, or
+ * the data of a non-empty tensor, is NULL), GFR_ERR_BAD_DTYPE,
+ * GFR_ERR_BAD_RANK, GFR_ERR_BAD_SHAPE (an extent disagrees with the sizes the
+ * others fix), GFR_ERR_BAD_OFFSET, GFR_ERR_BAD_ARG, GFR_ERR_UNSUPPORTED and
+ * GFR_ERR_BAD_ALIGNMENT as for gmm_finalize_routing_raw_ex, GFR_ERR_HIP.
  * Returns a gfr_status.
  */
-int gmm_finalize_routing(const void *x1, const void *x2, const uint8_t *scale,
-                         const uint8_t *pertoken_scale, const int64_t *group_list,
-                         int group_list_type, const float *logit,
-                         const int64_t *row_index, const uint16_t *shared_input,
+int gmm_finalize_routing(const gfr_tensor *x1, const gfr_tensor *x2, const gfr_tensor *scale,
+                         const gfr_tensor *pertoken_scale, const gfr_tensor *group_list,
+                         int group_list_type, const gfr_tensor *logit,
+                         const gfr_tensor *row_index, const gfr_tensor *shared_input,
                          float shared_input_weight, int64_t shared_input_offset,
-                         float *out, int transpose_x2, int fp8_kind,
-                         int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
-                         int64_t shared_rows, void *stream);
+                         const gfr_tensor *out, int transpose_x2, int fp8_kind, void *stream);
 
-/* gmm_finalize_routing with options (NULL opts = defaults: atomic mode, no
- * workspace, no status word).  Returns GFR_ERR_WORKSPACE_TOO_SMALL when the
- * deterministic mode is asked for without enough workspace. */
-int gmm_finalize_routing_ex(const void *x1, const void *x2, const uint8_t *scale,
-                            const uint8_t *pertoken_scale, const int64_t *group_list,
-                            int group_list_type, const float *logit,
-                            const int64_t *row_index, const uint16_t *shared_input,
+/* gmm_finalize_routing with options (NULL = atomic mode, no workspace, no
+ * status word, K split chosen on the device).  GFR_ERR_WORKSPACE_TOO_SMALL
+ * when the deterministic mode is asked for without gfr_workspace_size()
+ * bytes of workspace. */
+int gmm_finalize_routing_ex(const gfr_tensor *x1, const gfr_tensor *x2, const gfr_tensor *scale,
+                            const gfr_tensor *pertoken_scale, const gfr_tensor *group_list,
+                            int group_list_type, const gfr_tensor *logit,
+                            const gfr_tensor *row_index, const gfr_tensor *shared_input,
                             float shared_input_weight, int64_t shared_input_offset,
-                            float *out, int transpose_x2, int fp8_kind,
-                            int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
-                            int64_t shared_rows, void *stream,
+                            const gfr_tensor *out, int transpose_x2, int fp8_kind, void *stream,
                             const gfr_options *opts);
 
-/* Workspace bytes a call with these sizes and options needs — the first phase
- * of the two-phase call of [P3] ("GetWorkspaceSize", then execute).  Pure host
- * arithmetic: no device call.  Returns a gfr_status. */
-int gfr_workspace_size(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+/* The first phase of [P3]'s two-phase call ("GetWorkspaceSize", then
+ * execute): validates the same arguments as gmm_finalize_routing_ex (data
+ * pointers are not dereferenced; opts' workspace fields are ignored) and
+ * stores the workspace bytes the call needs in *bytes (0 in atomic mode).
+ * Pure host work.  Returns a gfr_status. */
+int gfr_workspace_size(const gfr_tensor *x1, const gfr_tensor *x2, const gfr_tensor *scale,
+                       const gfr_tensor *pertoken_scale, const gfr_tensor *group_list,
+                       int group_list_type, const gfr_tensor *logit,
+                       const gfr_tensor *row_index, const gfr_tensor *shared_input,
+                       float shared_input_weight, int64_t shared_input_offset,
+                       const gfr_tensor *out, int transpose_x2, int fp8_kind,
                        const gfr_options *opts, size_t *bytes);
 
 /*
@@ -186,34 +241,34 @@ int gfr_workspace_size(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch
  * OCP Microscaling rule, and dequantising the output reproduces sw within
  * half a code step (values that scale past the largest finite code saturate).
  *
- *  xin             [M, H] FP8 (fp8_kind), tokens sorted by expert.
- *  w13             [E, H, 2I] FP8, or [E, 2I, H] when transpose_w13 != 0.
- *  scale           E8M0 bytes, [ceil(H/64), 2I, 2], or [2I, ceil(H/64), 2]
- *                  when transpose_w13; a leading [E] axis with
- *                  gfr_options.scale_per_expert.
- *  xin_scale       E8M0 bytes, [M, ceil(H/64), 2].
- *  group_list      int64 [E], format per group_list_type.
- *  x1_out          [M, I] FP8 codes of out_kind (written; rows of tokens in no
- *                  expert's range are left untouched).
- *  x1_scale_out    [M, I/64, 2] E8M0 bytes (written, same rows).
+ *  xin             FP8 [M, H] (dtype FP8_E4M3FN or FP8_E5M2), tokens sorted
+ *                  by expert.
+ *  w13             [E, H, 2I], or [E, 2I, H] when transpose_w13 != 0, of
+ *                  xin's dtype.
+ *  scale           E8M0 (or U8) [ceil(H/64), 2I, 2], or [2I, ceil(H/64), 2]
+ *                  when transpose_w13; 4-D with a leading E extent for
+ *                  per-expert scales.
+ *  xin_scale       E8M0 (or U8) [M, ceil(H/64), 2].
+ *  group_list      I64 [E], format per group_list_type.
+ *  x1_out          [M, I], dtype FP8_E4M3FN or FP8_E5M2: the output codes
+ *                  (written; rows of tokens in no expert's range are left
+ *                  untouched).
+ *  x1_scale_out    E8M0 (or U8) [M, I/64, 2] (written, same rows).
  *  transpose_w13   0 or 1.
- *  fp8_kind        GFR_FP8_E4M3FN or GFR_FP8_E5M2 (xin and w13).
- *  out_kind        GFR_FP8_E4M3FN or GFR_FP8_E5M2 (x1_out).
- *  M, H, I, E      sizes; M = 0 or I = 0 is a no-op.
  *  stream          hipStream_t.
- *  opts            may be NULL; only scale_per_expert and status_dev are used
- *                  (the output is written once per element: no atomics, no
- *                  K split, bitwise repeatable).
+ *  opts            may be NULL; only status_dev is used (the output is
+ *                  written once per element: no atomics, no K split, bitwise
+ *                  repeatable); a nonzero scale_per_expert requires a 4-D scale.
  *
- * Limits (GFR_ERR_UNSUPPORTED): H % 128 != 0, I % 64 != 0, E outside
- * [1, 1024], 2I * H >= 2^31, GFR_FP4_E2M1 input.  xin, w13 and scale must be
- * 16-byte aligned.  Returns a gfr_status.
+ * M = 0 or I = 0 is a no-op.  Limits (GFR_ERR_UNSUPPORTED): H % 128 != 0,
+ * I % 64 != 0, E outside [1, 1024], 2I * H >= 2^31.  xin, w13 and scale must
+ * be 16-byte aligned.  Returns a gfr_status.
  */
-int gfr_gemm1_swiglu_quant(const void *xin, const void *w13, const uint8_t *scale,
-                           const uint8_t *xin_scale, const int64_t *group_list,
-                           int group_list_type, void *x1_out, uint8_t *x1_scale_out,
-                           int transpose_w13, int fp8_kind, int out_kind, int64_t M, int64_t H,
-                           int64_t I, int64_t E, void *stream, const gfr_options *opts);
+int gfr_gemm1_swiglu_quant(const gfr_tensor *xin, const gfr_tensor *w13, const gfr_tensor *scale,
+                           const gfr_tensor *xin_scale, const gfr_tensor *group_list,
+                           int group_list_type, const gfr_tensor *x1_out,
+                           const gfr_tensor *x1_scale_out, int transpose_w13, void *stream,
+                           const gfr_options *opts);
 
 /*
  * gfr_w4a8_finalize_routing — the A2/A3 W4A8 variant of the operator ([P3]
@@ -228,19 +283,20 @@ int gfr_gemm1_swiglu_quant(const void *xin, const void *w13, const uint8_t *scal
  *   out[row_index[t], n] += logit[t] * y[t, n]
  *   out[off + r, n]      += shared_input_weight * shared_input[r, n]
  *
- *  x1              int8 [M, K].
- *  x2              signed 4-bit weights [E, K, N/2] bytes: two per byte along
- *                  n, element 2j in the low nibble of byte j (the pages'
- *                  (e, k, n/8) INT32 packing read as little-endian nibbles).
- *  scale           float32 [E, 1, N]: the fused per-channel scale (the pages
+ *  x1              I8 [M, K].
+ *  x2              INT4X2 (or U8) [E, K, N/2] bytes: signed 4-bit weights,
+ *                  two per byte along n, element 2j in the low nibble (the
+ *                  pages' (e, k, n/8) INT32 packing read as little-endian
+ *                  nibbles).
+ *  scale           F32 [E, 1, N]: the fused per-channel scale (the pages
  *                  type it INT64; its value is taken here as FP32).
- *  offset          float32 [E, 1, N], or NULL for symmetric weights.
- *  pertoken_scale  float32 [M].
- *  group_list, group_list_type, logit, row_index, shared_input (bf16 [R, N]),
- *  shared_input_weight, shared_input_offset, out (float32 [batch, N], in/out),
- *  M, K, N, E, batch, shared_rows, stream: as gmm_finalize_routing.
+ *  offset          F32 [E, 1, N], or NULL for symmetric weights.
+ *  pertoken_scale  F32 [M].
+ *  group_list, group_list_type, logit, row_index, shared_input (BF16 [R, N]),
+ *  shared_input_weight, shared_input_offset, out (F32 [batch, N], in/out),
+ *  stream: as gmm_finalize_routing.
  *  opts            as gmm_finalize_routing_ex (deterministic mode, workspace
- *                  from gfr_workspace_size, status word, K split);
+ *                  from gfr_workspace_size_raw, status word, K split);
  *                  scale_per_expert must be 0 (the scale always has an expert
  *                  axis).
  *
@@ -253,13 +309,77 @@ int gfr_gemm1_swiglu_quant(const void *xin, const void *w13, const uint8_t *scal
  * outside [1, 1024], M or batch >= 2^31.  x1 and x2 must be 16-byte aligned,
  * scale and offset 8-byte aligned.  Returns a gfr_status.
  */
-int gfr_w4a8_finalize_routing(const int8_t *x1, const uint8_t *x2, const float *scale,
-                              const float *offset, const float *pertoken_scale,
-                              const int64_t *group_list, int group_list_type, const float *logit,
-                              const int64_t *row_index, const uint16_t *shared_input,
-                              float shared_input_weight, int64_t shared_input_offset, float *out,
-                              int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
-                              int64_t shared_rows, void *stream, const gfr_options *opts);
+int gfr_w4a8_finalize_routing(const gfr_tensor *x1, const gfr_tensor *x2, const gfr_tensor *scale,
+                              const gfr_tensor *offset, const gfr_tensor *pertoken_scale,
+                              const gfr_tensor *group_list, int group_list_type,
+                              const gfr_tensor *logit, const gfr_tensor *row_index,
+                              const gfr_tensor *shared_input, float shared_input_weight,
+                              int64_t shared_input_offset, const gfr_tensor *out, void *stream,
+                              const gfr_options *opts);
+
+/* ======================================================================== *
+ * Raw calls: device pointers plus sizes, semantics as the descriptor calls *
+ * above.  Nothing ties the sizes to the buffers: every buffer must hold at  *
+ * least the bytes of its shape at the given M, K, N, E, batch and R (x1 and *
+ * x2 packed for FP4 as above, row_index int64); a smaller buffer is read or *
+ * written out of bounds.                                                    *
+ * ======================================================================== */
+
+/* gmm_finalize_routing on pointers and sizes.  M, K, N count elements (FP4:
+ * x1 is [M, K/2] bytes, x2 [E, N, K/2] or [E, K, N/2] bytes).
+ *
+ * Implementation limits (GFR_ERR_UNSUPPORTED): K % 128 != 0, N % 16 != 0,
+ * E outside [1, 1024], M or batch >= 2^31; for GFR_FP4_E2M1 also K % 256 != 0
+ * with transpose_x2 == 1, N % 32 != 0 with transpose_x2 == 0.  x1, x2 and
+ * scale must be 16-byte aligned (GFR_ERR_BAD_ALIGNMENT).  Atomic mode needs no
+ * workspace.  Returns a gfr_status. */
+int gmm_finalize_routing_raw(const void *x1, const void *x2, const uint8_t *scale,
+                             const uint8_t *pertoken_scale, const int64_t *group_list,
+                             int group_list_type, const float *logit,
+                             const int64_t *row_index, const uint16_t *shared_input,
+                             float shared_input_weight, int64_t shared_input_offset,
+                             float *out, int transpose_x2, int fp8_kind,
+                             int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                             int64_t shared_rows, void *stream);
+
+/* gmm_finalize_routing_raw with options (as gmm_finalize_routing_ex). */
+int gmm_finalize_routing_raw_ex(const void *x1, const void *x2, const uint8_t *scale,
+                                const uint8_t *pertoken_scale, const int64_t *group_list,
+                                int group_list_type, const float *logit,
+                                const int64_t *row_index, const uint16_t *shared_input,
+                                float shared_input_weight, int64_t shared_input_offset,
+                                float *out, int transpose_x2, int fp8_kind,
+                                int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                                int64_t shared_rows, void *stream,
+                                const gfr_options *opts);
+
+/* Workspace bytes of a call with these sizes and options (first phase of
+ * [P3]'s two-phase call, sizes only).  Pure host arithmetic.  Returns a
+ * gfr_status. */
+int gfr_workspace_size_raw(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch,
+                           const gfr_options *opts, size_t *bytes);
+
+/* gfr_gemm1_swiglu_quant on pointers and sizes: xin [M, H], w13 [E, H, 2I] or
+ * [E, 2I, H], x1_out [M, I] bytes; fp8_kind names xin's and w13's format,
+ * out_kind x1_out's (GFR_FP8_E4M3FN or GFR_FP8_E5M2); opts->scale_per_expert
+ * selects a 4-D scale.  Limits as gfr_gemm1_swiglu_quant. */
+int gfr_gemm1_swiglu_quant_raw(const void *xin, const void *w13, const uint8_t *scale,
+                               const uint8_t *xin_scale, const int64_t *group_list,
+                               int group_list_type, void *x1_out, uint8_t *x1_scale_out,
+                               int transpose_w13, int fp8_kind, int out_kind, int64_t M,
+                               int64_t H, int64_t I, int64_t E, void *stream,
+                               const gfr_options *opts);
+
+/* gfr_w4a8_finalize_routing on pointers and sizes (x2 [E, K, N/2] bytes,
+ * scale / offset [E, 1, N]).  Limits as gfr_w4a8_finalize_routing. */
+int gfr_w4a8_finalize_routing_raw(const int8_t *x1, const uint8_t *x2, const float *scale,
+                                  const float *offset, const float *pertoken_scale,
+                                  const int64_t *group_list, int group_list_type,
+                                  const float *logit, const int64_t *row_index,
+                                  const uint16_t *shared_input, float shared_input_weight,
+                                  int64_t shared_input_offset, float *out, int64_t M, int64_t K,
+                                  int64_t N, int64_t E, int64_t batch, int64_t shared_rows,
+                                  void *stream, const gfr_options *opts);
 
 /* Static, NUL-terminated description of a gfr_status. */
 const char *gfr_status_string(int status);

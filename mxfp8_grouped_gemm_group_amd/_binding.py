@@ -35,11 +35,48 @@ class GfrOptions(ctypes.Structure):
                 ("split_k", ctypes.c_int), ("scale_per_expert", ctypes.c_int)]
 
 
+class GfrTensor(ctypes.Structure):
+    """gfr_tensor: device pointer, gfr_dtype, rank, extents."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4)]
+
+
+# torch dtype -> gfr_dtype (include/gfr.h)
+DTYPES = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1, torch.float4_e2m1fn_x2: 2,
+          torch.float8_e8m0fnu: 3, torch.uint8: 4, torch.bfloat16: 5, torch.float32: 6,
+          torch.int64: 7, torch.int32: 8, torch.int8: 9}
+
+
+def tensor_desc(t: Optional[torch.Tensor]):
+    """A gfr_tensor describing t (None for an absent optional tensor)."""
+    if t is None:
+        return None
+    _need(t.dtype in DTYPES, f"dtype {t.dtype} has no gfr_dtype")
+    _need(1 <= t.dim() <= 4, f"rank {t.dim()} is outside 1..4")
+    d = GfrTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i, n in enumerate(t.shape):
+        d.shape[i] = n
+    return d
+
+
+def _ref(d):
+    return None if d is None else ctypes.byref(d)
+
+
 _lib: Optional[ctypes.CDLL] = None
 
-_MAIN_ARGS = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [
-    ctypes.c_float, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [
-    ctypes.c_int64] * 6 + [ctypes.c_void_p]
+_P = ctypes.c_void_p
+_T = ctypes.POINTER(GfrTensor)
+_O = ctypes.POINTER(GfrOptions)
+_RAW_MAIN_ARGS = [_P] * 5 + [ctypes.c_int] + [_P] * 3 + [
+    ctypes.c_float, ctypes.c_int64, _P, ctypes.c_int, ctypes.c_int] + [ctypes.c_int64] * 6 + [_P]
+# descriptor finalize: x1 x2 scale pts group_list, type, logit row_index shared, weight,
+# offset, out, transpose, kind
+_DESC_MAIN_ARGS = [_T] * 5 + [ctypes.c_int] + [_T] * 3 + [ctypes.c_float, ctypes.c_int64, _T,
+                                                          ctypes.c_int, ctypes.c_int]
 
 
 def load_library() -> ctypes.CDLL:
@@ -50,21 +87,27 @@ def load_library() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "mxfp8_grouped_gemm_group_amd.build_lib.build()")
         lib = ctypes.CDLL(LIB_PATH)
-        lib.gmm_finalize_routing.argtypes = _MAIN_ARGS
-        lib.gmm_finalize_routing.restype = ctypes.c_int
-        lib.gmm_finalize_routing_ex.argtypes = _MAIN_ARGS + [ctypes.POINTER(GfrOptions)]
-        lib.gmm_finalize_routing_ex.restype = ctypes.c_int
-        lib.gfr_workspace_size.argtypes = [ctypes.c_int64] * 5 + [
-            ctypes.POINTER(GfrOptions), ctypes.POINTER(ctypes.c_size_t)]
-        lib.gfr_workspace_size.restype = ctypes.c_int
-        lib.gfr_gemm1_swiglu_quant.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [
-            ctypes.c_void_p] * 2 + [ctypes.c_int] * 3 + [ctypes.c_int64] * 4 + [
-            ctypes.c_void_p, ctypes.POINTER(GfrOptions)]
-        lib.gfr_gemm1_swiglu_quant.restype = ctypes.c_int
-        lib.gfr_w4a8_finalize_routing.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] + [
-            ctypes.c_void_p] * 3 + [ctypes.c_float, ctypes.c_int64, ctypes.c_void_p] + [
-            ctypes.c_int64] * 6 + [ctypes.c_void_p, ctypes.POINTER(GfrOptions)]
-        lib.gfr_w4a8_finalize_routing.restype = ctypes.c_int
+        lib.gmm_finalize_routing.argtypes = _DESC_MAIN_ARGS + [_P]
+        lib.gmm_finalize_routing_ex.argtypes = _DESC_MAIN_ARGS + [_P, _O]
+        lib.gfr_workspace_size.argtypes = _DESC_MAIN_ARGS + [_O, ctypes.POINTER(ctypes.c_size_t)]
+        lib.gfr_gemm1_swiglu_quant.argtypes = [_T] * 5 + [ctypes.c_int] + [_T] * 2 + [
+            ctypes.c_int, _P, _O]
+        lib.gfr_w4a8_finalize_routing.argtypes = [_T] * 6 + [ctypes.c_int] + [_T] * 3 + [
+            ctypes.c_float, ctypes.c_int64, _T, _P, _O]
+        lib.gmm_finalize_routing_raw.argtypes = _RAW_MAIN_ARGS
+        lib.gmm_finalize_routing_raw_ex.argtypes = _RAW_MAIN_ARGS + [_O]
+        lib.gfr_workspace_size_raw.argtypes = [ctypes.c_int64] * 5 + [
+            _O, ctypes.POINTER(ctypes.c_size_t)]
+        lib.gfr_gemm1_swiglu_quant_raw.argtypes = [_P] * 5 + [ctypes.c_int] + [_P] * 2 + [
+            ctypes.c_int] * 3 + [ctypes.c_int64] * 4 + [_P, _O]
+        lib.gfr_w4a8_finalize_routing_raw.argtypes = [_P] * 6 + [ctypes.c_int] + [_P] * 3 + [
+            ctypes.c_float, ctypes.c_int64, _P] + [ctypes.c_int64] * 6 + [_P, _O]
+        for name in ("gmm_finalize_routing", "gmm_finalize_routing_ex", "gfr_workspace_size",
+                     "gfr_gemm1_swiglu_quant", "gfr_w4a8_finalize_routing",
+                     "gmm_finalize_routing_raw", "gmm_finalize_routing_raw_ex",
+                     "gfr_workspace_size_raw", "gfr_gemm1_swiglu_quant_raw",
+                     "gfr_w4a8_finalize_routing_raw"):
+            getattr(lib, name).restype = ctypes.c_int
         lib.gfr_status_string.argtypes = [ctypes.c_int]
         lib.gfr_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -76,9 +119,11 @@ def status_string(code: int) -> str:
 
 
 def workspace_size(M: int, K: int, N: int, E: int, batch: int, deterministic: bool = False) -> int:
+    """Workspace bytes of a call of these sizes (gfr_workspace_size_raw)."""
     opts = GfrOptions(int(deterministic), None, 0, None, 0, 0)
     n = ctypes.c_size_t(0)
-    rc = load_library().gfr_workspace_size(M, K, N, E, batch, ctypes.byref(opts), ctypes.byref(n))
+    rc = load_library().gfr_workspace_size_raw(M, K, N, E, batch, ctypes.byref(opts),
+                                               ctypes.byref(n))
     if rc:
         raise GfrError(rc, status_string(rc))
     return n.value
@@ -93,6 +138,14 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _on_device(tensors, dev):
+    """Device and layout checks the descriptors cannot carry."""
+    for t in tensors:
+        if t is not None:
+            _need(t.is_cuda and t.device == dev, "all tensors must be on out's CUDA device")
+            _need(t.is_contiguous(), "all tensors must be contiguous")
+
+
 def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_type, logit,
                          row_index, shared_input, shared_input_weight, shared_input_offset,
                          out, transpose_x2=False, *, deterministic=False, workspace=None,
@@ -102,66 +155,39 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
     x1 [M,K] / x2 [E,K,N] (or [E,N,K] when transpose_x2) are float8_e4m3fn or
     float8_e5m2, or float4_e2m1fn_x2 (MXFP4: the last axis holds half as many
     bytes as elements); scale / pertoken_scale hold E8M0 codes (uint8 or
-    float8_e8m0fnu); a 4-D scale (leading expert axis) is per expert; group_list int64 [E]; logit float32 [M] or None;
-    row_index int64 [M]; shared_input bfloat16 [R,N] or None; out float32
-    [batch,N].  ``status`` (int32 CUDA tensor, 1 element) receives device-side
-    data-error bits.  ``workspace`` (uint8 CUDA tensor) is allocated here when
-    the deterministic mode needs one and none is given.
+    float8_e8m0fnu); a 4-D scale (leading expert axis) is per expert;
+    group_list int64 [E]; logit float32 [M] or None; row_index int64 or int32
+    [M]; shared_input bfloat16 [R,N] or None; out float32 [batch,N].
+    ``status`` (int32 CUDA tensor, 1 element) receives device-side data-error
+    bits.  ``workspace`` (uint8 CUDA tensor) is allocated here when the
+    deterministic mode needs one and none is given.  Dtypes, ranks and shapes
+    are checked by the library (gmm_finalize_routing_ex), which raises
+    GfrError here.
     """
     lib = load_library()
-    _need(x1.dtype in _FP8_KIND and x2.dtype == x1.dtype, "x1/x2 must share an FP8 / FP4 dtype")
-    _need(x1.dim() == 2 and x2.dim() == 3, "x1 must be 2-D and x2 3-D")
-    per = 2 if x1.dtype == _PACKED else 1     # elements per stored byte along the last axis
-    M, K = x1.shape[0], x1.shape[1] * per
-    E = x2.shape[0]
-    if transpose_x2:
-        N = x2.shape[1]
-        _need(x2.shape[2] * per == K, "x2 [E,N,K] does not match K")
-    else:
-        N = x2.shape[2] * per
-        _need(x2.shape[1] == K, "x2 [E,K,N] does not match K")
-    KB = (K + 63) // 64
-    _need(scale.dtype in _E8M0 and pertoken_scale.dtype in _E8M0, "scales must be E8M0 bytes")
-    s3 = (N, KB, 2) if transpose_x2 else (KB, N, 2)
-    per_expert = scale.dim() == 4
-    _need(tuple(scale.shape) == ((E,) + s3 if per_expert else s3),
-          "bad scale shape (3-D shared, or 4-D with a leading expert axis)")
-    _need(tuple(pertoken_scale.shape) == (M, KB, 2), "bad pertoken_scale shape")
-    _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
-    _need(row_index.dtype == torch.int64 and tuple(row_index.shape) == (M,), "bad row_index")
-    if logit is not None:
-        _need(logit.dtype == torch.float32 and tuple(logit.shape) == (M,), "bad logit")
-    _need(out.dtype == torch.float32 and out.dim() == 2 and out.shape[1] == N, "bad out")
-    batch = out.shape[0]
-    R = 0
-    if shared_input is not None:
-        _need(shared_input.dtype == torch.bfloat16 and shared_input.dim() == 2
-              and shared_input.shape[1] == N, "bad shared_input")
-        R = shared_input.shape[0]
-    tensors = [x1, x2, scale, pertoken_scale, group_list, row_index, out, logit, shared_input,
-               workspace, status]
     dev = out.device
-    for t in tensors:
-        if t is not None:
-            _need(t.is_cuda and t.device == dev, "all tensors must be on out's CUDA device")
-            _need(t.is_contiguous(), "all tensors must be contiguous")
+    _on_device([x1, x2, scale, pertoken_scale, group_list, row_index, out, logit, shared_input,
+                workspace, status], dev)
+    kind = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1, torch.float4_e2m1fn_x2: 2}.get(x1.dtype, -1)
+    descs = [tensor_desc(t) for t in (x1, x2, scale, pertoken_scale, group_list)]
+    lg, ri, sh, od = (tensor_desc(t) for t in (logit, row_index, shared_input, out))
+    args = [_ref(d) for d in descs] + [int(group_list_type), _ref(lg), _ref(ri), _ref(sh),
+                                       float(shared_input_weight), int(shared_input_offset),
+                                       _ref(od), int(bool(transpose_x2)), kind]
+    opts = GfrOptions(int(bool(deterministic)), None, 0, _ptr(status), int(split_k), 0)
+    if deterministic:
+        need = ctypes.c_size_t(0)
+        rc = lib.gfr_workspace_size(*args, ctypes.byref(opts), ctypes.byref(need))
+        if rc:
+            raise GfrError(rc, status_string(rc))
+        if workspace is None:
+            workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    ws_bytes = 0
-    if deterministic:
-        need = workspace_size(M, K, N, E, batch, True)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        ws_bytes = workspace.numel() * workspace.element_size()
-    opts = GfrOptions(int(bool(deterministic)), _ptr(workspace), ws_bytes, _ptr(status),
-                      int(split_k), int(per_expert))
     with torch.cuda.device(dev):
-        rc = lib.gmm_finalize_routing_ex(
-            _ptr(x1), _ptr(x2), _ptr(scale), _ptr(pertoken_scale), _ptr(group_list),
-            int(group_list_type), _ptr(logit), _ptr(row_index), _ptr(shared_input),
-            float(shared_input_weight), int(shared_input_offset), _ptr(out),
-            int(bool(transpose_x2)), _FP8_KIND[x1.dtype], M, K, N, E, batch, R,
-            ctypes.c_void_p(stream), ctypes.byref(opts))
+        rc = lib.gmm_finalize_routing_ex(*args, ctypes.c_void_p(stream), ctypes.byref(opts))
     if rc:
         raise GfrError(rc, status_string(rc))
     return out
@@ -181,48 +207,26 @@ def gemm1_swiglu_quant(xin, w13, scale, xin_scale, group_list, group_list_type,
     pertoken_scale.  Rows of tokens in no expert's range are left as they were
     in x1_out / x1_scale_out (zeros when the call allocates them)."""
     lib = load_library()
-    _need(xin.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) and w13.dtype == xin.dtype,
-          "xin/w13 must share an FP8 dtype")
-    _need(out_dtype in (torch.float8_e4m3fn, torch.float8_e5m2), "out_dtype must be FP8")
-    _need(xin.dim() == 2 and w13.dim() == 3, "xin must be 2-D and w13 3-D")
-    M, H = xin.shape
-    E = w13.shape[0]
-    if transpose_w13:
-        _need(w13.shape[2] == H, "w13 [E,2I,H] does not match H")
-        N2 = w13.shape[1]
-    else:
-        _need(w13.shape[1] == H, "w13 [E,H,2I] does not match H")
-        N2 = w13.shape[2]
-    _need(N2 % 2 == 0, "w13 must have an even number (2I) of columns")
-    I = N2 // 2
-    KB = (H + 63) // 64
-    s3 = (N2, KB, 2) if transpose_w13 else (KB, N2, 2)
-    _need(scale.dtype in _E8M0 and xin_scale.dtype in _E8M0, "scales must be E8M0 bytes")
-    per_expert = scale.dim() == 4
-    _need(tuple(scale.shape) == ((E,) + s3 if per_expert else s3), "bad scale shape")
-    _need(tuple(xin_scale.shape) == (M, KB, 2), "bad xin_scale shape")
-    _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
     dev = xin.device
+    _need(xin.dim() == 2 and w13.dim() == 3, "xin must be 2-D and w13 3-D")
+    M = xin.shape[0]
+    N2 = w13.shape[1] if transpose_w13 else w13.shape[2]
+    I = N2 // 2
     if x1_out is None:
         x1_out = torch.zeros((M, I), dtype=torch.uint8, device=dev).view(out_dtype)
     if x1_scale_out is None:
         x1_scale_out = torch.zeros((M, (I + 63) // 64, 2), dtype=torch.uint8, device=dev)
-    _need(x1_out.dtype == out_dtype and tuple(x1_out.shape) == (M, I), "bad x1_out")
-    _need(x1_scale_out.dtype in _E8M0 and tuple(x1_scale_out.shape) == (M, (I + 63) // 64, 2),
-          "bad x1_scale_out")
-    for t in (xin, w13, scale, xin_scale, group_list, x1_out, x1_scale_out, status):
-        if t is not None:
-            _need(t.is_cuda and t.device == dev, "all tensors must be on xin's CUDA device")
-            _need(t.is_contiguous(), "all tensors must be contiguous")
+    _need(x1_out.dtype == out_dtype, "x1_out must have out_dtype")
+    _on_device([xin, w13, scale, xin_scale, group_list, x1_out, x1_scale_out, status], dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    opts = GfrOptions(0, None, 0, _ptr(status), 0, int(per_expert))
+    opts = GfrOptions(0, None, 0, _ptr(status), 0, 0)
+    d = [tensor_desc(t) for t in (xin, w13, scale, xin_scale, group_list)]
+    dq, dqs = tensor_desc(x1_out), tensor_desc(x1_scale_out)
     with torch.cuda.device(dev):
         rc = lib.gfr_gemm1_swiglu_quant(
-            _ptr(xin), _ptr(w13), _ptr(scale), _ptr(xin_scale), _ptr(group_list),
-            int(group_list_type), _ptr(x1_out), _ptr(x1_scale_out), int(bool(transpose_w13)),
-            _FP8_KIND[xin.dtype], _FP8_KIND[out_dtype], M, H, I, E, ctypes.c_void_p(stream),
-            ctypes.byref(opts))
+            *[_ref(x) for x in d], int(group_list_type), _ref(dq), _ref(dqs),
+            int(bool(transpose_w13)), ctypes.c_void_p(stream), ctypes.byref(opts))
     if rc:
         raise GfrError(rc, status_string(rc))
     return x1_out, x1_scale_out
@@ -238,50 +242,28 @@ def w4a8_finalize_routing(x1, x2, scale, offset, pertoken_scale, group_list, gro
     [E, 1, N]; pertoken_scale float32 [M]; the rest as gmm_finalize_routing.
     Updates out in place and returns it."""
     lib = load_library()
-    _need(x1.dtype == torch.int8 and x1.dim() == 2, "x1 must be int8 [M, K]")
-    _need(x2.dtype == torch.uint8 and x2.dim() == 3, "x2 must be uint8 [E, K, N/2]")
-    M, K = x1.shape
-    E = x2.shape[0]
-    _need(x2.shape[1] == K, "x2 [E, K, N/2] does not match K")
-    N = 2 * x2.shape[2]
-    _need(scale.dtype == torch.float32 and tuple(scale.shape) == (E, 1, N), "bad scale")
-    _need(offset is None or (offset.dtype == torch.float32 and tuple(offset.shape) == (E, 1, N)),
-          "bad offset")
-    _need(pertoken_scale.dtype == torch.float32 and tuple(pertoken_scale.shape) == (M,),
-          "bad pertoken_scale")
-    _need(group_list.dtype == torch.int64 and tuple(group_list.shape) == (E,), "bad group_list")
-    _need(row_index.dtype == torch.int64 and tuple(row_index.shape) == (M,), "bad row_index")
-    if logit is not None:
-        _need(logit.dtype == torch.float32 and tuple(logit.shape) == (M,), "bad logit")
-    _need(out.dtype == torch.float32 and out.dim() == 2 and out.shape[1] == N, "bad out")
-    batch = out.shape[0]
-    R = 0
-    if shared_input is not None:
-        _need(shared_input.dtype == torch.bfloat16 and shared_input.dim() == 2
-              and shared_input.shape[1] == N, "bad shared_input")
-        R = shared_input.shape[0]
     dev = out.device
-    for t in (x1, x2, scale, offset, pertoken_scale, group_list, row_index, out, logit,
-              shared_input, workspace, status):
-        if t is not None:
-            _need(t.is_cuda and t.device == dev, "all tensors must be on out's CUDA device")
-            _need(t.is_contiguous(), "all tensors must be contiguous")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    _on_device([x1, x2, scale, offset, pertoken_scale, group_list, row_index, out, logit,
+                shared_input, workspace, status], dev)
+    _need(x1.dim() == 2 and x2.dim() == 3 and out.dim() == 2, "x1 [M, K], x2 [E, K, N/2], out 2-D")
     ws_bytes = 0
     if deterministic:
-        need = workspace_size(M, K, N, E, batch, True)
+        M, K, E, N = x1.shape[0], x1.shape[1], x2.shape[0], 2 * x2.shape[2]
+        need = workspace_size(M, K, N, E, out.shape[0], True)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
     opts = GfrOptions(int(bool(deterministic)), _ptr(workspace), ws_bytes, _ptr(status),
                       int(split_k), 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    d = [tensor_desc(t) for t in (x1, x2, scale, offset, pertoken_scale, group_list)]
+    lg, ri, sh, od = (tensor_desc(t) for t in (logit, row_index, shared_input, out))
     with torch.cuda.device(dev):
         rc = lib.gfr_w4a8_finalize_routing(
-            _ptr(x1), _ptr(x2), _ptr(scale), _ptr(offset), _ptr(pertoken_scale),
-            _ptr(group_list), int(group_list_type), _ptr(logit), _ptr(row_index),
-            _ptr(shared_input), float(shared_input_weight), int(shared_input_offset), _ptr(out),
-            M, K, N, E, batch, R, ctypes.c_void_p(stream), ctypes.byref(opts))
+            *[_ref(x) for x in d], int(group_list_type), _ref(lg), _ref(ri), _ref(sh),
+            float(shared_input_weight), int(shared_input_offset), _ref(od),
+            ctypes.c_void_p(stream), ctypes.byref(opts))
     if rc:
         raise GfrError(rc, status_string(rc))
     return out

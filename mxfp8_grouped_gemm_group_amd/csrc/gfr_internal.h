@@ -30,7 +30,8 @@ struct FusedParams {
     const uint8_t *pts;
     const int64_t *group_list;
     const float *logit;        // may be null (weight 1)
-    const int64_t *row_index;
+    const void *row_index;     // int64 [M], or int32 [M] when row_index_i32
+    int32_t row_index_i32;
     const uint16_t *shared;    // may be null
     float shared_w;
     int32_t shared_off;

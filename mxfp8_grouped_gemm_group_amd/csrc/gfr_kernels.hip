@@ -297,9 +297,9 @@ __device__ __forceinline__ int find_expert(const int *pref, int E, int q) {
 //   scales: the E8M0 of 32-block b of row (column) c comes from lane c + 32b,
 //          so lane (c, g) supplies block g.
 //   D: 16 floats; element r is row 8(r/4) + 4g + r%4, column c.
-// Column c of MFMA j maps to output column n0 + 4c + j for the [K, N] layout
-// (each lane loads 4 adjacent columns and transposes them in registers) and
-// n0 + 32j + c for the [N, K] layout.
+// Column c of MFMA j maps to output column n0 + 32j + c in both layouts: the
+// [K, N] tile's operands come out of LDS K-contiguous per column through
+// transpose reads, the [N, K] tile's through plain 16-byte reads.
 // ---------------------------------------------------------------------------
 
 // s_waitcnt vmcnt(N) (other counters untouched), gfx9 encoding.
@@ -490,8 +490,16 @@ __device__ __forceinline__ RowInfo load_row_info(const FusedParams &p, int m0, i
     constexpr int kRows = kTileM * RF;
     RowInfo ri{v2i{0, 0}, 0.0f, lane < kRows && lane < mcount};
     const int cnt = mcount < kRows ? (mcount > 0 ? mcount : 0) : kRows;
-    const rsrc_t rr = make_rsrc(p.row_index + m0, static_cast<int64_t>(cnt) * 8);
-    ri.dst = __builtin_amdgcn_raw_buffer_load_b64(rr, 8 * lane, 0, 0);
+    if (p.row_index_i32) {   // sign-extended to the two-dword form
+        const rsrc_t rr = make_rsrc(static_cast<const int32_t *>(p.row_index) + m0,
+                                    static_cast<int64_t>(cnt) * 4);
+        const int v = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rr, 4 * lane, 0, 0));
+        ri.dst = v2i{v, v >> 31};
+    } else {
+        const rsrc_t rr = make_rsrc(static_cast<const int64_t *>(p.row_index) + m0,
+                                    static_cast<int64_t>(cnt) * 8);
+        ri.dst = __builtin_amdgcn_raw_buffer_load_b64(rr, 8 * lane, 0, 0);
+    }
     if (p.logit) {
         const rsrc_t rl = make_rsrc(p.logit + m0, static_cast<int64_t>(cnt) * 4);
         ri.w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lane, 0, 0));
@@ -1606,10 +1614,16 @@ __global__ __launch_bounds__(kBlockThreads, 1) void gemm1_swiglu_kernel(FusedPar
 // Deterministic mode: CSR of row_index, then a fixed-order reduction
 //   out[b] = ((init + W[t_1]) + W[t_2]) + ... + shared,  t_1 < t_2 < ...
 // ---------------------------------------------------------------------------
+// Destination row of token t (int64 or int32 row_index).
+__device__ __forceinline__ int64_t row_of(const FusedParams &p, int t) {
+    return p.row_index_i32 ? static_cast<int64_t>(static_cast<const int32_t *>(p.row_index)[t])
+                           : static_cast<const int64_t *>(p.row_index)[t];
+}
+
 __global__ void det_count_kernel(FusedParams p, int *counts) {
     const int T = *p.det_total;
     for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
-        const int64_t b = p.row_index[t];
+        const int64_t b = row_of(p, t);
         if (b >= 0 && b < p.batch) atomicAdd(counts + b, 1);
     }
 }
@@ -1638,7 +1652,7 @@ __global__ void det_scan_kernel(FusedParams p, const int *counts, int *offsets, 
 __global__ void det_fill_kernel(FusedParams p, int *cursor, int *tokens) {
     const int T = *p.det_total;
     for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
-        const int64_t b = p.row_index[t];
+        const int64_t b = row_of(p, t);
         if (b >= 0 && b < p.batch) tokens[atomicAdd(cursor + b, 1)] = t;
     }
 }

@@ -75,7 +75,9 @@ enum gfr_status {
     GFR_ERR_HIP = 8,             /* a HIP runtime call failed */
     GFR_ERR_BAD_DTYPE = 9,       /* a descriptor's dtype is not one its argument takes,
                                     or x1 / x2 do not match fp8_kind */
-    GFR_ERR_BAD_RANK = 10        /* a descriptor's ndim is not its argument's rank */
+    GFR_ERR_BAD_RANK = 10,       /* a descriptor's ndim is not its argument's rank */
+    GFR_ERR_SCRATCH_TOO_SMALL = 11  /* the allocation-free call needs more than
+                                       GFR_STATIC_SCRATCH_BYTES of scratch */
 };
 
 /* Element types of a gfr_tensor.  Packed types hold two 4-bit elements per
@@ -123,6 +125,8 @@ enum gfr_group_list_type { GFR_GROUP_LIST_CUMSUM = 0, GFR_GROUP_LIST_COUNT = 1 }
 
 /* Limits of this implementation. */
 #define GFR_MAX_EXPERTS 1024       /* [P3] Atlas 350 notes: e <= 1024 */
+/* Static device scratch per GPU of gmm_finalize_routing_det_noalloc. */
+#define GFR_STATIC_SCRATCH_BYTES (64u << 20)
 
 typedef struct gfr_options {
     /* 0: scatter-add with FP32 atomics (default).  1: deterministic — the
@@ -316,6 +320,36 @@ int gfr_w4a8_finalize_routing(const gfr_tensor *x1, const gfr_tensor *x2, const 
                               const gfr_tensor *shared_input, float shared_input_weight,
                               int64_t shared_input_offset, const gfr_tensor *out, void *stream,
                               const gfr_options *opts);
+
+/*
+ * gmm_finalize_routing_det_noalloc — gmm_finalize_routing_ex in deterministic
+ * mode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Its
+ * workspace (the weighted rows W [M, N] float32 and the CSR of row_index,
+ * gfr_workspace_size bytes) is a static device array of
+ * GFR_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends; the call allocates and frees nothing.
+ *
+ *  Arguments as gmm_finalize_routing; status_dev as gfr_options.status_dev
+ *  (may be NULL).  The result is the deterministic mode's: bitwise equal to
+ *  gmm_finalize_routing_ex with opts.deterministic = 1.
+ *
+ * GFR_ERR_SCRATCH_TOO_SMALL when the call needs more than
+ * GFR_STATIC_SCRATCH_BYTES (4 * M * N bytes plus 4 * (3 * batch + 2 * M) for the
+ * CSR, each rounded up to 256: about M * N <= 16.7 M), with nothing enqueued;
+ * the other errors as gmm_finalize_routing_ex.  Every call on one GPU uses that
+ * GPU's one array and leaves its contents behind (what must start at zero is
+ * cleared by each call on its stream): calls that overlap in time on one GPU
+ * race, so the caller orders them (one stream, or events between streams).
+ */
+int gmm_finalize_routing_det_noalloc(const gfr_tensor *x1, const gfr_tensor *x2,
+                                     const gfr_tensor *scale, const gfr_tensor *pertoken_scale,
+                                     const gfr_tensor *group_list, int group_list_type,
+                                     const gfr_tensor *logit, const gfr_tensor *row_index,
+                                     const gfr_tensor *shared_input, float shared_input_weight,
+                                     int64_t shared_input_offset, const gfr_tensor *out,
+                                     int transpose_x2, int fp8_kind, void *stream,
+                                     int32_t *status_dev);
 
 /* ======================================================================== *
  * Raw calls: device pointers plus sizes, semantics as the descriptor calls *

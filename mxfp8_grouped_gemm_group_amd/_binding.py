@@ -94,6 +94,7 @@ def load_library() -> ctypes.CDLL:
             ctypes.c_int, _P, _O]
         lib.gfr_w4a8_finalize_routing.argtypes = [_T] * 6 + [ctypes.c_int] + [_T] * 3 + [
             ctypes.c_float, ctypes.c_int64, _T, _P, _O]
+        lib.gmm_finalize_routing_det_noalloc.argtypes = _DESC_MAIN_ARGS + [_P, _P]
         lib.gmm_finalize_routing_raw.argtypes = _RAW_MAIN_ARGS
         lib.gmm_finalize_routing_raw_ex.argtypes = _RAW_MAIN_ARGS + [_O]
         lib.gfr_workspace_size_raw.argtypes = [ctypes.c_int64] * 5 + [
@@ -103,6 +104,7 @@ def load_library() -> ctypes.CDLL:
         lib.gfr_w4a8_finalize_routing_raw.argtypes = [_P] * 6 + [ctypes.c_int] + [_P] * 3 + [
             ctypes.c_float, ctypes.c_int64, _P] + [ctypes.c_int64] * 6 + [_P, _O]
         for name in ("gmm_finalize_routing", "gmm_finalize_routing_ex", "gfr_workspace_size",
+                     "gmm_finalize_routing_det_noalloc",
                      "gfr_gemm1_swiglu_quant", "gfr_w4a8_finalize_routing",
                      "gmm_finalize_routing_raw", "gmm_finalize_routing_raw_ex",
                      "gfr_workspace_size_raw", "gfr_gemm1_swiglu_quant_raw",
@@ -188,6 +190,34 @@ def gmm_finalize_routing(x1, x2, scale, pertoken_scale, group_list, group_list_t
         stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         rc = lib.gmm_finalize_routing_ex(*args, ctypes.c_void_p(stream), ctypes.byref(opts))
+    if rc:
+        raise GfrError(rc, status_string(rc))
+    return out
+
+
+def gmm_finalize_routing_det_noalloc(x1, x2, scale, pertoken_scale, group_list,
+                                     group_list_type, logit, row_index, shared_input,
+                                     shared_input_weight, shared_input_offset, out,
+                                     transpose_x2=False, *, status=None, stream=None):
+    """Deterministic gmm_finalize_routing whose workspace is the library's
+    static per-GPU scratch (include/gfr.h, gmm_finalize_routing_det_noalloc):
+    allocates nothing, so it may run where allocation is not allowed.  Calls
+    that overlap in time on one GPU race on that scratch.  Arguments as
+    gmm_finalize_routing; returns out."""
+    lib = load_library()
+    dev = out.device
+    _on_device([x1, x2, scale, pertoken_scale, group_list, row_index, out, logit, shared_input,
+                status], dev)
+    kind = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1, torch.float4_e2m1fn_x2: 2}.get(x1.dtype, -1)
+    descs = [tensor_desc(t) for t in (x1, x2, scale, pertoken_scale, group_list)]
+    lg, ri, sh, od = (tensor_desc(t) for t in (logit, row_index, shared_input, out))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = lib.gmm_finalize_routing_det_noalloc(
+            *[_ref(d) for d in descs], int(group_list_type), _ref(lg), _ref(ri), _ref(sh),
+            float(shared_input_weight), int(shared_input_offset), _ref(od),
+            int(bool(transpose_x2)), kind, ctypes.c_void_p(stream), _ptr(status))
     if rc:
         raise GfrError(rc, status_string(rc))
     return out

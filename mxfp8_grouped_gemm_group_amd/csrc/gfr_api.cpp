@@ -366,6 +366,7 @@ const char *gfr_status_string(int status) {
     case GFR_ERR_HIP: return "HIP runtime error";
     case GFR_ERR_BAD_DTYPE: return "a tensor's dtype is not one its argument takes (or x1 / x2 do not match fp8_kind)";
     case GFR_ERR_BAD_RANK: return "a tensor's rank is not its argument's";
+    case GFR_ERR_SCRATCH_TOO_SMALL: return "the call needs more than the library's static scratch (GFR_STATIC_SCRATCH_BYTES per GPU); use gmm_finalize_routing_ex with a workspace";
     default: return "unknown status";
     }
 }
@@ -532,6 +533,46 @@ int gfr_workspace_size(const gfr_tensor *x1, const gfr_tensor *x2, const gfr_ten
                      fp8_kind, d.M, d.K, d.N, d.E, d.batch, d.R));
     *bytes = (opts && opts->deterministic) ? gfr::det_layout(d.M, d.N, d.batch).total : 0;
     return GFR_OK;
+}
+
+int gmm_finalize_routing_det_noalloc(const gfr_tensor *x1, const gfr_tensor *x2,
+                                     const gfr_tensor *scale, const gfr_tensor *pertoken_scale,
+                                     const gfr_tensor *group_list, int group_list_type,
+                                     const gfr_tensor *logit, const gfr_tensor *row_index,
+                                     const gfr_tensor *shared_input, float shared_input_weight,
+                                     int64_t shared_input_offset, const gfr_tensor *out,
+                                     int transpose_x2, int fp8_kind, void *stream,
+                                     int32_t *status_dev) {
+    Dims d;
+    GFR_TRY(resolve_finalize(x1, x2, scale, pertoken_scale, group_list, logit, row_index,
+                             shared_input, out, transpose_x2, fp8_kind, nullptr, d));
+    const uint16_t *shared =
+        present(shared_input) ? static_cast<const uint16_t *>(shared_input->data) : nullptr;
+    GFR_TRY(validate(x1->data, x2->data, static_cast<const uint8_t *>(scale->data),
+                     static_cast<const uint8_t *>(pertoken_scale->data),
+                     static_cast<const int64_t *>(group_list->data), group_list_type,
+                     row_index->data, shared, shared_input_offset,
+                     static_cast<const float *>(out->data), transpose_x2, fp8_kind, d.M, d.K,
+                     d.N, d.E, d.batch, d.R));
+    if (d.N == 0 || d.batch == 0) return GFR_OK;   // empty output: nothing to do
+    if (gfr::det_layout(d.M, d.N, d.batch).total > GFR_STATIC_SCRATCH_BYTES)
+        return GFR_ERR_SCRATCH_TOO_SMALL;
+    void *ws = nullptr;
+    if (gfr::static_scratch(&ws) != hipSuccess) return GFR_ERR_HIP;
+    gfr_options o{};
+    o.deterministic = 1;
+    o.workspace = ws;
+    o.workspace_bytes = GFR_STATIC_SCRATCH_BYTES;
+    o.status_dev = status_dev;
+    o.scale_per_expert = d.per_expert;
+    return finalize_impl(
+        x1->data, x2->data, static_cast<const uint8_t *>(scale->data),
+        static_cast<const uint8_t *>(pertoken_scale->data),
+        static_cast<const int64_t *>(group_list->data), group_list_type,
+        present(logit) ? static_cast<const float *>(logit->data) : nullptr, row_index->data,
+        d.ri32, shared, shared_input_weight, shared_input_offset,
+        static_cast<float *>(out->data), transpose_x2, fp8_kind, d.M, d.K, d.N, d.E, d.batch,
+        d.R, stream, &o);
 }
 
 int gfr_w4a8_finalize_routing(const gfr_tensor *x1, const gfr_tensor *x2, const gfr_tensor *scale,

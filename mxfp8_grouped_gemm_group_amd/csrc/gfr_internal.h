@@ -72,6 +72,11 @@ struct DetLayout {
 };
 DetLayout det_layout(int64_t M, int64_t N, int64_t batch);
 
+// Device address of the library's static scratch array on the current device
+// (GFR_STATIC_SCRATCH_BYTES bytes, 256-byte aligned), looked up once per
+// device with hipGetSymbolAddress; allocates nothing.
+hipError_t static_scratch(void **ptr);
+
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_fused(const FusedParams &p, int transpose_x2, int fp8_kind,
                         hipStream_t stream);

@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1782,6 +1783,32 @@ hipError_t launch_gemm1_t(const FusedParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free deterministic entry point: the deterministic
+// mode's workspace (weighted rows and the row_index CSR) for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it.  In host code the name is
+// only a handle for hipGetSymbolAddress: kernels get the address it returns.
+static __device__ __align__(256) unsigned char scratch[GFR_STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 DetLayout det_layout(int64_t M, int64_t N, int64_t batch) {
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };

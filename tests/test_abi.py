@@ -32,13 +32,14 @@ def test_library_exports_every_declared_function():
     assert {"gmm_finalize_routing", "gmm_finalize_routing_ex", "gfr_workspace_size",
             "gfr_status_string", "gfr_gemm1_swiglu_quant", "gfr_w4a8_finalize_routing",
             "gmm_finalize_routing_raw", "gmm_finalize_routing_raw_ex", "gfr_workspace_size_raw",
-            "gfr_gemm1_swiglu_quant_raw", "gfr_w4a8_finalize_routing_raw"} <= names
+            "gfr_gemm1_swiglu_quant_raw", "gfr_w4a8_finalize_routing_raw",
+            "gmm_finalize_routing_det_noalloc"} <= names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings():
-    for code in range(0, 11):
+    for code in range(0, 12):
         assert gfr.status_string(code) != "unknown status"
     assert gfr.status_string(0) == "ok"
     assert gfr.status_string(999) == "unknown status"
@@ -345,3 +346,17 @@ def _gemm1_descs(**over):
 ])
 def test_gemm1_descriptor_validation(over, code):
     assert gfr.load_library().gfr_gemm1_swiglu_quant(*_gemm1_descs(**over), None, None) == code
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """c5's weighted rows (16384 x 4096 float32 = 256 MiB) exceed the static
+    scratch: rejected on the host, nothing launched."""
+    lib = gfr.load_library()
+    M, K, N, E, B = 16384, 7168, 4096, 256, 2048
+    d = _c3_descs(x1=D(E5M2, M, K), x2=D(E5M2, E, N, K), scale=D(E8M0, N, K // 64, 2),
+                  pts=D(U8, M, K // 64, 2), gl=D(I64, E), logit=D(F32, M), ri=D(I64, M),
+                  shared=D(BF16, B, N), out=D(F32, B, N), trans=1, kind=1)
+    assert lib.gmm_finalize_routing_det_noalloc(*_args(d), None, None) == 11
+    # validation comes first, as in the other calls
+    assert lib.gmm_finalize_routing_det_noalloc(*_args(_c3_descs(gl=D(I64, 3))), None, None) == 2
+    assert gfr.status_string(11) != "unknown status"

@@ -34,9 +34,10 @@ int check_sizes(int64_t M, int64_t K, int64_t N, int64_t E, int64_t batch) {
     if (E > GFR_MAX_EXPERTS) return GFR_ERR_UNSUPPORTED;
     if (M > kMaxRows || batch > kMaxRows || K > kMaxRows || N > kMaxRows) return GFR_ERR_UNSUPPORTED;
     if (K % 128 != 0 || N % 16 != 0) return GFR_ERR_UNSUPPORTED;
-    // One expert's weight slice and the weight-scale tensor are addressed with
-    // 32-bit buffer offsets.
-    if (K * N > kMaxRows || M * K > int64_t{1} << 40) return GFR_ERR_UNSUPPORTED;
+    // One expert's weight slice (and, for [N, K] weights, a 128-column tile
+    // past its end) and the weight-scale tensor are addressed with 32-bit
+    // buffer offsets.
+    if (K * (N + 128) > kMaxRows || M * K > int64_t{1} << 40) return GFR_ERR_UNSUPPORTED;
     // Work-item count (one K split, the narrower of the two layouts' column
     // tiles) must fit an int32.
     const int64_t n_tiles = (N + gfr::kTileNNK - 1) / gfr::kTileNNK;

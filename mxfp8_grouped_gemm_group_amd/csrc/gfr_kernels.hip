@@ -134,8 +134,9 @@ constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 constexpr int kCoopBand = 2;
 
 template <bool WIDE>
-__device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles, WorkList &wl,
-                                int64_t *s_scan) {
+__device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles,
+                                                int n_tiles_coop, WorkList &wl,
+                                                int64_t *s_scan) {
     const int tid = threadIdx.x;
     static_assert(kPerThread == 4, "one thread reads 4 consecutive group_list entries");
     // All loads are issued before any is used (one memory latency, not one per
@@ -187,7 +188,7 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         run += c[i];
         const int64_t si = cnt >= kCoopMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
         const int gr = coop_group_rows<WIDE>(cnt);
-        const int64_t li = cnt >= kCoopMinRows ? ((cnt + gr - 1) / gr) * n_tiles : 0;
+        const int64_t li = cnt >= kCoopMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
         items[i] = si | (li << 32);
         isum += items[i];
     }
@@ -821,12 +822,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // instruction), into a per-wave ring after the block's weight ring; the
     // 16-byte chunks of row r are XOR-swizzled by (r >> 1) & 3 and the
     // operands come out with ds_read_b128, one step ahead, like the weights.
-    // FP8 [N, K] cooperative units stage the first 64 bytes of each row's
-    // 128-byte step the same way (whole steps would need 128 KB of x1 slots);
-    // the second 64 bytes stay register loads (kXLH).  One-fragment units
-    // (32 rows per wave, 8-slot weight ring) do the same with 2 KB slots.
-    constexpr bool kXLH = !KN && COOP && !FP4 && !I8 && OP == 0;
-    constexpr bool kXL = (KN && COOP && !FP4 && !I8 && OP == 0) || kXLH;
+    // One-fragment units (32 rows per wave, 8-slot weight ring) do the same
+    // with 2 KB slots.  (FP8 [N, K] units of the finalize operator are
+    // ck_unit / cw_item below.)
+    constexpr bool kXL = KN && COOP && !FP4 && !I8 && OP == 0;
     constexpr int kXLoads = 2 * RF;                       // 16-row x1 loads per step
     constexpr int kXSlotBytes = RF * kTileM * kStepK;     // 32 or 64 rows x 64 bytes
     char *const xring = ring + D * kSlotBytes + w * D * kXSlotBytes;
@@ -1053,19 +1052,11 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
         if constexpr (kXL) {
-            static_assert(!kXL || RF * kAL == (kXLH ? 2 : 1) * kXLoads,
-                          "as many x1 loads per step as in registers");
+            static_assert(!kXL || RF * kAL == kXLoads, "as many x1 loads per step as in registers");
 #pragma unroll
             for (int u = 0; u < kXLoads; ++u) {
                 lds_void_t *dst = (lds_void_t *)(xring + slot * kXSlotBytes + u * 1024);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vx[u], k0, 0, 0);
-            }
-            if constexpr (kXLH) {   // the step's second 64 bytes: registers
-#pragma unroll
-                for (int f = 0; f < RF; ++f)
-#pragma unroll
-                    for (int q = 2; q < 4; ++q)
-                        r.a[f][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[f], k0 + 32 * q, 0);
             }
         } else {
 #pragma unroll
@@ -1245,9 +1236,6 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     v8i a = on ? cat(r.a[f][2 * s2], r.a[f][2 * s2 + 1]) : v8i{};
-                    if constexpr (kXLH) {   // the first 64-K half came through LDS
-                        if (s2 == 0) a = on ? cat(ax[2 * f], ax[2 * f + 1]) : v8i{};
-                    }
                     const int shf = 8 * (2 * s2 + g);
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
@@ -1362,6 +1350,456 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
 
+// ---------------------------------------------------------------------------
+// Cooperative unit for FP8 [N, K] weights (finalize operator): RF x 128 rows
+// of one expert (wave w: rows [32 RF w, 32 RF (w + 1)) of the group) x 128
+// columns, in K steps of 128.  Every operand is staged through LDS with
+// direct-to-LDS loads of whole 128-byte lines -- one load covers 8 rows (or
+// columns) x 128 B, so each line is requested once per step -- where a
+// register gather of the MFMA layout touches 32 rows x 32 B per load, and a
+// 64-K step leaves every line to be requested twice.  A stage holds the
+// step's 128 weight columns (16 KB) and the four waves' x1 rows (RF x 32 x
+// 128 B each); both use the [N, K] wave items' slot layout (128-byte rows,
+// 16-byte chunks XOR-swizzled by (row >> 1) & 7) and operand reads.  Two
+// stages: a step's loads are issued right after the barrier that frees its
+// stage, before the previous step's 16 (RF 2) MFMAs, which cover their
+// latency.  Scales: one 16-byte load per x1 row and weight column per four
+// steps (WS), or per-step dwords for shorter K ranges.
+// ---------------------------------------------------------------------------
+constexpr int kCkStages = 2;
+constexpr int kCkWSlot = kTileN * kStepKNK;   // 16 KB: 128 columns x 128 K
+
+// Operand reads of one 64-K half s of a step, reads h = 0, 1 (logical chunk
+// 4s + 2h + g of row c: bytes 32 h + 16 g of the half), issued without
+// waiting: t[2j + h] = weight column group j (columns 32j..), t[8 + 2f + h]
+// = x1 fragment f (rows 32f..); wa* / xa* = slot base + the lane's row
+// offset for h = 0, 1.
+template <int NT>
+__device__ __forceinline__ void lds_issue_w8(uint32_t wa0, uint32_t wa1, v4i (&t)[NT]) {
+    static_assert(32 * kStepKNK == 4096 && NT >= 8, "group stride; eight reads");
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %8 offset:4096\n\t"
+        "ds_read_b128 %3, %9 offset:4096\n\t"
+        "ds_read_b128 %4, %8 offset:8192\n\t"
+        "ds_read_b128 %5, %9 offset:8192\n\t"
+        "ds_read_b128 %6, %8 offset:12288\n\t"
+        "ds_read_b128 %7, %9 offset:12288"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+          "=&v"(t[6]), "=&v"(t[7])
+        : "v"(wa0), "v"(wa1)
+        : "memory");
+}
+
+template <int RF>
+__device__ __forceinline__ void lds_issue_ck(uint32_t wa0, uint32_t wa1, uint32_t xa0,
+                                             uint32_t xa1, v4i (&t)[8 + 2 * RF]) {
+    lds_issue_w8(wa0, wa1, t);
+    if constexpr (RF == 2)
+        asm volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %5\n\t"
+            "ds_read_b128 %2, %4 offset:4096\n\t"
+            "ds_read_b128 %3, %5 offset:4096"
+            : "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11])
+            : "v"(xa0), "v"(xa1)
+            : "memory");
+    else
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %3"
+            : "=&v"(t[8]), "=&v"(t[9])
+            : "v"(xa0), "v"(xa1)
+            : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_all(v4i (&t)[N]) {
+    static_assert(N == 8 || N == 10 || N == 12, "operand buffer of one half step");
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                       "+v"(t[6]), "+v"(t[7])
+                     :
+                     : "memory");
+    else if constexpr (N == 12)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                       "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11])
+                     :
+                     : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]),
+                       "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9])
+                     :
+                     : "memory");
+}
+
+template <int FMT, int RF, bool WS>
+__device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int mcount, int n0,
+                                        int ks0, int ks1, bool store_rows, char *ring, int w) {
+    constexpr int D = kCkStages;
+    constexpr int kXSlot = RF * kTileM * kStepKNK;                // one wave's x1 per step
+    constexpr int kStage = kCkWSlot + kWavesPerBlock * kXSlot;    // 48 KB (RF 2), 32 KB (RF 1)
+    static_assert(D * kStage <= kWavesPerBlock * kRingBytes, "stages fit the block's LDS ring");
+    constexpr int kWLd = kCkWSlot / 1024 / kWavesPerBlock;        // weight loads per wave: 4
+    constexpr int kXLd = kXSlot / 1024;                           // x1 loads per wave: 4 RF
+    constexpr int kNH = 8 + 2 * RF;                               // operand reads per half step
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    mcount = __builtin_amdgcn_readfirstlane(mcount);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    ks0 = __builtin_amdgcn_readfirstlane(ks0);
+    ks1 = __builtin_amdgcn_readfirstlane(ks1);
+    w = __builtin_amdgcn_readfirstlane(w);
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+    const int K = p.K, N = p.N, KS = p.K / 32;
+    if (mcount < 0) mcount = 0;
+    // x1 rows of this wave (rows past the expert's last token read as zero
+    // through the range-checked descriptor), the expert's weights, the scales
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
+    const int64_t wbytes = static_cast<int64_t>(N) * K;
+    const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
+    const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
+    // load v of 8 rows (columns): row 8v + l/8 fills physical chunk l%8 of its
+    // slot row, which holds logical chunk (l%8) ^ ((row >> 1) & 7) =
+    // (l%8) ^ ((4v + l/16) & 7).  Columns past N re-read column n0.
+    int vw[kWLd], vx[kXLd];
+#pragma unroll
+    for (int uu = 0; uu < kWLd; ++uu) {
+        const int u = w * kWLd + uu;
+        const int col = n0 + 8 * u + (lane >> 3);
+        vw[uu] = (col < N ? col : n0) * K + 16 * ((lane & 7) ^ ((4 * u + (lane >> 4)) & 7));
+    }
+#pragma unroll
+    for (int v = 0; v < kXLd; ++v)
+        vx[v] = (8 * v + (lane >> 3)) * K + 16 * ((lane & 7) ^ ((4 * v + (lane >> 4)) & 7));
+    uint32_t o[4];
+#pragma unroll
+    for (int sh = 0; sh < 4; ++sh) o[sh] = c * kStepKNK + 16 * ((2 * sh + g) ^ ((c >> 1) & 7));
+    // scale rows: x1 row 32f + c (row 0 past the last token: its operand is
+    // zero), weight column 32j + c; each holds the step's four bytes
+    int vsa[RF], vsb[4];
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+        vsa[f] = (kTileM * f + c < mcount ? kTileM * f + c : 0) * KS;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + 32 * j + c;
+        vsb[j] = (col < N ? col : n0) * KS;
+    }
+    const RowInfo rinfo = load_row_info<RF>(p, m0, mcount);
+    v16f acc[RF][4];
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[f][j] = v16f{};
+
+    const int k_row = K / kStepKNK;
+    const int n_steps = ks1 - ks0;
+    auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
+    // WS: scale windows of four steps, [0] current / [1] next; wdl = shift of
+    // a window moved back from the row end
+    v4i wa[2][RF], wb[2][4];
+    int wdl[2] = {0, 0};
+    auto wload = [&](int ks, int set) {
+        const int start = ks < k_row - 4 ? ks : k_row - 4;
+        wdl[set] = ks - start;
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+            wa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + 4 * start, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            wb[set][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+    };
+    // per-step scale dwords (no WS), register set = stage
+    uint32_t sa_r[D][RF], sb_r[D][4];
+    auto issue_dma = [&](int ks, int stage) {
+        char *st = ring + stage * kStage;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int uu = 0; uu < kWLd; ++uu)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void_t *)(st + (w * kWLd + uu) * 1024), 16, vw[uu], ks * kStepKNK, 0, 0);
+#pragma unroll
+        for (int v = 0; v < kXLd; ++v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void_t *)(st + kCkWSlot + w * kXSlot + v * 1024), 16, vx[v],
+                ks * kStepKNK, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_scales = [&](int ks, int set) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+            sa_r[set][f] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f], 4 * ks, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sb_r[set][j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // operands of half s of the step in `stage`
+    auto read_half = [&](int stage, int s2, v4i (&t)[kNH]) {
+        const uint32_t base = lds_addr(ring + stage * kStage);
+        const uint32_t xbase = base + kCkWSlot + w * kXSlot;
+        lds_issue_ck<RF>(base + o[2 * s2], base + o[2 * s2 + 1], xbase + o[2 * s2],
+                         xbase + o[2 * s2 + 1], t);
+    };
+    v4i hb[2][kNH];   // [0]: half 0 of a step, [1]: half 1
+    // (x1 rows past the expert's last token are zero in LDS: the DMA reads
+    // them through the range-checked descriptor)
+    auto mma_half = [&](const v4i (&t)[kNH], int s2, int set, int wpos) {
+        const int shf = 8 * (2 * s2 + g);
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+            uint32_t sa = sa_r[set][f];
+            if constexpr (WS) sa = pick(wa[0][f], wpos + wdl[0]);
+            const v8i a = cat(t[8 + 2 * f], t[8 + 2 * f + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t sb = sb_r[set][j];
+                if constexpr (WS) sb = pick(wb[0][j], wpos + wdl[0]);
+                acc[f][j] = mfma<FMT, 0>(a, cat(t[2 * j], t[2 * j + 1]), acc[f][j], sa >> shf,
+                                         sb >> shf);
+            }
+        }
+    };
+
+    // Prologue: the first window, the first D steps; wait for step 0.
+    if constexpr (WS) wload(step_of(0), 0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        issue_dma(step_of(d), d);
+        if constexpr (!WS) issue_scales(step_of(d), d);
+    }
+    constexpr int kOps = kWLd + kXLd + (WS ? 0 : RF + 4);
+    static_assert((D - 1) * kOps < 64, "vmcnt range");
+    wait_vmcnt<(D - 1) * kOps>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(0, 0, hb[0]);
+    lds_wait_all(hb[0]);
+    // Iteration i (step i's half 0 already in hb[0]):
+    //   read half 1 of step i; half 0's MFMAs; wait for the reads;
+    //   wait for step i + 1 (everything issued so far) and barrier: every
+    //   wave's share of step i + 1 is in and every wave has read all of step
+    //   i's stage; read half 0 of step i + 1; refill step i's stage with step
+    //   i + 2 (WS: with the next window when step i + 2 starts one); half 1's
+    //   MFMAs; per-step scales of step i + 2 into the set just consumed; wait
+    //   for the reads.
+    for (int i0 = 0; i0 < n_steps; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = i0 + d;
+            const bool live = i < n_steps;
+            read_half(d, 1, hb[1]);
+            if (live) mma_half(hb[0], 0, d, i & 3);   // padding steps past the range: none
+            lds_wait_all(hb[1]);
+            wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_half((d + 1) % D, 0, hb[0]);
+            if constexpr (WS) {
+                if (((i + D) & 3) == 0) wload(step_of(i + D), 1);
+            }
+            issue_dma(step_of(i + D), d);
+            if (live) mma_half(hb[1], 1, d, i & 3);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!WS) issue_scales(step_of(i + D), d);
+            lds_wait_all(hb[0]);
+            if constexpr (WS) {
+                if ((i & 3) == 3) {   // the next window becomes current
+#pragma unroll
+                    for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) wb[0][j] = wb[1][j];
+                    wdl[0] = wdl[1];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();   // the trailing re-reads, before the stages are reused
+    epilogue<4, RF, 4>(p, acc, m0, n0, store_rows, rinfo);
+}
+
+// ---------------------------------------------------------------------------
+// Wave item for FP8 [N, K] weights (finalize operator, experts below the
+// cooperative size): 32 tokens x 128 columns, K steps of 128, one wave.
+// The weight tile moves global -> LDS in the cooperative units' slot layout
+// (16 loads of 8 columns x 128 B per step, two 16 KB stages per wave);
+// the x1 rows go to registers in the MFMA layout (four 32-row gathers per
+// step, each line's four 32-byte pieces in one step).  Against 64-column
+// items, each x1 row is gathered once per 128 columns instead of 64.  A
+// step's loads are issued before the second half of the previous step's
+// MFMAs; the wave's other loads in flight and the block's other three waves
+// keep the memory system busy meanwhile.
+// ---------------------------------------------------------------------------
+template <int FMT, bool WS>
+__device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int mcount, int n0,
+                                        int ks0, int ks1, bool store_rows, char *ring) {
+    constexpr int D = kCkStages;
+    static_assert(D * kCkWSlot <= kRingBytes, "a wave's stages fit its ring");
+    constexpr int kWLd = kCkWSlot / 1024;   // 16 weight loads per step
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    mcount = __builtin_amdgcn_readfirstlane(mcount);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    ks0 = __builtin_amdgcn_readfirstlane(ks0);
+    ks1 = __builtin_amdgcn_readfirstlane(ks1);
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int c = lane & 31, g = lane >> 5;
+    const int K = p.K, N = p.N, KS = p.K / 32;
+    if (mcount < 0) mcount = 0;
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
+    const int64_t wbytes = static_cast<int64_t>(N) * K;
+    const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
+    const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
+    // load u of 8 columns: column n0 + 8u + l/8 (lane offset below, 8u K in the
+    // scalar offset; columns past N lie past the expert's slice and read as
+    // zero), physical chunk l%8 holding logical chunk (l%8) ^ ((4u + l/16) & 7)
+    int vw[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        vw[par] = (n0 + (lane >> 3)) * K + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7));
+    uint32_t o[4];
+#pragma unroll
+    for (int sh = 0; sh < 4; ++sh) o[sh] = c * kStepKNK + 16 * ((2 * sh + g) ^ ((c >> 1) & 7));
+    // x1: lane (c, g) gathers row c's bytes 32q + 16g of the step (rows past
+    // the last token read as zero); its scales sit in row c (row 0 past it)
+    const int arow = c < mcount ? c : 0;
+    const int va = arow * K + 16 * g;
+    const int vsa = arow * KS;
+    int vsb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + 32 * j + c;
+        vsb[j] = (col < N ? col : n0) * KS;
+    }
+    const RowInfo rinfo = load_row_info<1>(p, m0, mcount);
+    v16f acc[1][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[0][j] = v16f{};
+
+    const int k_row = K / kStepKNK;
+    const int n_steps = ks1 - ks0;
+    auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
+    v4i wa[2], wb[2][4];   // WS windows of four steps: [0] current, [1] next
+    int wdl[2] = {0, 0};
+    auto wload = [&](int ks, int set) {
+        const int start = ks < k_row - 4 ? ks : k_row - 4;
+        wdl[set] = ks - start;
+        if (set) {
+            wa[1] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa + 4 * start, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wb[1][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+        } else {
+            wa[0] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa + 4 * start, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wb[0][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+        }
+    };
+    v4i xr[D][4];                 // x1 operands of a step, register set = stage
+    uint32_t sa_r[D], sb_r[D][4];  // per-step scale dwords (no WS)
+    auto issue_dma = [&](int ks, int stage) {
+        char *st = ring + stage * kCkWSlot;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kWLd; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + u * 1024), 16,
+                                                     vw[u & 1], 8 * u * K + ks * kStepKNK, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_regs = [&](int ks, int set) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xr[set][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, ks * kStepKNK + 32 * q, 0);
+        if constexpr (!WS) {
+            sa_r[set] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, 4 * ks, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sb_r[set][j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto read_half = [&](int stage, int s2, v4i (&t)[8]) {
+        const uint32_t base = lds_addr(ring + stage * kCkWSlot);
+        lds_issue_w8(base + o[2 * s2], base + o[2 * s2 + 1], t);
+    };
+    v4i hb[2][8];
+    auto mma_half = [&](const v4i (&t)[8], int s2, int set, int wpos) {
+        const int shf = 8 * (2 * s2 + g);
+        uint32_t sa = sa_r[set];
+        if constexpr (WS) sa = pick(wa[0], wpos + wdl[0]);
+        const v8i a = cat(xr[set][2 * s2], xr[set][2 * s2 + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t sb = sb_r[set][j];
+            if constexpr (WS) sb = pick(wb[0][j], wpos + wdl[0]);
+            acc[0][j] = mfma<FMT, 0>(a, cat(t[2 * j], t[2 * j + 1]), acc[0][j], sa >> shf,
+                                     sb >> shf);
+        }
+    };
+
+    if constexpr (WS) wload(step_of(0), 0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        issue_dma(step_of(d), d);
+        issue_regs(step_of(d), d);
+    }
+    constexpr int kOps = kWLd + 4 + (WS ? 0 : 5);
+    static_assert((D - 1) * kOps < 64, "vmcnt range");
+    wait_vmcnt<(D - 1) * kOps>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(0, 0, hb[0]);
+    lds_wait_all(hb[0]);
+    // Iteration i (half 0 of step i already in hb[0]): read half 1; half 0's
+    // MFMAs; wait for the reads and for step i + 1 (all loads issued so far);
+    // read half 0 of step i + 1; refill step i's stage with step i + 2 (WS:
+    // with the next window when step i + 2 starts one); half 1's MFMAs; x1 and
+    // scales of step i + 2 into the register set just consumed.
+    for (int i0 = 0; i0 < n_steps; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = i0 + d;
+            const bool live = i < n_steps;
+            read_half(d, 1, hb[1]);
+            if (live) mma_half(hb[0], 0, d, i & 3);
+            lds_wait_all(hb[1]);
+            wait_vmcnt<0>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_half((d + 1) % D, 0, hb[0]);
+            if constexpr (WS) {
+                if (((i + D) & 3) == 0) wload(step_of(i + D), 1);
+            }
+            issue_dma(step_of(i + D), d);
+            if (live) mma_half(hb[1], 1, d, i & 3);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_regs(step_of(i + D), d);
+            lds_wait_all(hb[0]);
+            if constexpr (WS) {
+                if ((i & 3) == 3) {   // the next window becomes current
+                    wa[0] = wa[1];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) wb[0][j] = wb[1][j];
+                    wdl[0] = wdl[1];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();
+    epilogue<4, 1, 4>(p, acc, m0, n0, store_rows, rinfo);
+}
+
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
 // contiguous slice of the R*N elements per wave, so every wave carries the
 // same small share (done after its routed work).  Lane l handles elements
@@ -1419,12 +1857,16 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // output columns per item: the weight columns, or for the upstream step
     // half of them ([N,K]: gate and up columns in one tile) or all of them
     // ([K,N]: gate and up tiles streamed in turn)
-    constexpr int kOutN = OP == 0 || !TRANS ? kTN : kTN / 2;
+    // FP8 [N, K] finalize: ck_unit / cw_item, 128-column tiles for both kinds
+    constexpr bool kTB = TRANS && (FMT == 0 || FMT == 1) && OP == 0;
+    constexpr int kOutN = kTB ? kTileN : OP == 0 || !TRANS ? kTN : kTN / 2;
     const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
+    constexpr int kOutNC = kOutN;                   // output columns per cooperative unit
+    const int n_tiles_c = n_tiles;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, s_perm, 0, 0, 0, 0};
     // two-fragment cooperative groups except where a fragment has 8 accumulators
     constexpr bool kWide = FMT != 4 && FMT != 8 && !(OP == 1 && !TRANS);
-    build_work_list<kWide>(p, n_tiles, wl, s_scan);
+    build_work_list<kWide>(p, n_tiles, n_tiles_c, wl, s_scan);
     if (OP == 0 && p.det_total && blockIdx.x == 0 && threadIdx.x == 0)
         *p.det_total = wl.routed_tokens;
 
@@ -1440,6 +1882,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // K elements per step: 64 ([K,N]), 128 ([N,K] FP8), 256 ([N,K] FP4): one
     // step always moves 8 KB of the weight tile
     const int k_steps = p.K / (!TRANS ? kStepK : FMT == 4 ? 2 * kStepKNK : kStepKNK);
+    const int k_steps_c = k_steps;                          // steps of a cooperative unit
+    const bool wsc_tb = p.K >= 4 * kStepKNK;                // ck_unit: a window of four steps
     const int blocks = gridDim.x;
     int S = p.split_k;
     const int base_units = wl.litems + (wl.sitems + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -1535,11 +1979,11 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             // blocks of one XCD (consecutive units) then share both the
             // band's x1 rows and its column tiles' weights through L2.
             const int64_t local = u - static_cast<int64_t>(e_pref) * S;
-            const int64_t per_s = static_cast<int64_t>(mg_count) * n_tiles;
+            const int64_t per_s = static_cast<int64_t>(mg_count) * n_tiles_c;
             const int s = static_cast<int>(local / per_s);
             const int r = static_cast<int>(local - s * per_s);
-            const int band = r / (kCoopBand * n_tiles);
-            const int j = r - band * kCoopBand * n_tiles;
+            const int band = r / (kCoopBand * n_tiles_c);
+            const int j = r - band * kCoopBand * n_tiles_c;
             const int hb = min(kCoopBand, mg_count - band * kCoopBand);
             const int mg = band * kCoopBand + j % hb;
             const int nt = j / hb;
@@ -1547,22 +1991,39 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int row0 = mg * gr + w * wr;                // this wave's rows
             const int mcount = min(wr, e_cnt - row0);
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
-            const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
-            const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
-            if (kWide && gr > kCoopRows) {
-                if constexpr (kWSC) {
-                    if (wsc_ok) {
-                        routed_item<FMT, !TRANS, true, 2, OP, true>(
-                            p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
-                        continue;
-                    }
+            const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps_c) * s / S);
+            const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps_c) * (s + 1) / S);
+            if constexpr (kTB) {
+                if (gr > kCoopRows) {
+                    if (wsc_tb)
+                        ck_unit<FMT, 2, true>(p, e, m0, mcount, nt * kOutNC, ks0, ks1,
+                                              store_rows, s_ring, w);
+                    else
+                        ck_unit<FMT, 2, false>(p, e, m0, mcount, nt * kOutNC, ks0, ks1,
+                                               store_rows, s_ring, w);
+                } else if (wsc_tb) {
+                    ck_unit<FMT, 1, true>(p, e, m0, mcount, nt * kOutNC, ks0, ks1, store_rows,
+                                          s_ring, w);
+                } else {
+                    ck_unit<FMT, 1, false>(p, e, m0, mcount, nt * kOutNC, ks0, ks1, store_rows,
+                                           s_ring, w);
                 }
-                routed_item<FMT, !TRANS, true, (kWide ? 2 : 1), OP>(
-                    p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
+            } else {
+                if (kWide && gr > kCoopRows) {
+                    if constexpr (kWSC) {
+                        if (wsc_ok) {
+                            routed_item<FMT, !TRANS, true, 2, OP, true>(
+                                p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
+                            continue;
+                        }
+                    }
+                    routed_item<FMT, !TRANS, true, (kWide ? 2 : 1), OP>(
+                        p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
+                } else {
+                    routed_item<FMT, !TRANS, true, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0,
+                                                          ks1, store_rows, s_ring, w);
+                }
             }
-            else
-                routed_item<FMT, !TRANS, true, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
-                                                      store_rows, s_ring, w);
         } else {
             const int64_t it = (u - coop_units) * kWavesPerBlock + w;
             if (it >= wave_items) continue;
@@ -1582,15 +2043,22 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
-            if constexpr (kWS) {
-                if (ws_ok) {
-                    routed_item<FMT, !TRANS, false, 1, OP, true>(p, e, m0, mcount, nt * kOutN,
-                                                                 ks0, ks1, store_rows, own, w);
-                    continue;
+            if constexpr (kTB) {
+                if (wsc_tb)
+                    cw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own);
+                else
+                    cw_item<FMT, false>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own);
+            } else {
+                if constexpr (kWS) {
+                    if (ws_ok) {
+                        routed_item<FMT, !TRANS, false, 1, OP, true>(
+                            p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own, w);
+                        continue;
+                    }
                 }
+                routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
+                                                       store_rows, own, w);
             }
-            routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
-                                                   store_rows, own, w);
         }
     }
     // The shared-expert term last: at the start its loads would delay the

@@ -180,6 +180,15 @@ SMALL_MANY_T = _reg(Workload("small_many_t", batch=600, M=sum(_MANY), K=512, N=3
                              group_list_type=0, exp_range=(-4, 4), row_index="perm",
                              out_init="normal", seed=1037))
 
+# [N, K] cooperative units with K = 128: two 64-K steps, too few for the
+# four-step scale windows (per-step scale loads), in a 256-row group (300
+# rows: two groups, the second short) and a 128-row group (70 rows).
+SMALL_COOP_T_K128 = _reg(Workload("small_coop_t_k128", batch=120, M=370, K=128, N=352, E=3,
+                                  fp8="e5m2", transpose_x2=True, groups=(300, 0, 70),
+                                  group_list_type=1, exp_range=(-4, 4), row_index="perm",
+                                  shared_rows=24, shared_weight=0.5, shared_offset=60,
+                                  out_init="normal", seed=1038))
+
 # The small [N, K] cases again with K = 768 (six 128-K steps instead of five)
 SMALL_T_K768 = _reg(replace(SMALL_T, name="small_t_k768", K=768, seed=1025))
 SMALL_BIG_T_K768 = _reg(replace(SMALL_BIG_T, name="small_big_t_k768", K=768, seed=1026))
@@ -228,6 +237,7 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_HUGE_N,
+              SMALL_COOP_T_K128,
               SMALL_HUGE_T, SMALL_MANY_N, SMALL_MANY_T, SMALL_T_K768,
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,

@@ -38,10 +38,11 @@ REL, ABS = 2e-5, 1e-6
 # most seen in any K split or mode, since the FP32 summation order of atomics
 # varies between runs).  Measured on the MI355X: small_t 3 of 36864 elements
 # (E5M2, E8M0 exponents +-6, K 640) in every K split and in deterministic
-# mode, small_t_k384 2 of 36864, small_many_n 5 of 307200 (E4M3FN, +-4); every
-# other case, each MXFP4 one at under 1 % of the bar, stays within it.  No
-# other case may exceed it.
-SLACK_CASES = {"small_t": 6, "small_t_k384": 4, "small_many_n": 10}
+# mode, small_t_k384 2 of 36864, small_many_n 5 of 307200 (E4M3FN, +-4),
+# small_coop_t_k128 3 of 42240 (E5M2, +-4, K 128: a dominant run weighs more
+# in a short sum); every other case, each MXFP4 one at under 1 % of the bar,
+# stays within it.  No other case may exceed it.
+SLACK_CASES = {"small_t": 6, "small_t_k384": 4, "small_many_n": 10, "small_coop_t_k128": 6}
 
 
 def _gfr():
@@ -123,7 +124,8 @@ def slack_for(inp, rows=None):
                                   "small_t_k512_exact", "small_t_k384_exact",
                                   "small_huge_n", "small_huge_t", "small_huge_n_exact",
                                   "small_huge_t_exact", "small_many_n", "small_many_t",
-                                  "small_many_n_exact", "small_many_t_exact"])
+                                  "small_many_n_exact", "small_many_t_exact",
+                                  "small_coop_t_k128", "small_coop_t_k128_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]

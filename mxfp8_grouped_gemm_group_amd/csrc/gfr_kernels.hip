@@ -1440,10 +1440,15 @@ __device__ __forceinline__ void lds_wait_all(v4i (&t)[N]) {
 template <int FMT, int RF, bool WS>
 __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int mcount, int n0,
                                         int ks0, int ks1, bool store_rows, char *ring, int w) {
-    constexpr int D = kCkStages;
+    // Stages: the weight tile two (16 KB each), the x1 rows three with scale
+    // windows (K >= 512) -- x1 is two thirds of a step's bytes, so its loads
+    // go out two steps ahead -- or two without.
+    constexpr int DW = kCkStages;
+    constexpr int DX = WS ? 3 : 2;
     constexpr int kXSlot = RF * kTileM * kStepKNK;                // one wave's x1 per step
-    constexpr int kStage = kCkWSlot + kWavesPerBlock * kXSlot;    // 48 KB (RF 2), 32 KB (RF 1)
-    static_assert(D * kStage <= kWavesPerBlock * kRingBytes, "stages fit the block's LDS ring");
+    constexpr int kXStage = kWavesPerBlock * kXSlot;              // 32 KB (RF 2), 16 KB (RF 1)
+    static_assert(DW * kCkWSlot + DX * kXStage <= kWavesPerBlock * kRingBytes,
+                  "stages fit the block's LDS ring");
     constexpr int kWLd = kCkWSlot / 1024 / kWavesPerBlock;        // weight loads per wave: 4
     constexpr int kXLd = kXSlot / 1024;                           // x1 loads per wave: 4 RF
     constexpr int kNH = 8 + 2 * RF;                               // operand reads per half step
@@ -1516,20 +1521,26 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
         for (int j = 0; j < 4; ++j)
             wb[set][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
     };
-    // per-step scale dwords (no WS), register set = stage
-    uint32_t sa_r[D][RF], sb_r[D][4];
-    auto issue_dma = [&](int ks, int stage) {
-        char *st = ring + stage * kStage;
+    // per-step scale dwords (no WS), register set = weight stage
+    uint32_t sa_r[DW][RF], sb_r[DW][4];
+    char *const wring = ring;                                  // DW weight stages
+    char *const xring = ring + DW * kCkWSlot + w * kXSlot;     // this wave's DX x1 slots
+    auto issue_w = [&](int ks, int ws) {
+        char *st = wring + ws * kCkWSlot;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int uu = 0; uu < kWLd; ++uu)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_void_t *)(st + (w * kWLd + uu) * 1024), 16, vw[uu], ks * kStepKNK, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_x = [&](int ks, int xs) {
+        char *st = xring + xs * kXStage;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < kXLd; ++v)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void_t *)(st + kCkWSlot + w * kXSlot + v * 1024), 16, vx[v],
-                ks * kStepKNK, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + v * 1024), 16, vx[v],
+                                                     ks * kStepKNK, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto issue_scales = [&](int ks, int set) {
@@ -1542,11 +1553,11 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
             sb_r[set][j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // operands of half s of the step in `stage`
-    auto read_half = [&](int stage, int s2, v4i (&t)[kNH]) {
-        const uint32_t base = lds_addr(ring + stage * kStage);
-        const uint32_t xbase = base + kCkWSlot + w * kXSlot;
-        lds_issue_ck<RF>(base + o[2 * s2], base + o[2 * s2 + 1], xbase + o[2 * s2],
+    // operands of half s of the step in weight stage ws / x1 stage xs
+    auto read_half = [&](int ws, int xs, int s2, v4i (&t)[kNH]) {
+        const uint32_t wbase = lds_addr(wring + ws * kCkWSlot);
+        const uint32_t xbase = lds_addr(xring + xs * kXStage);
+        lds_issue_ck<RF>(wbase + o[2 * s2], wbase + o[2 * s2 + 1], xbase + o[2 * s2],
                          xbase + o[2 * s2 + 1], t);
     };
     v4i hb[2][kNH];   // [0]: half 0 of a step, [1]: half 1
@@ -1569,47 +1580,66 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
         }
     };
 
-    // Prologue: the first window, the first D steps; wait for step 0.
-    if constexpr (WS) wload(step_of(0), 0);
+    // Prologue.  WS: window 0, then weights and x1 of step 0, weights and x1
+    // of step 1, x1 of step 2, so that in every iteration the youngest group
+    // in flight is the x1 two steps ahead.  Without WS: two steps, each with
+    // its per-step scales.
+    if constexpr (WS) {
+        wload(step_of(0), 0);
+        issue_w(step_of(0), 0);
+        issue_x(step_of(0), 0);
+        issue_w(step_of(1), 1);
+        issue_x(step_of(1), 1);
+        issue_x(step_of(2), 2);
+        wait_vmcnt<kWLd + 2 * kXLd>();
+    } else {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        issue_dma(step_of(d), d);
-        if constexpr (!WS) issue_scales(step_of(d), d);
+        for (int d = 0; d < 2; ++d) {
+            issue_w(step_of(d), d);
+            issue_x(step_of(d), d);
+            issue_scales(step_of(d), d);
+        }
+        wait_vmcnt<kWLd + kXLd + RF + 4>();
     }
-    constexpr int kOps = kWLd + kXLd + (WS ? 0 : RF + 4);
-    static_assert((D - 1) * kOps < 64, "vmcnt range");
-    wait_vmcnt<(D - 1) * kOps>();
+    static_assert(kWLd + 2 * kXLd < 64 && kWLd + kXLd + RF + 4 < 64, "vmcnt range");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_half(0, 0, hb[0]);
+    read_half(0, 0, 0, hb[0]);
     lds_wait_all(hb[0]);
-    // Iteration i (step i's half 0 already in hb[0]):
-    //   read half 1 of step i; half 0's MFMAs; wait for the reads;
-    //   wait for step i + 1 (everything issued so far) and barrier: every
-    //   wave's share of step i + 1 is in and every wave has read all of step
-    //   i's stage; read half 0 of step i + 1; refill step i's stage with step
-    //   i + 2 (WS: with the next window when step i + 2 starts one); half 1's
+    // Iteration i (half 0 of step i already in hb[0]; xs = x1 stage of step i):
+    //   read half 1; half 0's MFMAs; wait for the reads;
+    //   wait for step i + 1 (WS: everything but the x1 of step i + 2) and
+    //   barrier: every wave's share of step i + 1 is in and every wave has
+    //   read all of step i; read half 0 of step i + 1; refill: weights of step
+    //   i + 2 into step i's weight stage (WS: with the next window when step
+    //   i + 2 starts one), x1 of step i + DX into step i's x1 stage; half 1's
     //   MFMAs; per-step scales of step i + 2 into the set just consumed; wait
     //   for the reads.
-    for (int i0 = 0; i0 < n_steps; i0 += D) {
+    int xs = 0;
+    for (int i0 = 0; i0 < n_steps; i0 += DW) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
+        for (int d = 0; d < DW; ++d) {
             const int i = i0 + d;
             const bool live = i < n_steps;
-            read_half(d, 1, hb[1]);
+            const int xn = xs + 1 == DX ? 0 : xs + 1;   // x1 stage of step i + 1
+            read_half(d, xs, 1, hb[1]);
             if (live) mma_half(hb[0], 0, d, i & 3);   // padding steps past the range: none
             lds_wait_all(hb[1]);
-            wait_vmcnt<0>();
+            if constexpr (WS)
+                wait_vmcnt<kXLd>();
+            else
+                wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            read_half((d + 1) % D, 0, hb[0]);
+            read_half((d + 1) % DW, xn, 0, hb[0]);
             if constexpr (WS) {
-                if (((i + D) & 3) == 0) wload(step_of(i + D), 1);
+                if (((i + 2) & 3) == 0) wload(step_of(i + 2), 1);
             }
-            issue_dma(step_of(i + D), d);
+            issue_w(step_of(i + 2), d);
+            issue_x(step_of(i + DX), xs);
             if (live) mma_half(hb[1], 1, d, i & 3);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (!WS) issue_scales(step_of(i + D), d);
+            if constexpr (!WS) issue_scales(step_of(i + 2), d);
             lds_wait_all(hb[0]);
             if constexpr (WS) {
                 if ((i & 3) == 3) {   // the next window becomes current
@@ -1620,6 +1650,7 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
                     wdl[0] = wdl[1];
                 }
             }
+            xs = xn;
             __builtin_amdgcn_sched_barrier(0);
         }
     }

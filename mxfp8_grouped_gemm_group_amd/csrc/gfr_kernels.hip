@@ -128,10 +128,11 @@ __device__ __forceinline__ int coop_group_rows(int cnt) {
 
 constexpr int kPerThread = kMaxExperts / kBlockThreads;  // experts per thread
 
-// Row groups per band in the order cooperative units are taken.  With x1
-// through LDS, c5 measured 2177 µs with 2, 2182 with 1, 2198 with 4, 2228
-// with 8 and 2250 with 16 (c4 within 1 % for 2 to 16, 2 % slower with 1).
-constexpr int kCoopBand = 2;
+// Row groups per band in the order cooperative units are taken.  With the
+// 128-column [N, K] units (ck_unit), 4 measured best: c5 1808 µs against 1819
+// with 2 and 1866 with 1, c4 459 against 473 and 484, c5_pe 1859 against 1897
+// and 1932.
+constexpr int kCoopBand = 4;
 
 template <bool WIDE>
 __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tiles,

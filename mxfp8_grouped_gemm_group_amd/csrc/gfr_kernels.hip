@@ -561,6 +561,37 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs
     }
 }
 
+// Epilogue of a block-split wave unit: the block's four waves computed four
+// K ranges of one item (same 32 rows, same 128 columns).  Each wave leaves
+// its four accumulator groups in its own 16 KB of the LDS ring, as [group
+// j][register r][lane] (every store and load covers 64 consecutive dwords);
+// after a block barrier wave w adds up the four waves' group w in wave order
+// and scatters columns n0 + 32w .. n0 + 32w + 31.  One atomic per output
+// element instead of one per K range.  Every wave of the block must call it
+// (block barrier), each after its last read of its own ring region.
+__device__ __forceinline__ void split_epilogue(const FusedParams &p, const v16f (&acc)[1][4],
+                                               int m0, int n0, bool store_rows, RowInfo ri,
+                                               char *ring) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float *own = reinterpret_cast<float *>(ring + w * kRingBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) own[(16 * j + r) * kWaveSize + lane] = acc[0][j][r];
+    __syncthreads();
+    v16f sum = v16f{};
+#pragma unroll
+    for (int w2 = 0; w2 < kWavesPerBlock; ++w2) {
+        const float *src = reinterpret_cast<const float *>(ring + w2 * kRingBytes) +
+                           16 * w * kWaveSize + lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] += src[r * kWaveSize];
+    }
+    const v16f one[1][1] = {{sum}};
+    epilogue<1, 1, 1>(p, one, m0, n0 + 32 * w, store_rows, ri);
+}
+
 // W4A8 epilogue.  acc[f][j] / acc[f][4 + j] hold 16 * the exact integer
 // products of the odd / even weight columns n0 + 2(32j + c) + {1, 0}; rsum
 // the lane's share of its row's x1 sum (K halves g = 0, 1 in lanes c, c + 32).
@@ -737,9 +768,12 @@ __device__ __forceinline__ uint32_t pick(const v4i &w, int k) {
     return static_cast<uint32_t>(k <= 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w);
 }
 
+// split: the block's LDS ring when the item is one of a block-split wave
+// unit's four K ranges (split_epilogue), else null.
 template <int FMT, bool KN, bool COOP, int RF, int OP, bool WS = false>
 __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
-                            int ks0, int ks1, bool store_rows, char *ring, int w) {
+                            int ks0, int ks1, bool store_rows, char *ring, int w,
+                            char *split = nullptr) {
     static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
     // FP4 E2M1 (MFMA format 4): elements packed two per byte along the
     // contiguous axis (x1 and [N, K] weights along K, [K, N] weights along N).
@@ -1347,7 +1381,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         epilogue_swiglu<SPLIT ? 8 : 2, RF, NA>(p, acc, m0, mcount, n0);
     else if constexpr (I8)
         epilogue_w4a8<RF>(p, acc, rsum, cscale, m0, n0, store_rows, rinfo);
-    else
+    else if constexpr (KN && !KN4 && !COOP && RF == 1 && NA == 4) {
+        if (split)
+            split_epilogue(p, acc, m0, n0, store_rows, rinfo, split);
+        else
+            epilogue<4, 1, 4>(p, acc, m0, n0, store_rows, rinfo);
+    } else
         epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
 
@@ -1671,9 +1710,11 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
 // MFMAs; the wave's other loads in flight and the block's other three waves
 // keep the memory system busy meanwhile.
 // ---------------------------------------------------------------------------
+// split: as for routed_item.
 template <int FMT, bool WS>
 __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int mcount, int n0,
-                                        int ks0, int ks1, bool store_rows, char *ring) {
+                                        int ks0, int ks1, bool store_rows, char *ring,
+                                        char *split) {
     constexpr int D = kCkStages;
     static_assert(D * kCkWSlot <= kRingBytes, "a wave's stages fit its ring");
     constexpr int kWLd = kCkWSlot / 1024;   // 16 weight loads per step
@@ -1829,7 +1870,10 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
         }
     }
     wait_vmcnt<0>();
-    epilogue<4, 1, 4>(p, acc, m0, n0, store_rows, rinfo);
+    if (split)
+        split_epilogue(p, acc, m0, n0, store_rows, rinfo, split);
+    else
+        epilogue<4, 1, 4>(p, acc, m0, n0, store_rows, rinfo);
 }
 
 // Shared-expert term out[off + r, n] += w * shared_input[r, n], as one
@@ -1930,6 +1974,17 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         S = S > 1 ? S : 1;
     }
     S = S < k_steps ? S : k_steps;
+    // Block-split wave units (FP8 finalize, only wave items, K split into a
+    // multiple of four ranges): the four waves of a unit take four K ranges
+    // of one item and add their partial sums in LDS before the scatter
+    // (split_epilogue), so each output element gets one atomic per four
+    // ranges.  c1 (16 tokens per expert, four ranges) spends a fifth of its
+    // time in atomics otherwise.  An explicit split that is not a multiple of
+    // four keeps one item per wave.
+    constexpr bool kSplitOK = OP == 0 && (FMT == 0 || FMT == 1);
+    const bool bsplit = kSplitOK && !store_rows && wl.litems == 0 && S >= kWavesPerBlock &&
+                        (p.split_k <= 0 || p.split_k % kWavesPerBlock == 0);
+    if (bsplit) S -= S % kWavesPerBlock;
     const int64_t coop_units = static_cast<int64_t>(wl.litems) * S;
     const int64_t wave_items = static_cast<int64_t>(wl.sitems) * S;
     const int64_t units = coop_units + (wave_items + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -2066,20 +2121,34 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int e_pref = __builtin_amdgcn_readfirstlane(s_spref[e]);
             const int mt_count = (e_cnt + kTileM - 1) / kTileM;
             const int64_t local = it - static_cast<int64_t>(e_pref) * S;
-            const int mt = static_cast<int>(local % mt_count);
-            const int64_t rest = local / mt_count;
-            const int s = static_cast<int>(rest % S);
-            const int nt = static_cast<int>(rest / S);
+            // items of an expert: row tiles fastest, then K ranges, then
+            // column tiles; block-split: K ranges fastest (a unit's four
+            // waves share the row and column tile)
+            int mt, s, nt;
+            if (bsplit) {
+                s = static_cast<int>(local % S);
+                const int64_t rest = local / S;
+                mt = static_cast<int>(rest % mt_count);
+                nt = static_cast<int>(rest / mt_count);
+            } else {
+                mt = static_cast<int>(local % mt_count);
+                const int64_t rest = local / mt_count;
+                s = static_cast<int>(rest % S);
+                nt = static_cast<int>(rest / S);
+            }
             const int m0 = e_start + mt * kTileM;
             const int mcount = min(kTileM, e_cnt - mt * kTileM);
             const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
             const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
             char *own = s_ring + w * kRingBytes;
+            char *split = bsplit ? s_ring : nullptr;
             if constexpr (kTB) {
                 if (wsc_tb)
-                    cw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own);
+                    cw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own,
+                                       split);
                 else
-                    cw_item<FMT, false>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own);
+                    cw_item<FMT, false>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own,
+                                        split);
             } else {
                 if constexpr (kWS) {
                     if (ws_ok) {
@@ -2089,7 +2158,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
                     }
                 }
                 routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
-                                                       store_rows, own, w);
+                                                       store_rows, own, w, split);
             }
         }
     }

@@ -189,6 +189,21 @@ SMALL_COOP_T_K128 = _reg(Workload("small_coop_t_k128", batch=120, M=370, K=128, 
                                   shared_rows=24, shared_weight=0.5, shared_offset=60,
                                   out_init="normal", seed=1038))
 
+# Only experts below the cooperative size, few items and K long enough for a
+# K split of four or more (32 K steps in either layout): the automatic split
+# puts the four K ranges of an item into one block and adds them in LDS
+# before the scatter.  Partial last column tile, a two-tile expert (40 rows),
+# an empty expert, tokens routed twice to a row (topk 2).
+SMALL_SPLIT_N = _reg(Workload("small_split_n", batch=21, topk=2, M=42, K=2048, N=320, E=4,
+                              fp8="e4m3fn", groups=(10, 0, 29, 3), group_list_type=1,
+                              exp_range=(-4, 4), logit="softmax", row_index="perm",
+                              shared_rows=6, shared_weight=0.5, shared_offset=3,
+                              out_init="normal", seed=1039))
+SMALL_SPLIT_T = _reg(Workload("small_split_t", batch=31, topk=2, M=62, K=4096, N=352, E=3,
+                              fp8="e5m2", transpose_x2=True, groups=(5, 17, 40),
+                              group_list_type=0, exp_range=(-4, 4), row_index="perm",
+                              out_init="normal", seed=1040))
+
 # The small [N, K] cases again with K = 768 (six 128-K steps instead of five)
 SMALL_T_K768 = _reg(replace(SMALL_T, name="small_t_k768", K=768, seed=1025))
 SMALL_BIG_T_K768 = _reg(replace(SMALL_BIG_T, name="small_big_t_k768", K=768, seed=1026))
@@ -237,7 +252,7 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_HUGE_N,
-              SMALL_COOP_T_K128,
+              SMALL_COOP_T_K128, SMALL_SPLIT_N, SMALL_SPLIT_T,
               SMALL_HUGE_T, SMALL_MANY_N, SMALL_MANY_T, SMALL_T_K768,
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,

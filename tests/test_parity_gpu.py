@@ -125,9 +125,27 @@ def slack_for(inp, rows=None):
                                   "small_huge_n", "small_huge_t", "small_huge_n_exact",
                                   "small_huge_t_exact", "small_many_n", "small_many_t",
                                   "small_many_n_exact", "small_many_t_exact",
-                                  "small_coop_t_k128", "small_coop_t_k128_exact"])
+                                  "small_coop_t_k128", "small_coop_t_k128_exact",
+                                  "small_split_n", "small_split_t", "small_split_n_exact",
+                                  "small_split_t_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
+    w = WORKLOADS[name]
+    print(f"case {name} split_k={split_k}", flush=True)
+    inp = make_inputs(w, DEV)
+    got = run_gpu(inp, split_k=split_k)
+    ref, mag = run_oracle(inp)
+    assert_parity(got, ref, mag, exact=w.exact, what=f"{name} split_k={split_k}", case=name,
+                  slack=lambda: slack_for(inp))
+
+
+# K splits that are multiples of four on shapes with only wave items: the
+# four K ranges of an item run in one block and are added in LDS before the
+# scatter (8: two such blocks per item, each with its own atomics).
+@pytest.mark.parametrize("name", ["small_split_n", "small_split_t", "small_split_n_exact",
+                                  "small_split_t_exact"])
+@pytest.mark.parametrize("split_k", [4, 8])
+def test_block_split(name, split_k):
     w = WORKLOADS[name]
     print(f"case {name} split_k={split_k}", flush=True)
     inp = make_inputs(w, DEV)

@@ -535,7 +535,14 @@ template <int NJ, int RF, int NA>
 __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs)[RF][NA],
                                          int m0, int n0, bool store_rows, RowInfo ri) {
     const int lane = threadIdx.x & (kWaveSize - 1);
-    const int c = lane & 31, g = lane >> 5;
+    const int c = lane & 31;
+    // The lane's half index through an opaque copy: the row numbers below are
+    // then computed here.  As plain lane constants the compiler hoists all of
+    // them out of the unit loop, where they stay live across every main loop
+    // and are spilled, and each reload in the loop below waits for every
+    // atomic still in flight (vmcnt 0).
+    int g;
+    asm volatile("v_lshrrev_b32 %0, 5, %1" : "=v"(g) : "v"(lane));
     const int my_dst = row_dst(p, ri);
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
@@ -2023,7 +2030,39 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // and wave units stream it, so mixing them keeps HBM busy while the
     // cooperative work proceeds (c5 2412 -> 2369 µs, c5_fp4 1732 -> 1619,
     // c4 516 -> 506 against all cooperative units first).
+    //
+    // A last round with at most half as many units as blocks would leave the
+    // other blocks idle for a whole unit (c4: 896 units, 3.5 per block, so
+    // half the blocks ran a fourth one).  In atomic finalize mode each of its
+    // units is cut into T K ranges instead (T = blocks / units left, at least
+    // eight K steps each) and the pieces fill the round; a piece adds its
+    // partial sums like any K split.  The deal is over positions: positions
+    // below R * blocks (R full rounds) are units, position R * blocks + q is
+    // piece q % T of unit R * blocks + q / T.
     const bool snake = kWide && coop_units > 0;
+    const bool tail_ok = OP == 0 && !store_rows && !bsplit;
+    auto tail_factor = [&](int64_t n) -> int {   // pieces per unit of n's last round
+        const int64_t left = n % blocks;
+        if (!tail_ok || left == 0 || 2 * left > blocks) return 1;
+        const int64_t t = blocks / left;
+        const int kmax = (k_steps / S) / 8;
+        return static_cast<int>(t < kmax ? t : kmax) > 1 ? static_cast<int>(t < kmax ? t : kmax) : 1;
+    };
+    // the split sequence: the single snake sequence, or the wave units when
+    // there are no cooperative ones
+    const int64_t seq_n = snake ? units : coop_units == 0 ? units : 0;
+    const int tT = seq_n > 0 ? tail_factor(seq_n) : 1;
+    const int64_t seq_full = seq_n / blocks * blocks;
+    const int64_t seq_pos = tT > 1 ? seq_full + (seq_n - seq_full) * tT : seq_n;
+    // position of the split sequence -> unit and piece (T = tT past seq_full)
+    auto unit_of = [&](int64_t g, int &piece) -> int64_t {
+        if (g < seq_full || tT == 1) {
+            piece = 0;
+            return g;
+        }
+        piece = static_cast<int>((g - seq_full) % tT);
+        return seq_full + (g - seq_full) / tT;
+    };
     auto g_of = [&](int64_t k) {
         return k * blocks + ((k & 1) ? blocks - 1 - xcd_block : xcd_block);
     };
@@ -2031,25 +2070,38 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     if (snake) {
         // this rank's rounds: the cooperative ones, then the wave ones (g
         // grows with k)
-        for (int64_t k = 0; k * blocks < units; ++k) {
+        for (int64_t k = 0; k * blocks < seq_pos; ++k) {
             const int64_t g = g_of(k);
-            n_coop += g < coop_units;
-            n_wave += g >= coop_units && g < units;
+            int pc;
+            const int64_t uu0 = g < seq_pos ? unit_of(g, pc) : units;
+            n_coop += uu0 < coop_units;
+            n_wave += uu0 >= coop_units && uu0 < units;
         }
     } else {
-        const int64_t wave_units = units - coop_units;
+        const int64_t wave_pos = coop_units == 0 ? seq_pos : units - coop_units;
         n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;
-        n_wave = wave_units > blockIdx.x ? (wave_units - blockIdx.x + blocks - 1) / blocks : 0;
+        n_wave = wave_pos > blockIdx.x ? (wave_pos - blockIdx.x + blocks - 1) / blocks : 0;
     }
-    auto coop_unit = [&](int64_t i) { return snake ? g_of(i) : xcd_block + i * blocks; };
-    auto wave_unit = [&](int64_t j) {
+    auto coop_pos = [&](int64_t i) { return snake ? g_of(i) : xcd_block + i * blocks; };
+    auto wave_pos_of = [&](int64_t j) {
         return snake ? g_of(n_coop + j) : coop_units + blockIdx.x + j * blocks;
     };
     int64_t i_coop = 0, i_wave = 0;
     for (int64_t uu = 0; uu < n_coop + n_wave; ++uu) {
         const bool take_coop = i_wave >= n_wave ||
                                (i_coop < n_coop && ((uu + blockIdx.x) & 1) == 0);
-        const int64_t u = take_coop ? coop_unit(i_coop++) : wave_unit(i_wave++);
+        const int64_t g = take_coop ? coop_pos(i_coop++) : wave_pos_of(i_wave++);
+        int piece = 0;
+        const int64_t u = unit_of(g, piece);
+        // K range of a last-round piece inside its unit's range
+        auto narrow = [&](int &a, int &b) {
+            if (tT > 1 && g >= seq_full) {
+                const int span = b - a;
+                const int a0 = a;
+                a = a0 + span * piece / tT;
+                b = a0 + span * (piece + 1) / tT;
+            }
+        };
         __syncthreads();   // the previous unit's waves are done with the LDS
         if (u < coop_units) {
             const int q = static_cast<int>(u / S);
@@ -2078,8 +2130,9 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int row0 = mg * gr + w * wr;                // this wave's rows
             const int mcount = min(wr, e_cnt - row0);
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
-            const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps_c) * s / S);
-            const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps_c) * (s + 1) / S);
+            int ks0 = static_cast<int>(static_cast<int64_t>(k_steps_c) * s / S);
+            int ks1 = static_cast<int>(static_cast<int64_t>(k_steps_c) * (s + 1) / S);
+            narrow(ks0, ks1);
             if constexpr (kTB) {
                 if (gr > kCoopRows) {
                     if (wsc_tb)
@@ -2138,8 +2191,9 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             }
             const int m0 = e_start + mt * kTileM;
             const int mcount = min(kTileM, e_cnt - mt * kTileM);
-            const int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
-            const int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
+            int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
+            int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
+            narrow(ks0, ks1);
             char *own = s_ring + w * kRingBytes;
             char *split = bsplit ? s_ring : nullptr;
             if constexpr (kTB) {

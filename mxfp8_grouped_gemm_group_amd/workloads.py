@@ -204,6 +204,20 @@ SMALL_SPLIT_T = _reg(Workload("small_split_t", batch=31, topk=2, M=62, K=4096, N
                               group_list_type=0, exp_range=(-4, 4), row_index="perm",
                               out_init="normal", seed=1040))
 
+# More units than workgroups with a short last round (two large experts and
+# 150 small ones, eight column tiles, 16 K steps): the last round's units are
+# cut into K halves so that they fill it.  A token of each batch row is
+# routed twice (topk 2).
+_TAIL = (150, 151) + tuple(1 + (7 * i) % 32 for i in range(150))
+SMALL_TAIL_N = _reg(Workload("small_tail_n", batch=sum(_TAIL) // 2, topk=2, M=sum(_TAIL),
+                             K=1024, N=1024, E=len(_TAIL), fp8="e4m3fn", groups=_TAIL,
+                             group_list_type=1, exp_range=(-4, 4), logit="softmax",
+                             row_index="perm", seed=1052))
+SMALL_TAIL_T = _reg(Workload("small_tail_t", batch=sum(_TAIL) // 2, topk=2, M=sum(_TAIL),
+                             K=2048, N=1024, E=len(_TAIL), fp8="e5m2", transpose_x2=True,
+                             groups=_TAIL, group_list_type=0, exp_range=(-4, 4),
+                             row_index="perm", out_init="normal", seed=1053))
+
 # The small [N, K] cases again with K = 768 (six 128-K steps instead of five)
 SMALL_T_K768 = _reg(replace(SMALL_T, name="small_t_k768", K=768, seed=1025))
 SMALL_BIG_T_K768 = _reg(replace(SMALL_BIG_T, name="small_big_t_k768", K=768, seed=1026))
@@ -252,7 +266,7 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 # Integer-valued variants: every partial sum is exactly representable in FP32,
 # so any summation order must reproduce the oracle bit for bit.
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_HUGE_N,
-              SMALL_COOP_T_K128, SMALL_SPLIT_N, SMALL_SPLIT_T,
+              SMALL_COOP_T_K128, SMALL_SPLIT_N, SMALL_SPLIT_T, SMALL_TAIL_N, SMALL_TAIL_T,
               SMALL_HUGE_T, SMALL_MANY_N, SMALL_MANY_T, SMALL_T_K768,
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,

@@ -40,9 +40,12 @@ REL, ABS = 2e-5, 1e-6
 # (E5M2, E8M0 exponents +-6, K 640) in every K split and in deterministic
 # mode, small_t_k384 2 of 36864, small_many_n 5 of 307200 (E4M3FN, +-4),
 # small_coop_t_k128 3 of 42240 (E5M2, +-4, K 128: a dominant run weighs more
-# in a short sum); every other case, each MXFP4 one at under 1 % of the bar,
-# stays within it.  No other case may exceed it.
-SLACK_CASES = {"small_t": 6, "small_t_k384": 4, "small_many_n": 10, "small_coop_t_k128": 6}
+# in a short sum), small_tail_n 6 of 1419264 (E4M3FN, +-4; the same six in
+# every K split, with the last-round K halves and in deterministic mode, at
+# 0.08 of the bound with the truncation term); every other case, each MXFP4
+# one at under 1 % of the bar, stays within it.  No other case may exceed it.
+SLACK_CASES = {"small_t": 6, "small_t_k384": 4, "small_many_n": 10, "small_coop_t_k128": 6,
+               "small_tail_n": 12}
 
 
 def _gfr():
@@ -127,7 +130,8 @@ def slack_for(inp, rows=None):
                                   "small_many_n_exact", "small_many_t_exact",
                                   "small_coop_t_k128", "small_coop_t_k128_exact",
                                   "small_split_n", "small_split_t", "small_split_n_exact",
-                                  "small_split_t_exact"])
+                                  "small_split_t_exact", "small_tail_n", "small_tail_t",
+                                  "small_tail_n_exact", "small_tail_t_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]

@@ -341,6 +341,14 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// Every LDS read issued so far has returned, and (a memory clobber) the
+// compiler moves no memory access across this point: the reads of a stage
+// made with ordinary loads or builtins are done before that stage is
+// refilled or a barrier hands it to the other waves.
+__device__ __forceinline__ void lds_reads_done() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // LDS reads of the weight tile.  They are inline asm because the compiler's
 // wait insertion cannot tell which direct-to-LDS load wrote which slot and
 // would otherwise drain every outstanding load before each read; the explicit
@@ -1725,6 +1733,263 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
 }
 
 // ---------------------------------------------------------------------------
+// Cooperative unit for FP8 [K, N] weights (finalize operator): ck_unit's
+// structure -- RF x 128 rows of one expert x 128 columns in K steps of 128,
+// two weight stages, two or three x1 stages, the x1 rows staged through LDS
+// as whole 128-byte lines -- with the [K, N] weight tile: a stage holds the
+// step's 128 K rows x 128 bytes as two 64-K halves of the [K, N] slot layout
+// (16-byte chunks of row r XOR-swizzled by (r >> 1) & 3), moved by 16
+// direct-to-LDS loads of 8 K rows (four per wave; every K row segment of the
+// tile is one 128-byte line), and read K-contiguous per column with
+// transposing reads.  Against the 64-K cooperative units each x1 line is
+// requested once per step instead of twice.  Weight scales ([K/64, N, 2]):
+// the step's two 64-K rows, per-step dwords loaded with the weights; x1
+// scales: ck_unit's windows of four steps (WS) or per-step dwords.
+// ---------------------------------------------------------------------------
+template <int FMT, int RF, bool WS>
+__device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int mcount, int n0,
+                                        int ks0, int ks1, bool store_rows, char *ring, int w) {
+    constexpr int DW = kCkStages;
+    constexpr int DX = WS ? 3 : 2;
+    constexpr int kXSlot = RF * kTileM * kStepKNK;                // one wave's x1 per step
+    constexpr int kXStage = kWavesPerBlock * kXSlot;
+    static_assert(DW * kCkWSlot + DX * kXStage <= kWavesPerBlock * kRingBytes,
+                  "stages fit the block's LDS ring");
+    constexpr int kWLd = kCkWSlot / 1024 / kWavesPerBlock;        // weight loads per wave: 4
+    constexpr int kXLd = kXSlot / 1024;                           // x1 loads per wave: 4 RF
+    constexpr int kSbLd = 8;                                      // weight-scale dwords per step
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    mcount = __builtin_amdgcn_readfirstlane(mcount);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    ks0 = __builtin_amdgcn_readfirstlane(ks0);
+    ks1 = __builtin_amdgcn_readfirstlane(ks1);
+    w = __builtin_amdgcn_readfirstlane(w);
+    const int lane = lane_id();
+    const int c = lane & 31, g = lane >> 5;
+    const int K = p.K, N = p.N, KS = p.K / 32;
+    if (mcount < 0) mcount = 0;
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
+    const int64_t wbytes = static_cast<int64_t>(K) * N;
+    const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
+    const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
+    // weight load u (u = 4w + uu): K row 8u + l/8 of the step (row offset in
+    // the scalar offset); it fills physical chunk l%8 of its slot row, which
+    // holds logical chunk (l%8) ^ ((l >> 4) & 3); columns past N re-read n0
+    const int chunk_col = n0 + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+    const int vw = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
+    // x1 load v of 8 rows: ck_unit's
+    int vx[kXLd];
+#pragma unroll
+    for (int v = 0; v < kXLd; ++v)
+        vx[v] = (8 * v + (lane >> 3)) * K + 16 * ((lane & 7) ^ ((4 * v + (lane >> 4)) & 7));
+    uint32_t o[4];   // x1 operand reads (ck_unit's)
+#pragma unroll
+    for (int sh = 0; sh < 4; ++sh) o[sh] = c * kStepKNK + 16 * ((2 * sh + g) ^ ((c >> 1) & 7));
+    // transposing reads of a 64-K half: lane s of 16-lane group G reads K row
+    // 16g + (s >> 1) (+ the read's offset), columns 32j + 16(G & 1) + 8(s & 1)
+    uint32_t tr[4];
+    {
+        const int G = lane >> 4, sl = lane & 15, ii = sl >> 1, h = sl & 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            tr[j] = (16 * g + ii) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((ii >> 1) & 3)) + 8 * h;
+    }
+    // scale rows: x1 row 32f + c (row 0 past the last token: its operand is
+    // zero); weight scale dword of (64-K row, column pair of 32j + c)
+    int vsa[RF], vsb[4];
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+        vsa[f] = (kTileM * f + c < mcount ? kTileM * f + c : 0) * KS;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + 32 * j + c;
+        vsb[j] = ((col < N ? col : n0) & ~1) * 2;
+    }
+    const int sb_shift = 8 * (2 * (c & 1) + g);
+    const RowInfo rinfo = load_row_info<RF>(p, m0, mcount);
+    v16f acc[RF][4];
+#pragma unroll
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[f][j] = v16f{};
+
+    const int k_row = K / kStepKNK;
+    const int n_steps = ks1 - ks0;
+    auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
+    v4i wa[2][RF];   // WS: x1 scale windows, [0] current / [1] next
+    int wdl[2] = {0, 0};
+    auto wload = [&](int ks, int set) {
+        const int start = ks < k_row - 4 ? ks : k_row - 4;
+        wdl[set] = ks - start;
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+            wa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + 4 * start, 0, 0);
+    };
+    uint32_t sa_r[DW][RF], sb_r[DW][2][4];   // per-step scale dwords, set = weight stage
+    char *const wring = ring;
+    char *const xring = ring + DW * kCkWSlot + w * kXSlot;
+    // the weight tile of step ks into stage ws
+    auto issue_w = [&](int ks, int ws) {
+        char *st = wring + ws * kCkWSlot;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int uu = 0; uu < kWLd; ++uu) {
+            const int u = w * kWLd + uu;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void_t *)(st + u * 1024), 16, vw, (ks * kStepKNK + 8 * u) * N, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // its scales into register set ws (issued after the MFMAs that still
+    // read that set)
+    auto issue_sc = [&](int ks, int ws) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sb_r[ws][h][j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j],
+                                                                      (2 * ks + h) * 2 * N, 0);
+        if constexpr (!WS) {
+#pragma unroll
+            for (int f = 0; f < RF; ++f)
+                sa_r[ws][f] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f], 4 * ks, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_x = [&](int ks, int xs) {
+        char *st = xring + xs * kXStage;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = 0; v < kXLd; ++v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + v * 1024), 16, vx[v],
+                                                     ks * kStepKNK, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // operands of half s2 of the step in weight stage ws / x1 stage xs
+    struct Half {
+        v8i b[4];
+        v8i a[RF];
+    };
+    auto read_half = [&](int ws, int xs, int s2, Half &t) {
+        char *wb = wring + ws * kCkWSlot + s2 * (kStepK * kTileN);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lds_v2i_t *q = (lds_v2i_t *)(wb + tr[j]);
+            const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(q);
+            const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(q + 1024 / 8);
+            const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(q + 4096 / 8);
+            const v2i r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(q + 5120 / 8);
+            t.b[j] = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+        }
+        char *xb = xring + xs * kXStage;
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+            const v4i lo = *reinterpret_cast<const __attribute__((address_space(3))) v4i *>(
+                (lds_void_t *)(xb + f * 4096 + o[2 * s2]));
+            const v4i hi = *reinterpret_cast<const __attribute__((address_space(3))) v4i *>(
+                (lds_void_t *)(xb + f * 4096 + o[2 * s2 + 1]));
+            t.a[f] = cat(lo, hi);
+        }
+    };
+    Half hb[2];   // [0]: half 0 of a step, [1]: half 1
+    auto mma_half = [&](const Half &t, int s2, int set, int wpos) {
+        const int shf = 8 * (2 * s2 + g);
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+            uint32_t sa = 0;
+            if constexpr (WS)
+                sa = pick(wa[0][f], wpos + wdl[0]);
+            else
+                sa = sa_r[set][f];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[f][j] = mfma<FMT, 0>(t.a[f], t.b[j], acc[f][j], sa >> shf,
+                                         sb_r[set][s2][j] >> sb_shift);
+        }
+    };
+
+    // Prologue (ck_unit's): WS: window 0, then weights and x1 of step 0,
+    // weights and x1 of step 1, x1 of step 2; without: two steps.
+    // (scale loads are register loads: the compiler waits for them before
+    // their use; the explicit waits count them only as later loads)
+    constexpr int kSc = kSbLd + (WS ? 0 : RF);   // scale loads per step
+    if constexpr (WS) {
+        wload(step_of(0), 0);
+        issue_w(step_of(0), 0);
+        issue_sc(step_of(0), 0);
+        issue_x(step_of(0), 0);
+        issue_w(step_of(1), 1);
+        issue_sc(step_of(1), 1);
+        issue_x(step_of(1), 1);
+        issue_x(step_of(2), 2);
+        wait_vmcnt<kWLd + kSc + 2 * kXLd>();
+    } else {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            issue_w(step_of(d), d);
+            issue_sc(step_of(d), d);
+            issue_x(step_of(d), d);
+        }
+        wait_vmcnt<kWLd + kSc + kXLd>();
+    }
+    static_assert(kWLd + kSc + 2 * kXLd < 64 && kXLd + kSc < 64, "vmcnt range");
+    lds_reads_done();
+    __builtin_amdgcn_s_barrier();
+    lds_reads_done();
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(0, 0, 0, hb[0]);
+    // Iteration i (ck_unit's order): read half 1; half 0's MFMAs; wait for
+    // step i + 1 and barrier; read half 0 of step i + 1; refill: weights of
+    // step i + 2 into step i's weight stage (WS: with the next window when
+    // step i + 2 starts one), x1 of step i + DX into step i's x1 stage; half
+    // 1's MFMAs; step i + 2's scales into the register set just consumed.
+    int xs = 0;
+    for (int i0 = 0; i0 < n_steps; i0 += DW) {
+#pragma unroll
+        for (int d = 0; d < DW; ++d) {
+            const int i = i0 + d;
+            const bool live = i < n_steps;
+            const int xn = xs + 1 == DX ? 0 : xs + 1;
+            read_half(d, xs, 1, hb[1]);
+            if (live) mma_half(hb[0], 0, d, i & 3);
+            // step i + 1's tile and x1 are in: pending may be the scales of
+            // step i + 1 (issued last) and, WS, the x1 of step i + 2
+            if constexpr (WS)
+                wait_vmcnt<kXLd + kSc>();
+            else
+                wait_vmcnt<kSc>();
+            lds_reads_done();   // this wave's reads of step i are done ...
+            __builtin_amdgcn_s_barrier();   // ... and every wave's: its stages may be refilled
+            lds_reads_done();
+            __builtin_amdgcn_sched_barrier(0);
+            read_half((d + 1) % DW, xn, 0, hb[0]);
+            if constexpr (WS) {
+                if (((i + 2) & 3) == 0) wload(step_of(i + 2), 1);
+            }
+            issue_w(step_of(i + 2), d);
+            issue_x(step_of(i + DX), xs);
+            if (live) mma_half(hb[1], 1, d, i & 3);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_sc(step_of(i + 2), d);
+            if constexpr (WS) {
+                if ((i & 3) == 3) {   // the next window becomes current
+#pragma unroll
+                    for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
+                    wdl[0] = wdl[1];
+                }
+            }
+            xs = xn;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();   // the trailing re-reads, before the stages are reused
+    epilogue<4, RF, 4>(p, acc, m0, n0, store_rows, rinfo);
+}
+
+// ---------------------------------------------------------------------------
 // Wave item for FP8 [N, K] weights (finalize operator, experts below the
 // cooperative size): 32 tokens x 128 columns, K steps of 128, one wave.
 // The weight tile moves global -> LDS in the cooperative units' slot layout
@@ -2064,6 +2329,7 @@ __device__ __forceinline__ void kw_item(const FusedParams &p, int e, int m0, int
             read_half(d, 1, hb[1]);
             if (live) mma_half(hb[0], 0, d, i & 3);
             wait_vmcnt<0>();
+            lds_reads_done();   // stage d's reads are done before its refill below
             __builtin_amdgcn_sched_barrier(0);
             read_half((d + 1) % D, 0, hb[0]);
             if constexpr (WS) {
@@ -2360,6 +2626,24 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
                                           s_ring, w);
                 } else {
                     ck_unit<FMT, 1, false>(p, e, m0, mcount, nt * kOutNC, ks0, ks1, store_rows,
+                                           s_ring, w);
+                }
+            } else if constexpr (kKW) {
+                int k0c = static_cast<int>(static_cast<int64_t>(k_steps_w) * s / S);
+                int k1c = static_cast<int>(static_cast<int64_t>(k_steps_w) * (s + 1) / S);
+                narrow(k0c, k1c);
+                if (gr > kCoopRows) {
+                    if (wsc_tb)
+                        kc_unit<FMT, 2, true>(p, e, m0, mcount, nt * kOutNC, k0c, k1c,
+                                              store_rows, s_ring, w);
+                    else
+                        kc_unit<FMT, 2, false>(p, e, m0, mcount, nt * kOutNC, k0c, k1c,
+                                               store_rows, s_ring, w);
+                } else if (wsc_tb) {
+                    kc_unit<FMT, 1, true>(p, e, m0, mcount, nt * kOutNC, k0c, k1c, store_rows,
+                                          s_ring, w);
+                } else {
+                    kc_unit<FMT, 1, false>(p, e, m0, mcount, nt * kOutNC, k0c, k1c, store_rows,
                                            s_ring, w);
                 }
             } else {

@@ -2461,6 +2461,9 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         S = S > 1 ? S : 1;
     }
     S = S < k_steps ? S : k_steps;
+    // Unit and item numbers below are 32-bit: keep (items) x S under 2^30
+    // (the host bounds the items; only an explicit split could reach it).
+    while (S > 1 && static_cast<int64_t>(wl.litems + wl.sitems) * S >= (int64_t{1} << 30)) S >>= 1;
     // Block-split wave units (FP8 finalize, only wave items, K split into a
     // multiple of four ranges): the four waves of a unit take four K ranges
     // of one item and add their partial sums in LDS before the scatter
@@ -2472,9 +2475,9 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     const bool bsplit = kSplitOK && !store_rows && wl.litems == 0 && S >= kWavesPerBlock &&
                         (p.split_k <= 0 || p.split_k % kWavesPerBlock == 0);
     if (bsplit) S -= S % kWavesPerBlock;
-    const int64_t coop_units = static_cast<int64_t>(wl.litems) * S;
-    const int64_t wave_items = static_cast<int64_t>(wl.sitems) * S;
-    const int64_t units = coop_units + (wave_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int coop_units = static_cast<int>(wl.litems) * S;
+    const int wave_items = static_cast<int>(wl.sitems) * S;
+    const int units = coop_units + (wave_items + kWavesPerBlock - 1) / kWavesPerBlock;
 
     // Everything that selects a work item is wave-uniform; readfirstlane makes
     // that visible to the compiler so buffer descriptors and row offsets live
@@ -2487,10 +2490,10 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // large experts' weights are read from HBM once per row group).  Wave
     // units are taken in plain order (measured faster for streaming: each XCD
     // then reads many experts' weights at once).
-    const int64_t xcd_block =
-        (blocks % 8 == 0) ? static_cast<int64_t>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
+    const int xcd_block =
+        (blocks % 8 == 0) ? static_cast<int>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
                           : blockIdx.x;
-    const int64_t waves = static_cast<int64_t>(blocks) * kWavesPerBlock;
+    const int waves = static_cast<int>(blocks) * kWavesPerBlock;
 
     // The deal.  With two-fragment cooperative units present, units g = 0,
     // 1, ... (the cooperative units in the order of the work list, experts
@@ -2521,21 +2524,21 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // piece q % T of unit R * blocks + q / T.
     const bool snake = kWide && coop_units > 0;
     const bool tail_ok = OP == 0 && !store_rows && !bsplit;
-    auto tail_factor = [&](int64_t n) -> int {   // pieces per unit of n's last round
-        const int64_t left = n % blocks;
+    auto tail_factor = [&](int n) -> int {   // pieces per unit of n's last round
+        const int left = n % blocks;
         if (!tail_ok || left == 0 || 2 * left > blocks) return 1;
-        const int64_t t = blocks / left;
+        const int t = blocks / left;
         const int kmax = (k_steps / S) / 8;
         return static_cast<int>(t < kmax ? t : kmax) > 1 ? static_cast<int>(t < kmax ? t : kmax) : 1;
     };
     // the split sequence: the single snake sequence, or the wave units when
     // there are no cooperative ones
-    const int64_t seq_n = snake ? units : coop_units == 0 ? units : 0;
+    const int seq_n = snake ? units : coop_units == 0 ? units : 0;
     const int tT = seq_n > 0 ? tail_factor(seq_n) : 1;
-    const int64_t seq_full = seq_n / blocks * blocks;
-    const int64_t seq_pos = tT > 1 ? seq_full + (seq_n - seq_full) * tT : seq_n;
+    const int seq_full = seq_n / blocks * blocks;
+    const int seq_pos = tT > 1 ? seq_full + (seq_n - seq_full) * tT : seq_n;
     // position of the split sequence -> unit and piece (T = tT past seq_full)
-    auto unit_of = [&](int64_t g, int &piece) -> int64_t {
+    auto unit_of = [&](int g, int &piece) -> int {
         if (g < seq_full || tT == 1) {
             piece = 0;
             return g;
@@ -2543,36 +2546,36 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         piece = static_cast<int>((g - seq_full) % tT);
         return seq_full + (g - seq_full) / tT;
     };
-    auto g_of = [&](int64_t k) {
+    auto g_of = [&](int k) {
         return k * blocks + ((k & 1) ? blocks - 1 - xcd_block : xcd_block);
     };
-    int64_t n_coop = 0, n_wave = 0;
+    int n_coop = 0, n_wave = 0;
     if (snake) {
         // this rank's rounds: the cooperative ones, then the wave ones (g
         // grows with k)
-        for (int64_t k = 0; k * blocks < seq_pos; ++k) {
-            const int64_t g = g_of(k);
+        for (int k = 0; k * blocks < seq_pos; ++k) {
+            const int g = g_of(k);
             int pc;
-            const int64_t uu0 = g < seq_pos ? unit_of(g, pc) : units;
+            const int uu0 = g < seq_pos ? unit_of(g, pc) : units;
             n_coop += uu0 < coop_units;
             n_wave += uu0 >= coop_units && uu0 < units;
         }
     } else {
-        const int64_t wave_pos = coop_units == 0 ? seq_pos : units - coop_units;
+        const int wave_pos = coop_units == 0 ? seq_pos : units - coop_units;
         n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;
         n_wave = wave_pos > blockIdx.x ? (wave_pos - blockIdx.x + blocks - 1) / blocks : 0;
     }
-    auto coop_pos = [&](int64_t i) { return snake ? g_of(i) : xcd_block + i * blocks; };
-    auto wave_pos_of = [&](int64_t j) {
+    auto coop_pos = [&](int i) { return snake ? g_of(i) : xcd_block + i * blocks; };
+    auto wave_pos_of = [&](int j) {
         return snake ? g_of(n_coop + j) : coop_units + blockIdx.x + j * blocks;
     };
-    int64_t i_coop = 0, i_wave = 0;
-    for (int64_t uu = 0; uu < n_coop + n_wave; ++uu) {
+    int i_coop = 0, i_wave = 0;
+    for (int uu = 0; uu < n_coop + n_wave; ++uu) {
         const bool take_coop = i_wave >= n_wave ||
                                (i_coop < n_coop && ((uu + blockIdx.x) & 1) == 0);
-        const int64_t g = take_coop ? coop_pos(i_coop++) : wave_pos_of(i_wave++);
+        const int g = take_coop ? coop_pos(i_coop++) : wave_pos_of(i_wave++);
         int piece = 0;
-        const int64_t u = unit_of(g, piece);
+        const int u = unit_of(g, piece);
         // K range of a last-round piece inside its unit's range
         auto narrow = [&](int &a, int &b) {
             if (tT > 1 && g >= seq_full) {
@@ -2597,8 +2600,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             // column tile are consecutive, then the next column tile.  The
             // blocks of one XCD (consecutive units) then share both the
             // band's x1 rows and its column tiles' weights through L2.
-            const int64_t local = u - static_cast<int64_t>(e_pref) * S;
-            const int64_t per_s = static_cast<int64_t>(mg_count) * n_tiles_c;
+            const int local = u - static_cast<int>(e_pref) * S;
+            const int per_s = static_cast<int>(mg_count) * n_tiles_c;
             const int s = static_cast<int>(local / per_s);
             const int r = static_cast<int>(local - s * per_s);
             const int band = r / (kCoopBand * n_tiles_c);
@@ -2610,8 +2613,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int row0 = mg * gr + w * wr;                // this wave's rows
             const int mcount = min(wr, e_cnt - row0);
             const int m0 = e_start + (mcount > 0 ? row0 : 0);
-            int ks0 = static_cast<int>(static_cast<int64_t>(k_steps_c) * s / S);
-            int ks1 = static_cast<int>(static_cast<int64_t>(k_steps_c) * (s + 1) / S);
+            int ks0 = static_cast<int>(static_cast<int>(k_steps_c) * s / S);
+            int ks1 = static_cast<int>(static_cast<int>(k_steps_c) * (s + 1) / S);
             narrow(ks0, ks1);
             if constexpr (kTB) {
                 if (gr > kCoopRows) {
@@ -2629,8 +2632,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
                                            s_ring, w);
                 }
             } else if constexpr (kKW) {
-                int k0c = static_cast<int>(static_cast<int64_t>(k_steps_w) * s / S);
-                int k1c = static_cast<int>(static_cast<int64_t>(k_steps_w) * (s + 1) / S);
+                int k0c = static_cast<int>(static_cast<int>(k_steps_w) * s / S);
+                int k1c = static_cast<int>(static_cast<int>(k_steps_w) * (s + 1) / S);
                 narrow(k0c, k1c);
                 if (gr > kCoopRows) {
                     if (wsc_tb)
@@ -2663,7 +2666,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
                 }
             }
         } else {
-            const int64_t it = (u - coop_units) * kWavesPerBlock + w;
+            const int it = (u - coop_units) * kWavesPerBlock + w;
             if (it >= wave_items) continue;
             const int q = static_cast<int>(it / S);
             const int e = __builtin_amdgcn_readfirstlane(find_expert(s_spref, p.E, q));
@@ -2671,26 +2674,26 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
             const int e_pref = __builtin_amdgcn_readfirstlane(s_spref[e]);
             const int mt_count = (e_cnt + kTileM - 1) / kTileM;
-            const int64_t local = it - static_cast<int64_t>(e_pref) * S;
+            const int local = it - static_cast<int>(e_pref) * S;
             // items of an expert: row tiles fastest, then K ranges, then
             // column tiles; block-split: K ranges fastest (a unit's four
             // waves share the row and column tile)
             int mt, s, nt;
             if (bsplit) {
                 s = static_cast<int>(local % S);
-                const int64_t rest = local / S;
+                const int rest = local / S;
                 mt = static_cast<int>(rest % mt_count);
                 nt = static_cast<int>(rest / mt_count);
             } else {
                 mt = static_cast<int>(local % mt_count);
-                const int64_t rest = local / mt_count;
+                const int rest = local / mt_count;
                 s = static_cast<int>(rest % S);
                 nt = static_cast<int>(rest / S);
             }
             const int m0 = e_start + mt * kTileM;
             const int mcount = min(kTileM, e_cnt - mt * kTileM);
-            int ks0 = static_cast<int>(static_cast<int64_t>(k_steps) * s / S);
-            int ks1 = static_cast<int>(static_cast<int64_t>(k_steps) * (s + 1) / S);
+            int ks0 = static_cast<int>(static_cast<int>(k_steps) * s / S);
+            int ks1 = static_cast<int>(static_cast<int>(k_steps) * (s + 1) / S);
             narrow(ks0, ks1);
             char *own = s_ring + w * kRingBytes;
             char *split = bsplit ? s_ring : nullptr;
@@ -2704,8 +2707,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             } else {
                 if constexpr (kKW) {
                     if (kw_on) {
-                        int k0w = static_cast<int>(static_cast<int64_t>(k_steps_w) * s / S);
-                        int k1w = static_cast<int>(static_cast<int64_t>(k_steps_w) * (s + 1) / S);
+                        int k0w = static_cast<int>(static_cast<int>(k_steps_w) * s / S);
+                        int k1w = static_cast<int>(static_cast<int>(k_steps_w) * (s + 1) / S);
                         narrow(k0w, k1w);
                         if (wsc_tb)
                             kw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, k0w, k1w, store_rows,

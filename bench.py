@@ -227,9 +227,11 @@ def gemm1_main(args, w):
 
     ms_per_step, per_launch = time_steps(step, args, dev)
     st = launch_stats(per_launch)
-    mean_launch_ms = st["mean_launch_ms"]
     flops, alg_bytes = w.flops(), w.algorithmic_bytes()
-    achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    # average launch duration: the timed back-to-back run's total / steps (one
+    # launch per step in atomic mode); it agrees with rocprofv3's kernel-trace
+    # average, where an event pair around each launch also times its dispatch
+    achieved_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": "effective TFLOP/s (2*M*H*2I/t) + % of binding roofline, upstream gate||up "
                   "step (SwiGLU + MX quantisation)",
@@ -260,10 +262,10 @@ def gemm1_main(args, w):
             "kernel": "gemm1_swiglu_kernel (gfr gate||up grouped MXFP8 GEMM + SwiGLU + MX quant)",
             "algorithmic_bytes_per_launch": alg_bytes,
             **st,
-            "launch_timing": "an event pair around each launch, in a second pass of the "
-                             "same number of calls after the timed one",
-            "frac_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
+            "launch_timing": "achieved = bytes / (timed back-to-back run / steps); "
+                             "mean/median/min_launch_ms: an event pair around each launch "
+                             "(including its dispatch), in a second pass after the timed one",
+            "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
         },
         "cpu_baseline": None,
     }
@@ -325,12 +327,14 @@ def main():
 
     ms_per_step, per_launch = time_steps(step, args, dev)
     st = launch_stats(per_launch)
-    mean_launch_ms = st["mean_launch_ms"]
 
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    # average launch duration: the timed back-to-back run's total / steps (one
+    # launch per step in atomic mode); it agrees with rocprofv3's kernel-trace
+    # average, where an event pair around each launch also times its dispatch
+    achieved_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     # HBM bytes per launch from rocprofv3 counters of this very kernel source
     # (null when the kernel changed after the counters were taken)
     traffic = None
@@ -372,10 +376,10 @@ def main():
             "kernel": "fused_kernel (gfr grouped MXFP8 GEMM + finalize routing)",
             "algorithmic_bytes_per_launch": alg_bytes,
             **st,
-            "launch_timing": "an event pair around each launch, in a second pass of the "
-                             "same number of calls after the timed one",
-            "frac_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_frac": round(flops / (mean_launch_ms * 1e-3) / 1e12 /
+            "launch_timing": "achieved = bytes / (timed back-to-back run / steps); "
+                             "mean/median/min_launch_ms: an event pair around each launch "
+                             "(including its dispatch), in a second pass after the timed one",
+            "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 /
                                (MXFP4_PEAK_TFLOPS if w.fp8 == "e2m1" else
                                 INT8_PEAK_TOPS if w4a8 else MXFP8_PEAK_TFLOPS), 4),
         },

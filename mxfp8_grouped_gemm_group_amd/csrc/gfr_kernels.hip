@@ -1425,9 +1425,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 }
 
 // ---------------------------------------------------------------------------
-// Cooperative unit for FP8 [N, K] weights (finalize operator): RF x 128 rows
-// of one expert (wave w: rows [32 RF w, 32 RF (w + 1)) of the group) x 128
-// columns, in K steps of 128.  Every operand is staged through LDS with
+// Cooperative unit for FP8 and MXFP4 [N, K] weights (finalize operator): RF x
+// 128 rows of one expert (wave w: rows [32 RF w, 32 RF (w + 1)) of the group)
+// x 128 columns, in K steps of 128 bytes of a row (128 K, MXFP4 256 K: two
+// elements per byte).  Every operand is staged through LDS with
 // direct-to-LDS loads of whole 128-byte lines -- one load covers 8 rows (or
 // columns) x 128 B, so each line is requested once per step -- where a
 // register gather of the MFMA layout touches 32 rows x 32 B per load, and a
@@ -1438,7 +1439,8 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
 // stages: a step's loads are issued right after the barrier that frees its
 // stage, before the previous step's 16 (RF 2) MFMAs, which cover their
 // latency.  Scales: one 16-byte load per x1 row and weight column per four
-// steps (WS), or per-step dwords for shorter K ranges.
+// steps (MXFP4: two, eight scale bytes a step) (WS), or per-step dwords
+// (MXFP4: qwords) for shorter K ranges.
 // ---------------------------------------------------------------------------
 constexpr int kCkStages = 2;
 constexpr int kCkWSlot = kTileN * kStepKNK;   // 16 KB: 128 columns x 128 K
@@ -1526,6 +1528,11 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     constexpr int kWLd = kCkWSlot / 1024 / kWavesPerBlock;        // weight loads per wave: 4
     constexpr int kXLd = kXSlot / 1024;                           // x1 loads per wave: 4 RF
     constexpr int kNH = 8 + 2 * RF;                               // operand reads per half step
+    // MXFP4: a step is 128 bytes of a row = 256 K (8 scale bytes), so a
+    // 16-byte scale window covers two steps instead of four
+    constexpr bool FP4 = FMT == 4;
+    constexpr int kWin = FP4 ? 2 : 4;                             // steps per scale window
+    constexpr int kScW = FP4 ? 2 : 1;                             // scale dwords per step
     e = __builtin_amdgcn_readfirstlane(e);
     m0 = __builtin_amdgcn_readfirstlane(m0);
     mcount = __builtin_amdgcn_readfirstlane(mcount);
@@ -1536,12 +1543,13 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     const int lane = lane_id();
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
+    const int Kb = FP4 ? K / 2 : K;    // bytes of an x1 row / a weight column
     if (mcount < 0) mcount = 0;
     // x1 rows of this wave (rows past the expert's last token read as zero
     // through the range-checked descriptor), the expert's weights, the scales
-    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * Kb, static_cast<int64_t>(mcount) * Kb);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
-    const int64_t wbytes = static_cast<int64_t>(N) * K;
+    const int64_t wbytes = static_cast<int64_t>(N) * Kb;
     const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     // load v of 8 rows (columns): row 8v + l/8 fills physical chunk l%8 of its
@@ -1552,16 +1560,17 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     for (int uu = 0; uu < kWLd; ++uu) {
         const int u = w * kWLd + uu;
         const int col = n0 + 8 * u + (lane >> 3);
-        vw[uu] = (col < N ? col : n0) * K + 16 * ((lane & 7) ^ ((4 * u + (lane >> 4)) & 7));
+        vw[uu] = (col < N ? col : n0) * Kb + 16 * ((lane & 7) ^ ((4 * u + (lane >> 4)) & 7));
     }
 #pragma unroll
     for (int v = 0; v < kXLd; ++v)
-        vx[v] = (8 * v + (lane >> 3)) * K + 16 * ((lane & 7) ^ ((4 * v + (lane >> 4)) & 7));
+        vx[v] = (8 * v + (lane >> 3)) * Kb + 16 * ((lane & 7) ^ ((4 * v + (lane >> 4)) & 7));
     uint32_t o[4];
 #pragma unroll
     for (int sh = 0; sh < 4; ++sh) o[sh] = c * kStepKNK + 16 * ((2 * sh + g) ^ ((c >> 1) & 7));
     // scale rows: x1 row 32f + c (row 0 past the last token: its operand is
-    // zero), weight column 32j + c; each holds the step's four bytes
+    // zero), weight column 32j + c; each holds the step's four (FP4: eight)
+    // bytes
     int vsa[RF], vsb[4];
 #pragma unroll
     for (int f = 0; f < RF; ++f)
@@ -1578,25 +1587,27 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[f][j] = v16f{};
 
-    const int k_row = K / kStepKNK;
+    const int k_row = Kb / kStepKNK;
     const int n_steps = ks1 - ks0;
     auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
-    // WS: scale windows of four steps, [0] current / [1] next; wdl = shift of
-    // a window moved back from the row end
+    // WS: scale windows of kWin steps, [0] current / [1] next; wdl = shift
+    // of a window moved back from the row end
     v4i wa[2][RF], wb[2][4];
     int wdl[2] = {0, 0};
     auto wload = [&](int ks, int set) {
-        const int start = ks < k_row - 4 ? ks : k_row - 4;
+        const int start = ks < k_row - kWin ? ks : k_row - kWin;
         wdl[set] = ks - start;
 #pragma unroll
         for (int f = 0; f < RF; ++f)
-            wa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + 4 * start, 0, 0);
+            wa[set][f] =
+                __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + 4 * kScW * start, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            wb[set][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+            wb[set][j] =
+                __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * kScW * start, 0, 0);
     };
     // per-step scale dwords (no WS), register set = weight stage
-    uint32_t sa_r[DW][RF], sb_r[DW][4];
+    uint32_t sa_r[DW][RF][kScW], sb_r[DW][4][kScW];
     char *const wring = ring;                                  // DW weight stages
     char *const xring = ring + DW * kCkWSlot + w * kXSlot;     // this wave's DX x1 slots
     auto issue_w = [&](int ks, int ws) {
@@ -1620,11 +1631,25 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     auto issue_scales = [&](int ks, int set) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int f = 0; f < RF; ++f)
-            sa_r[set][f] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f], 4 * ks, 0);
+        for (int f = 0; f < RF; ++f) {
+            if constexpr (FP4) {
+                const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[f], 8 * ks, 0);
+                sa_r[set][f][0] = static_cast<uint32_t>(v.x);
+                sa_r[set][f][1] = static_cast<uint32_t>(v.y);
+            } else {
+                sa_r[set][f][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f], 4 * ks, 0);
+            }
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sb_r[set][j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (FP4) {
+                const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[j], 8 * ks, 0);
+                sb_r[set][j][0] = static_cast<uint32_t>(v.x);
+                sb_r[set][j][1] = static_cast<uint32_t>(v.y);
+            } else {
+                sb_r[set][j][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
     // operands of half s of the step in weight stage ws / x1 stage xs
@@ -1637,19 +1662,48 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     v4i hb[2][kNH];   // [0]: half 0 of a step, [1]: half 1
     // (x1 rows past the expert's last token are zero in LDS: the DMA reads
     // them through the range-checked descriptor)
+    // FP8: the half is one 64-K MFMA per (f, j), lane (c, g) holding bytes
+    // 16g and 32 + 16g of it; the scale of 32-block 2 s + g is byte 2 s + g
+    // of the step's dword.  FP4: the half is 128 K, two MFMAs h, lane (c, g)
+    // holding 16 bytes = K [64h + 32g, +32) of it (the chunk the FP8 read
+    // gives as its 2h-th); the scale of 32-block 4 s + 2 h + g is byte 2 h + g
+    // of the step's dword s.
     auto mma_half = [&](const v4i (&t)[kNH], int s2, int set, int wpos) {
-        const int shf = 8 * (2 * s2 + g);
+        const int sw = kScW * (wpos + wdl[0]) + (FP4 ? s2 : 0);   // window dword
+        uint32_t sa[RF], sb[4];
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-            uint32_t sa = sa_r[set][f];
-            if constexpr (WS) sa = pick(wa[0][f], wpos + wdl[0]);
-            const v8i a = cat(t[8 + 2 * f], t[8 + 2 * f + 1]);
+            sa[f] = sa_r[set][f][FP4 ? s2 : 0];
+            if constexpr (WS) sa[f] = pick(wa[0][f], sw);
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t sb = sb_r[set][j];
-                if constexpr (WS) sb = pick(wb[0][j], wpos + wdl[0]);
-                acc[f][j] = mfma<FMT, 0>(a, cat(t[2 * j], t[2 * j + 1]), acc[f][j], sa >> shf,
-                                         sb >> shf);
+        for (int j = 0; j < 4; ++j) {
+            sb[j] = sb_r[set][j][FP4 ? s2 : 0];
+            if constexpr (WS) sb[j] = pick(wb[0][j], sw);
+        }
+        if constexpr (FP4) {
+            const v4i z = {0, 0, 0, 0};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int shf = 8 * (2 * h + g);
+#pragma unroll
+                for (int f = 0; f < RF; ++f) {
+                    const v8i a = cat(t[8 + 2 * f + h], z);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[f][j] = mfma<FMT, 0>(a, cat(t[2 * j + h], z), acc[f][j],
+                                                 sa[f] >> shf, sb[j] >> shf);
+                }
+            }
+        } else {
+            const int shf = 8 * (2 * s2 + g);
+#pragma unroll
+            for (int f = 0; f < RF; ++f) {
+                const v8i a = cat(t[8 + 2 * f], t[8 + 2 * f + 1]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[f][j] = mfma<FMT, 0>(a, cat(t[2 * j], t[2 * j + 1]), acc[f][j],
+                                             sa[f] >> shf, sb[j] >> shf);
             }
         }
     };
@@ -1697,7 +1751,7 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
             const bool live = i < n_steps;
             const int xn = xs + 1 == DX ? 0 : xs + 1;   // x1 stage of step i + 1
             read_half(d, xs, 1, hb[1]);
-            if (live) mma_half(hb[0], 0, d, i & 3);   // padding steps past the range: none
+            if (live) mma_half(hb[0], 0, d, i & (kWin - 1));   // padding steps past the range: none
             lds_wait_all(hb[1]);
             if constexpr (WS)
                 wait_vmcnt<kXLd>();
@@ -1707,16 +1761,16 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
             __builtin_amdgcn_sched_barrier(0);
             read_half((d + 1) % DW, xn, 0, hb[0]);
             if constexpr (WS) {
-                if (((i + 2) & 3) == 0) wload(step_of(i + 2), 1);
+                if (((i + 2) & (kWin - 1)) == 0) wload(step_of(i + 2), 1);
             }
             issue_w(step_of(i + 2), d);
             issue_x(step_of(i + DX), xs);
-            if (live) mma_half(hb[1], 1, d, i & 3);
+            if (live) mma_half(hb[1], 1, d, i & (kWin - 1));
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (!WS) issue_scales(step_of(i + 2), d);
             lds_wait_all(hb[0]);
             if constexpr (WS) {
-                if ((i & 3) == 3) {   // the next window becomes current
+                if ((i & (kWin - 1)) == kWin - 1) {   // the next window becomes current
 #pragma unroll
                     for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
 #pragma unroll
@@ -1990,8 +2044,9 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
 }
 
 // ---------------------------------------------------------------------------
-// Wave item for FP8 [N, K] weights (finalize operator, experts below the
-// cooperative size): 32 tokens x 128 columns, K steps of 128, one wave.
+// Wave item for FP8 and MXFP4 [N, K] weights (finalize operator, experts
+// below the cooperative size): 32 tokens x 128 columns, K steps of 128 bytes
+// of a row (MXFP4: 256 K), one wave.
 // The weight tile moves global -> LDS in the cooperative units' slot layout
 // (16 loads of 8 columns x 128 B per step, two 16 KB stages per wave);
 // the x1 rows go to registers in the MFMA layout (four 32-row gathers per
@@ -2009,6 +2064,9 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
     constexpr int D = kCkStages;
     static_assert(D * kCkWSlot <= kRingBytes, "a wave's stages fit its ring");
     constexpr int kWLd = kCkWSlot / 1024;   // 16 weight loads per step
+    constexpr bool FP4 = FMT == 4;          // 128 bytes a step = 256 K, 8 scale bytes
+    constexpr int kWin = FP4 ? 2 : 4;       // steps per 16-byte scale window
+    constexpr int kScW = FP4 ? 2 : 1;       // scale dwords per step
     e = __builtin_amdgcn_readfirstlane(e);
     m0 = __builtin_amdgcn_readfirstlane(m0);
     mcount = __builtin_amdgcn_readfirstlane(mcount);
@@ -2018,26 +2076,27 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
     const int lane = lane_id();
     const int c = lane & 31, g = lane >> 5;
     const int K = p.K, N = p.N, KS = p.K / 32;
+    const int Kb = FP4 ? K / 2 : K;         // bytes of an x1 row / a weight column
     if (mcount < 0) mcount = 0;
-    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * K, static_cast<int64_t>(mcount) * K);
+    const rsrc_t ra = make_rsrc(p.x1 + static_cast<int64_t>(m0) * Kb, static_cast<int64_t>(mcount) * Kb);
     const rsrc_t rsa = make_rsrc(p.pts + static_cast<int64_t>(m0) * KS, static_cast<int64_t>(mcount) * KS);
-    const int64_t wbytes = static_cast<int64_t>(N) * K;
+    const int64_t wbytes = static_cast<int64_t>(N) * Kb;
     const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
-    // load u of 8 columns: column n0 + 8u + l/8 (lane offset below, 8u K in the
-    // scalar offset; columns past N lie past the expert's slice and read as
+    // load u of 8 columns: column n0 + 8u + l/8 (lane offset below, 8u rows in
+    // the scalar offset; columns past N lie past the expert's slice and read as
     // zero), physical chunk l%8 holding logical chunk (l%8) ^ ((4u + l/16) & 7)
     int vw[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par)
-        vw[par] = (n0 + (lane >> 3)) * K + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7));
+        vw[par] = (n0 + (lane >> 3)) * Kb + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7));
     uint32_t o[4];
 #pragma unroll
     for (int sh = 0; sh < 4; ++sh) o[sh] = c * kStepKNK + 16 * ((2 * sh + g) ^ ((c >> 1) & 7));
     // x1: lane (c, g) gathers row c's bytes 32q + 16g of the step (rows past
     // the last token read as zero); its scales sit in row c (row 0 past it)
     const int arow = c < mcount ? c : 0;
-    const int va = arow * K + 16 * g;
+    const int va = arow * Kb + 16 * g;
     const int vsa = arow * KS;
     int vsb[4];
 #pragma unroll
@@ -2050,35 +2109,36 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[0][j] = v16f{};
 
-    const int k_row = K / kStepKNK;
+    const int k_row = Kb / kStepKNK;
     const int n_steps = ks1 - ks0;
     auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
-    v4i wa[2], wb[2][4];   // WS windows of four steps: [0] current, [1] next
+    v4i wa[2], wb[2][4];   // WS windows of kWin steps: [0] current, [1] next
     int wdl[2] = {0, 0};
     auto wload = [&](int ks, int set) {
-        const int start = ks < k_row - 4 ? ks : k_row - 4;
+        const int start = ks < k_row - kWin ? ks : k_row - kWin;
+        const int off = 4 * kScW * start;
         wdl[set] = ks - start;
         if (set) {
-            wa[1] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa + 4 * start, 0, 0);
+            wa[1] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa + off, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                wb[1][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+                wb[1][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + off, 0, 0);
         } else {
-            wa[0] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa + 4 * start, 0, 0);
+            wa[0] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa + off, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                wb[0][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + 4 * start, 0, 0);
+                wb[0][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + off, 0, 0);
         }
     };
-    v4i xr[D][4];                 // x1 operands of a step, register set = stage
-    uint32_t sa_r[D], sb_r[D][4];  // per-step scale dwords (no WS)
+    v4i xr[D][4];                             // x1 operands of a step, register set = stage
+    uint32_t sa_r[D][kScW], sb_r[D][4][kScW];  // per-step scale dwords (no WS)
     auto issue_dma = [&](int ks, int stage) {
         char *st = ring + stage * kCkWSlot;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kWLd; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + u * 1024), 16,
-                                                     vw[u & 1], 8 * u * K + ks * kStepKNK, 0, 0);
+                                                     vw[u & 1], 8 * u * Kb + ks * kStepKNK, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto issue_regs = [&](int ks, int set) {
@@ -2086,11 +2146,21 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             xr[set][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, ks * kStepKNK + 32 * q, 0);
-        if constexpr (!WS) {
-            sa_r[set] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, 4 * ks, 0);
+        if constexpr (!WS && FP4) {
+            const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa, 8 * ks, 0);
+            sa_r[set][0] = static_cast<uint32_t>(v.x);
+            sa_r[set][1] = static_cast<uint32_t>(v.y);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v2i u = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[j], 8 * ks, 0);
+                sb_r[set][j][0] = static_cast<uint32_t>(u.x);
+                sb_r[set][j][1] = static_cast<uint32_t>(u.y);
+            }
+        } else if constexpr (!WS) {
+            sa_r[set][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, 4 * ks, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                sb_r[set][j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
+                sb_r[set][j][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vsb[j], 4 * ks, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -2099,17 +2169,35 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
         lds_issue_w8(base + o[2 * s2], base + o[2 * s2 + 1], t);
     };
     v4i hb[2][8];
+    // operands and scale bytes as in ck_unit's halves (FP4: two MFMAs h per
+    // half, x1 bytes 32 h + 16 g of the half = xr[2 s + h])
     auto mma_half = [&](const v4i (&t)[8], int s2, int set, int wpos) {
-        const int shf = 8 * (2 * s2 + g);
-        uint32_t sa = sa_r[set];
-        if constexpr (WS) sa = pick(wa[0], wpos + wdl[0]);
-        const v8i a = cat(xr[set][2 * s2], xr[set][2 * s2 + 1]);
+        const int sw = kScW * (wpos + wdl[0]) + (FP4 ? s2 : 0);   // window dword
+        uint32_t sa = sa_r[set][FP4 ? s2 : 0], sb[4];
+        if constexpr (WS) sa = pick(wa[0], sw);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t sb = sb_r[set][j];
-            if constexpr (WS) sb = pick(wb[0][j], wpos + wdl[0]);
-            acc[0][j] = mfma<FMT, 0>(a, cat(t[2 * j], t[2 * j + 1]), acc[0][j], sa >> shf,
-                                     sb >> shf);
+            sb[j] = sb_r[set][j][FP4 ? s2 : 0];
+            if constexpr (WS) sb[j] = pick(wb[0][j], sw);
+        }
+        if constexpr (FP4) {
+            const v4i z = {0, 0, 0, 0};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int shf = 8 * (2 * h + g);
+                const v8i a = cat(xr[set][2 * s2 + h], z);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[0][j] = mfma<FMT, 0>(a, cat(t[2 * j + h], z), acc[0][j], sa >> shf,
+                                             sb[j] >> shf);
+            }
+        } else {
+            const int shf = 8 * (2 * s2 + g);
+            const v8i a = cat(xr[set][2 * s2], xr[set][2 * s2 + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[0][j] = mfma<FMT, 0>(a, cat(t[2 * j], t[2 * j + 1]), acc[0][j], sa >> shf,
+                                         sb[j] >> shf);
         }
     };
 
@@ -2136,21 +2224,21 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
             const int i = i0 + d;
             const bool live = i < n_steps;
             read_half(d, 1, hb[1]);
-            if (live) mma_half(hb[0], 0, d, i & 3);
+            if (live) mma_half(hb[0], 0, d, i & (kWin - 1));
             lds_wait_all(hb[1]);
             wait_vmcnt<0>();
             __builtin_amdgcn_sched_barrier(0);
             read_half((d + 1) % D, 0, hb[0]);
             if constexpr (WS) {
-                if (((i + D) & 3) == 0) wload(step_of(i + D), 1);
+                if (((i + D) & (kWin - 1)) == 0) wload(step_of(i + D), 1);
             }
             issue_dma(step_of(i + D), d);
-            if (live) mma_half(hb[1], 1, d, i & 3);
+            if (live) mma_half(hb[1], 1, d, i & (kWin - 1));
             __builtin_amdgcn_sched_barrier(0);
             issue_regs(step_of(i + D), d);
             lds_wait_all(hb[0]);
             if constexpr (WS) {
-                if ((i & 3) == 3) {   // the next window becomes current
+                if ((i & (kWin - 1)) == kWin - 1) {   // the next window becomes current
                     wa[0] = wa[1];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) wb[0][j] = wb[1][j];
@@ -2412,15 +2500,17 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // output columns per item: the weight columns, or for the upstream step
     // half of them ([N,K]: gate and up columns in one tile) or all of them
     // ([K,N]: gate and up tiles streamed in turn)
-    // FP8 [N, K] finalize: ck_unit / cw_item, 128-column tiles for both kinds
-    constexpr bool kTB = TRANS && (FMT == 0 || FMT == 1) && OP == 0;
+    // FP8 and MXFP4 [N, K] finalize: ck_unit / cw_item, 128-column tiles for
+    // both kinds
+    constexpr bool kTB = TRANS && (FMT == 0 || FMT == 1 || FMT == 4) && OP == 0;
     constexpr int kOutN = kTB ? kTileN : OP == 0 || !TRANS ? kTN : kTN / 2;
     const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
     constexpr int kOutNC = kOutN;                   // output columns per cooperative unit
     const int n_tiles_c = n_tiles;
     WorkList wl{s_start, s_cnt, s_spref, s_lpref, s_perm, 0, 0, 0, 0};
-    // two-fragment cooperative groups except where a fragment has 8 accumulators
-    constexpr bool kWide = FMT != 4 && FMT != 8 && !(OP == 1 && !TRANS);
+    // two-fragment cooperative groups except where a fragment has 8
+    // accumulators (MXFP4 and W4A8 [K, N], the upstream step with [K, N])
+    constexpr bool kWide = FMT != 8 && !(OP == 1 && !TRANS) && (FMT != 4 || TRANS);
     build_work_list<kWide>(p, n_tiles, n_tiles_c, wl, s_scan);
     if (OP == 0 && p.det_total && blockIdx.x == 0 && threadIdx.x == 0)
         *p.det_total = wl.routed_tokens;

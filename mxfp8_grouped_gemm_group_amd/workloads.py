@@ -241,6 +241,17 @@ SMALL_BIG_T_FP4 = _reg(replace(SMALL_BIG_T, name="small_big_t_fp4", fp8="e2m1", 
                                seed=1042))
 SMALL_T_FP4_K1280 = _reg(replace(SMALL_T, name="small_t_fp4_k1280", fp8="e2m1", K=1280,
                                  seed=1051))
+# ... K = 256 (one 256-K step per row: per-step scale loads) in cooperative
+# units of both sizes and wave items; the K-split, short-last-round and
+# many-cooperative-expert cases in MXFP4 (32, 16 and 4 steps of 256 K)
+SMALL_BIG_T_FP4_K256 = _reg(replace(SMALL_BIG_T, name="small_big_t_fp4_k256", fp8="e2m1",
+                                    K=256, seed=1054))
+SMALL_SPLIT_T_FP4 = _reg(replace(SMALL_SPLIT_T, name="small_split_t_fp4", fp8="e2m1", K=8192,
+                                 seed=1055))
+SMALL_TAIL_T_FP4 = _reg(replace(SMALL_TAIL_T, name="small_tail_t_fp4", fp8="e2m1", K=4096,
+                                seed=1056))
+SMALL_MANY_T_FP4 = _reg(replace(SMALL_MANY_T, name="small_many_t_fp4", fp8="e2m1", K=1024,
+                                seed=1057))
 C2_FP4 = _reg(replace(C2, name="c2_fp4", fp8="e2m1", seed=1043))
 C3_FP4T = _reg(replace(C3, name="c3_fp4t", fp8="e2m1", transpose_x2=True, seed=1044))
 C5_FP4 = _reg(replace(C5, name="c5_fp4", fp8="e2m1", seed=1045))
@@ -269,7 +280,8 @@ for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SM
               SMALL_COOP_T_K128, SMALL_SPLIT_N, SMALL_SPLIT_T, SMALL_TAIL_N, SMALL_TAIL_T,
               SMALL_HUGE_T, SMALL_MANY_N, SMALL_MANY_T, SMALL_T_K768,
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
-              SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, C3_FP4T, SMALL_N_FP4,
+              SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, SMALL_BIG_T_FP4_K256,
+              SMALL_SPLIT_T_FP4, SMALL_TAIL_T_FP4, SMALL_MANY_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))

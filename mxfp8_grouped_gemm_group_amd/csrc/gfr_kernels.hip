@@ -802,6 +802,26 @@ __device__ __forceinline__ uint32_t pick(const v4i &w, int k) {
     return static_cast<uint32_t>(k <= 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w);
 }
 
+// Rotation of an [N, K] wave item's K order.  A step reads the same 128-byte
+// piece of 128 weight rows (columns); where a row is 4 KB long (MXFP4 K 8192)
+// every item in flight then hits the same in-row offset, the rows of
+// different column tiles and experts lie a multiple of 512 KB apart, and the
+// reads crowd onto a few memory channels: streaming 128 rows x 4 KB this way
+// ran at 3.9 TB/s, against 5.6 with each item starting at its own step, the
+// same as reading the bytes in order (c3_fp4t 149 -> 116 µs).  So an item
+// runs its steps from ks0 + rot to ks1 - 1, then from ks0 to ks0 + rot - 1,
+// rot chosen by expert: the column tiles of one expert keep the same order,
+// as they share its x1 rows through L2 (keyed on the column tile as well, c5
+// ran 2 % slower).  With scale windows of WIN steps, rot = n mod WIN + WIN h
+// (n steps in the range): the wrap then falls on a window boundary.  The
+// addition order changes with rot; the sum does not.  The cooperative units
+// keep the plain order (rotated, c5 ran 1-3 % slower).
+__device__ __forceinline__ int k_rotation(int e, int n, int win) {
+    const int q = n / win;   // whole windows in the range
+    if (q < 2) return 0;
+    return n % win + win * (e % q);
+}
+
 // split: the block's LDS ring when the item is one of a block-split wave
 // unit's four K ranges (split_epilogue), else null.
 template <int FMT, bool KN, bool COOP, int RF, int OP, bool WS = false>
@@ -1341,7 +1361,12 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     static_assert((D - 1) * kOpsPerStep < 64 && (D - 2) * kOpsPerStep + kXW < 64, "vmcnt range");
     static_assert(D % 2 == 0, "operand double buffer alternates with the slot index");
     const int n_steps = (ks1 - ks0) * kVS;        // virtual steps
-    auto step_of = [&](int i) { return ks0 * kVS + (i < n_steps ? i : n_steps - 1); };
+    // [N, K] wave items: rotated K order (windows of four steps)
+    const int rot = !KN && !COOP ? k_rotation(e, n_steps, WS ? 4 : 1) : 0;
+    auto step_of = [&](int i) {
+        const int j = (i < n_steps ? i : n_steps - 1) + rot;
+        return ks0 * kVS + (j < n_steps ? j : j - n_steps);
+    };
 
     if constexpr (WS) wload(step_of(0), 0);   // older than every step's loads
 #pragma unroll
@@ -2111,7 +2136,11 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
 
     const int k_row = Kb / kStepKNK;
     const int n_steps = ks1 - ks0;
-    auto step_of = [&](int i) { return ks0 + (i < n_steps ? i : n_steps - 1); };
+    const int rot = k_rotation(e, n_steps, WS ? kWin : 1);
+    auto step_of = [&](int i) {   // rotated; past the range: the last step again
+        const int j = (i < n_steps ? i : n_steps - 1) + rot;
+        return ks0 + (j < n_steps ? j : j - n_steps);
+    };
     v4i wa[2], wb[2][4];   // WS windows of kWin steps: [0] current, [1] next
     int wdl[2] = {0, 0};
     auto wload = [&](int ks, int set) {

@@ -79,6 +79,69 @@ __device__ __forceinline__ int lane_id() {
     return l;
 }
 
+// Lane l of the wave gets v[0] op v[1] op ... op v[l]: DPP row shifts within
+// each row of 16 lanes, then row broadcasts of lanes 15 and 31 (gfx9 DPP),
+// seven steps without LDS traffic (a shuffle scan moves every step through
+// the LDS crossbar: the work-list build's four scans took 0.7-1.3 µs each).
+// op is associative with identity 0; every lane of the wave takes part.
+template <int CTRL, int ROWS, int BANKS, bool BOUND>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {   // lanes not written give 0
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROWS, BANKS, BOUND));
+}
+template <class F>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, F op) {
+    uint32_t x = op(v, dpp_u32<0x111, 0xf, 0xf, true>(v));   // row_shr:1
+    x = op(x, dpp_u32<0x112, 0xf, 0xf, true>(v));            // row_shr:2
+    x = op(x, dpp_u32<0x113, 0xf, 0xf, true>(v));            // row_shr:3
+    x = op(x, dpp_u32<0x114, 0xf, 0xe, false>(x));           // row_shr:4 into lanes 4-15
+    x = op(x, dpp_u32<0x118, 0xf, 0xc, false>(x));           // row_shr:8 into lanes 8-15
+    x = op(x, dpp_u32<0x142, 0xa, 0xf, false>(x));           // row_bcast:15 into rows 1, 3
+    x = op(x, dpp_u32<0x143, 0xc, 0xf, false>(x));           // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// Exclusive block-wide scans of NV 32-bit values per thread at once (v is
+// replaced by its exclusive prefix, total gets the block's): wave scans,
+// then the wave totals through LDS (s: 4 NV words; two barriers in all).
+template <int NV, class F>
+__device__ __forceinline__ void block_scan_u32(uint32_t (&v)[NV], uint32_t (&total)[NV],
+                                               uint32_t *s, F op) {
+    const int lane = threadIdx.x & (kWaveSize - 1), wv = threadIdx.x / kWaveSize;
+    uint32_t ex[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        const uint32_t x = wave_incl_scan(v[n], op);
+        if (lane == kWaveSize - 1) s[wv * NV + n] = x;
+        ex[n] = dpp_u32<0x138, 0xf, 0xf, true>(x);   // wave_shr:1: lane l - 1's, lane 0 0
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            const uint32_t t = s[i * NV + n];
+            if (i < wv) before = op(before, t);
+            all = op(all, t);
+        }
+        total[n] = all;
+        v[n] = op(before, ex[n]);
+    }
+    __syncthreads();   // s may be reused after return
+}
+
+struct AddU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+// a + b saturated at cap (a, b <= cap): associative, identity 0
+struct SatAddU32 {
+    uint32_t cap;
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+        return a >= cap - b ? cap : a + b;
+    }
+};
+
 // Exclusive block-wide prefix sum: a shuffle scan within each wave, then the
 // wave totals through LDS (two barriers in all).
 template <class T>
@@ -169,6 +232,7 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
     int c[kPerThread];
     int64_t csum = 0;
     bool bad = false;
+    uint32_t *const s32 = reinterpret_cast<uint32_t *>(s_scan);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = e0 + i;
@@ -181,11 +245,15 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         c[i] = static_cast<int>(v);
         csum += c[i];
     }
-    // 64-bit: with invalid lists the raw sum can exceed M many times over.
-    int64_t total_tokens = 0;
-    int64_t run = block_exclusive_scan<int64_t>(csum, s_scan, total_tokens);
-    // Both item counts in one 64-bit scan: wave items low, block items high
-    // (each total stays below 2^31: the host bounds (M/32 + E) * ceil(N/128)).
+    // With invalid lists the raw sum can exceed M many times over: the scan
+    // saturates at M + 1 (every prefix above M is treated alike below).
+    const uint32_t cap = static_cast<uint32_t>(p.M) + 1u;
+    uint32_t tok[1] = {static_cast<uint32_t>(csum < cap ? csum : cap)}, tok_total[1];
+    block_scan_u32<1>(tok, tok_total, s32, SatAddU32{cap});
+    const int64_t total_tokens = tok_total[0];
+    int64_t run = tok[0];
+    // Both item counts: wave items low, block items high (each total stays
+    // below 2^31: the host bounds (M/32 + E) * ceil(N/128)).
     int64_t isum = 0;
     int64_t items[kPerThread];
     int ccnt[kPerThread];
@@ -206,8 +274,10 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         items[i] = si | (li << 32);
         isum += items[i];
     }
-    int64_t total_items = 0;
-    int64_t ipre = block_exclusive_scan<int64_t>(isum, s_scan, total_items);
+    uint32_t iv[2] = {static_cast<uint32_t>(isum), static_cast<uint32_t>(isum >> 32)}, it[2];
+    block_scan_u32<2>(iv, it, s32, AddU32{});
+    const int64_t total_items = static_cast<int64_t>(it[0]) | (static_cast<int64_t>(it[1]) << 32);
+    int64_t ipre = static_cast<int64_t>(iv[0]) | (static_cast<int64_t>(iv[1]) << 32);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
@@ -260,8 +330,10 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         ord[i] = coop ? ((2 * kCoopRows - key) << 10) | e : -1;
         ncoop += coop;
     }
-    int n_ce = 0;
-    int slot = block_exclusive_scan<int>(ncoop, reinterpret_cast<int *>(s_scan), n_ce);
+    uint32_t sl[1] = {static_cast<uint32_t>(ncoop)}, sl_total[1];
+    block_scan_u32<1>(sl, sl_total, s32, AddU32{});
+    const int n_ce = static_cast<int>(sl_total[0]);
+    int slot = static_cast<int>(sl[0]);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i)
         if (ord[i] >= 0) wl.perm[slot++] = ord[i];
@@ -283,16 +355,16 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
     for (int i = 0; i < kPerThread; ++i)
         if (ord[i] >= 0) wl.perm[rank[i]] = tid * kPerThread + i;
     __syncthreads();
-    int64_t lv[kPerThread];
-    int64_t lsum = 0;
+    int lv[kPerThread];
+    uint32_t lsum[1] = {0}, ltotal[1];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int r = tid * kPerThread + i;
         lv[i] = r < n_ce ? wl.lpref[wl.perm[r] + 1] - wl.lpref[wl.perm[r]] : 0;
-        lsum += lv[i];
+        lsum[0] += static_cast<uint32_t>(lv[i]);
     }
-    int64_t ltotal = 0;
-    int64_t lpre = block_exclusive_scan<int64_t>(lsum, s_scan, ltotal);   // ends synchronised
+    block_scan_u32<1>(lsum, ltotal, s32, AddU32{});   // ends synchronised
+    int lpre = static_cast<int>(lsum[0]);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int r = tid * kPerThread + i;
@@ -2670,15 +2742,20 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     };
     int n_coop = 0, n_wave = 0;
     if (snake) {
-        // this rank's rounds: the cooperative ones, then the wave ones (g
-        // grows with k)
-        for (int k = 0; k * blocks < seq_pos; ++k) {
-            const int g = g_of(k);
-            int pc;
-            const int uu0 = g < seq_pos ? unit_of(g, pc) : units;
-            n_coop += uu0 < coop_units;
-            n_wave += uu0 >= coop_units && uu0 < units;
-        }
+        // this rank's rounds: the cooperative ones (positions below g_coop,
+        // where the wave units start), then the wave ones.  g_of(k) lies in
+        // [k blocks, (k + 1) blocks), so the rounds below position X are
+        // X / blocks and possibly one more.  (In closed form: a loop over the
+        // rounds took 3 µs of c5's start with its integer divisions.)
+        auto rounds_below = [&](int X) {
+            const int kq = X / blocks;
+            return kq + (g_of(kq) < X ? 1 : 0);
+        };
+        const int g_coop = coop_units <= seq_full || tT == 1
+                               ? coop_units
+                               : seq_full + (coop_units - seq_full) * tT;
+        n_coop = rounds_below(g_coop < seq_pos ? g_coop : seq_pos);
+        n_wave = rounds_below(seq_pos) - n_coop;
     } else {
         const int wave_pos = coop_units == 0 ? seq_pos : units - coop_units;
         n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;

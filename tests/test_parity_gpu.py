@@ -291,6 +291,30 @@ def test_device_status_bits():
     assert int(status.item()) & gfr.DEV_BAD_GROUP_LIST
 
 
+def test_invalid_group_list_clamped_bitwise_exact():
+    """An invalid group_list is clamped into [0, M) and flagged: counts past
+    the rows left (one as large as 2^40) and negative counts (a decreasing
+    prefix list) give exactly the valid list with the clamped ranges
+    (integer-exact data, so any summation order gives the same bits)."""
+    gfr = _gfr()
+    w = WORKLOADS["small_n_exact"]                  # counts (0, 37, 1, 120, 0, 95, 47), M 300
+    inp = make_inputs(w, DEV)
+    valid = torch.tensor([0, 37, 1, 262, 0, 0, 0], dtype=torch.int64, device=DEV)
+    want = run_gpu(dict(inp, group_list=valid))
+    ref, mag = run_oracle(dict(inp, group_list=valid))
+    assert_parity(want, ref, mag, exact=True, what="clamped ranges")
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    counts = torch.tensor([0, 37, 1, 1 << 40, 5, 95, 47], dtype=torch.int64, device=DEV)
+    got = run_gpu(dict(inp, group_list=counts), status=status)
+    assert int(status.item()) & gfr.DEV_BAD_GROUP_LIST
+    assert torch.equal(got, want)
+    status.zero_()
+    prefix = torch.tensor([0, 37, 38, 5000, 4000, 300, 300], dtype=torch.int64, device=DEV)
+    got = run_gpu(dict(inp, group_list=prefix, group_list_type=0), status=status)
+    assert int(status.item()) & gfr.DEV_BAD_GROUP_LIST
+    assert torch.equal(got, want)
+
+
 def test_group_list_type_equivalence_bitwise_exact():
     w = WORKLOADS["small_n_exact"]
     inp = make_inputs(w, DEV)

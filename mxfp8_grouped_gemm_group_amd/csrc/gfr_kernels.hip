@@ -81,9 +81,9 @@ __device__ __forceinline__ int lane_id() {
 
 // Lane l of the wave gets v[0] op v[1] op ... op v[l]: DPP row shifts within
 // each row of 16 lanes, then row broadcasts of lanes 15 and 31 (gfx9 DPP),
-// seven steps without LDS traffic (a shuffle scan moves every step through
-// the LDS crossbar: the work-list build's four scans took 0.7-1.3 µs each).
-// op is associative with identity 0; every lane of the wave takes part.
+// seven steps that stay in the VALU (a shuffle scan sends every step through
+// the LDS crossbar).  op is associative with identity 0; every lane of the
+// wave takes part.
 template <int CTRL, int ROWS, int BANKS, bool BOUND>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {   // lanes not written give 0
     return static_cast<uint32_t>(

@@ -668,34 +668,42 @@ __device__ __forceinline__ void epilogue(const FusedParams &p, const v16f (&accs
 }
 
 // Epilogue of a block-split wave unit: the block's four waves computed four
-// K ranges of one item (same 32 rows, same 128 columns).  Each wave leaves
-// its four accumulator groups in its own 16 KB of the LDS ring, as [group
-// j][register r][lane] (every store and load covers 64 consecutive dwords);
-// after a block barrier wave w adds up the four waves' group w in wave order
-// and scatters columns n0 + 32w .. n0 + 32w + 31.  One atomic per output
-// element instead of one per K range.  Every wave of the block must call it
-// (block barrier), each after its last read of its own ring region.
-__device__ __forceinline__ void split_epilogue(const FusedParams &p, const v16f (&acc)[1][4],
+// K ranges of one item (same 32 rows, same 32 NA columns: NA = 4, or 8 for
+// MXFP4 [K,N]).  Each wave leaves its NA accumulator groups in its own part
+// of the LDS ring (NA x 4 KB), as [group j][register r][lane] (every store
+// and load covers 64 consecutive dwords); after a block barrier wave w adds
+// up the four waves' groups NA/4 w .. NA/4 (w + 1) - 1 in wave order and
+// scatters their columns.  One atomic per output element instead of one per
+// K range.  Every wave of the block must call it (block barrier), each after
+// its last read of its own ring region.
+template <int NA>
+__device__ __forceinline__ void split_epilogue(const FusedParams &p, const v16f (&acc)[1][NA],
                                                int m0, int n0, bool store_rows, RowInfo ri,
                                                char *ring) {
+    constexpr int G = NA / kWavesPerBlock;   // groups summed by each wave
+    static_assert(NA % kWavesPerBlock == 0 && NA * 16 * kWaveSize * 4 <= kRingBytes,
+                  "a wave's accumulators fit its ring region");
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     float *own = reinterpret_cast<float *>(ring + w * kRingBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NA; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) own[(16 * j + r) * kWaveSize + lane] = acc[0][j][r];
     __syncthreads();
-    v16f sum = v16f{};
+    v16f sum[1][G];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) sum[0][jj] = v16f{};
 #pragma unroll
     for (int w2 = 0; w2 < kWavesPerBlock; ++w2) {
         const float *src = reinterpret_cast<const float *>(ring + w2 * kRingBytes) +
-                           16 * w * kWaveSize + lane;
+                           16 * G * w * kWaveSize + lane;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] += src[r * kWaveSize];
+        for (int jj = 0; jj < G; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[0][jj][r] += src[(16 * jj + r) * kWaveSize];
     }
-    const v16f one[1][1] = {{sum}};
-    epilogue<1, 1, 1>(p, one, m0, n0 + 32 * w, store_rows, ri);
+    epilogue<G, 1, G>(p, sum, m0, n0 + 32 * G * w, store_rows, ri);
 }
 
 // W4A8 epilogue.  acc[f][j] / acc[f][4 + j] hold 16 * the exact integer
@@ -1512,11 +1520,11 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         epilogue_swiglu<SPLIT ? 8 : 2, RF, NA>(p, acc, m0, mcount, n0);
     else if constexpr (I8)
         epilogue_w4a8<RF>(p, acc, rsum, cscale, m0, n0, store_rows, rinfo);
-    else if constexpr (KN && !KN4 && !COOP && RF == 1 && NA == 4) {
+    else if constexpr (KN && !COOP && RF == 1 && OP == 0) {
         if (split)
-            split_epilogue(p, acc, m0, n0, store_rows, rinfo, split);
+            split_epilogue<NA>(p, acc, m0, n0, store_rows, rinfo, split);
         else
-            epilogue<4, 1, 4>(p, acc, m0, n0, store_rows, rinfo);
+            epilogue<NA, 1, NA>(p, acc, m0, n0, store_rows, rinfo);
     } else
         epilogue<KN4 ? 8 : KN ? 4 : 2, RF, NA>(p, acc, m0, n0, store_rows, rinfo);
 }
@@ -2662,7 +2670,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // ranges.  c1 (16 tokens per expert, four ranges) spends a fifth of its
     // time in atomics otherwise.  An explicit split that is not a multiple of
     // four keeps one item per wave.
-    constexpr bool kSplitOK = OP == 0 && (FMT == 0 || FMT == 1);
+    constexpr bool kSplitOK = OP == 0 && (FMT == 0 || FMT == 1 || FMT == 4);
     const bool bsplit = kSplitOK && !store_rows && wl.litems == 0 && S >= kWavesPerBlock &&
                         (p.split_k <= 0 || p.split_k % kWavesPerBlock == 0);
     if (bsplit) S -= S % kWavesPerBlock;

@@ -256,8 +256,10 @@ C2_FP4 = _reg(replace(C2, name="c2_fp4", fp8="e2m1", seed=1043))
 C3_FP4T = _reg(replace(C3, name="c3_fp4t", fp8="e2m1", transpose_x2=True, seed=1044))
 C5_FP4 = _reg(replace(C5, name="c5_fp4", fp8="e2m1", seed=1045))
 # ... and with [K, N] x2 packed along N (N a multiple of 32); K = 640 is not a
-# multiple of 256.
+# multiple of 256; small_split_n_fp4 has 32 K steps of 64 (block-split units).
 SMALL_N_FP4 = _reg(replace(SMALL_N, name="small_n_fp4", fp8="e2m1", seed=1046))
+SMALL_SPLIT_N_FP4 = _reg(replace(SMALL_SPLIT_N, name="small_split_n_fp4", fp8="e2m1",
+                                 seed=1058))
 SMALL_BIG_N_FP4 = _reg(replace(SMALL_BIG_N, name="small_big_n_fp4", fp8="e2m1", K=640,
                                seed=1047))
 C1_FP4 = _reg(replace(C1, name="c1_fp4", fp8="e2m1", seed=1048))
@@ -282,6 +284,7 @@ for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SM
               SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, SMALL_BIG_T_FP4_K256,
               SMALL_SPLIT_T_FP4, SMALL_TAIL_T_FP4, SMALL_MANY_T_FP4, C3_FP4T, SMALL_N_FP4,
+              SMALL_SPLIT_N_FP4,
               SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))

@@ -135,7 +135,8 @@ def slack_for(inp, rows=None):
                                   "small_big_t_fp4_k256", "small_big_t_fp4_k256_exact",
                                   "small_split_t_fp4", "small_split_t_fp4_exact",
                                   "small_tail_t_fp4", "small_tail_t_fp4_exact",
-                                  "small_many_t_fp4", "small_many_t_fp4_exact"])
+                                  "small_many_t_fp4", "small_many_t_fp4_exact",
+                                  "small_split_n_fp4", "small_split_n_fp4_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]
@@ -152,7 +153,8 @@ def test_small_full(name, split_k):
 # scatter (8: two such blocks per item, each with its own atomics).
 @pytest.mark.parametrize("name", ["small_split_n", "small_split_t", "small_split_n_exact",
                                   "small_split_t_exact", "small_split_t_fp4",
-                                  "small_split_t_fp4_exact"])
+                                  "small_split_t_fp4_exact", "small_split_n_fp4",
+                                  "small_split_n_fp4_exact"])
 @pytest.mark.parametrize("split_k", [4, 8])
 def test_block_split(name, split_k):
     w = WORKLOADS[name]

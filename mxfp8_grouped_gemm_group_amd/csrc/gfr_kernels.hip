@@ -878,6 +878,15 @@ static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
               "cooperative ring fits the block's LDS");
 
 // One 32-bit element k (uniform, 0..3; larger values read element 3) of w.
+// Cache policy of the weight loads of a wave item whose weights no other
+// item reads (NT): non-temporal.  A probe streaming 1 GB as 32 experts x 8192
+// rows x 4 KB in 128-byte pieces of 64 rows (the [K,N] wave items' pattern)
+// read 6.3 TB/s with the default policy and 6.9-7.0 TB/s with nt; where
+// weights are shared through L2 (cooperative units, the row tiles of one
+// expert) the default policy is kept.
+constexpr int kNonTemporal = 2;
+constexpr int kStreamMinBytes = 256 << 10;   // an item's weight bytes for nt loads
+
 __device__ __forceinline__ uint32_t pick(const v4i &w, int k) {
     return static_cast<uint32_t>(k <= 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w);
 }
@@ -904,7 +913,7 @@ __device__ __forceinline__ int k_rotation(int e, int n, int win) {
 
 // split: the block's LDS ring when the item is one of a block-split wave
 // unit's four K ranges (split_epilogue), else null.
-template <int FMT, bool KN, bool COOP, int RF, int OP, bool WS = false>
+template <int FMT, bool KN, bool COOP, int RF, int OP, bool WS = false, bool NT = false>
 __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                             int ks0, int ks1, bool store_rows, char *ring, int w,
                             char *split = nullptr) {
@@ -1204,9 +1213,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             if (KN)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rb, dst, 16, vb[KN4 ? (u & 1) : SPLIT ? hf : 0], (ks * kStepK + 8 * u) * Nb,
-                    0, 0);
+                    0, NT ? kNonTemporal : 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[uu], k0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vb[uu], k0, 0, NT ? kNonTemporal : 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -2162,7 +2171,7 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
 // keep the memory system busy meanwhile.
 // ---------------------------------------------------------------------------
 // split: as for routed_item.
-template <int FMT, bool WS>
+template <int FMT, bool WS, bool NT = false>
 __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                                         int ks0, int ks1, bool store_rows, char *ring,
                                         char *split) {
@@ -2247,7 +2256,8 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
 #pragma unroll
         for (int u = 0; u < kWLd; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + u * 1024), 16,
-                                                     vw[u & 1], 8 * u * Kb + ks * kStepKNK, 0, 0);
+                                                     vw[u & 1], 8 * u * Kb + ks * kStepKNK, 0,
+                                                     NT ? kNonTemporal : 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto issue_regs = [&](int ks, int set) {
@@ -2377,7 +2387,7 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
 // half of step i's MFMAs.  Weight scales: the step's two [K/64, N, 2] rows
 // per column group (one line each); x1 scales: windows of four steps.
 // ---------------------------------------------------------------------------
-template <int FMT, bool WS>
+template <int FMT, bool WS, bool NT = false>
 __device__ __forceinline__ void kw_item(const FusedParams &p, int e, int m0, int mcount, int n0,
                                         int ks0, int ks1, bool store_rows, char *ring,
                                         char *split) {
@@ -2456,7 +2466,8 @@ __device__ __forceinline__ void kw_item(const FusedParams &p, int e, int m0, int
 #pragma unroll
         for (int u = 0; u < kWLd; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + u * 1024), 16, vw,
-                                                     (ks * kStepKNK + 8 * u) * N, 0, 0);
+                                                     (ks * kStepKNK + 8 * u) * N, 0,
+                                                     NT ? kNonTemporal : 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto issue_regs = [&](int ks, int set) {
@@ -2901,37 +2912,68 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             narrow(ks0, ks1);
             char *own = s_ring + w * kRingBytes;
             char *split = bsplit ? s_ring : nullptr;
+            // Non-temporal weight loads where no other item reads this K range
+            // of these weights (one row tile) and the range is long: on short
+            // ranges (80-192 KB per item: c1_fp4, c2_fp4) they ran 5-13 %
+            // slower, on long ones up to 9 % faster (c3, c3_fp4, g1_llada).
+            const bool stream =
+                e_cnt <= kTileM &&
+                (ks1 - ks0) * (kTB ? kCkWSlot : kSlotBytes) >= kStreamMinBytes;
             if constexpr (kTB) {
-                if (wsc_tb)
-                    cw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own,
-                                       split);
-                else
+                if (wsc_tb) {
+                    if (stream)
+                        cw_item<FMT, true, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
+                                                 store_rows, own, split);
+                    else
+                        cw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows,
+                                           own, split);
+                } else if (stream) {
+                    cw_item<FMT, false, true>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows,
+                                              own, split);
+                } else {
                     cw_item<FMT, false>(p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own,
                                         split);
+                }
             } else {
                 if constexpr (kKW) {
                     if (kw_on) {
                         int k0w = static_cast<int>(static_cast<int>(k_steps_w) * s / S);
                         int k1w = static_cast<int>(static_cast<int>(k_steps_w) * (s + 1) / S);
                         narrow(k0w, k1w);
-                        if (wsc_tb)
-                            kw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, k0w, k1w, store_rows,
-                                               own, split);
-                        else
+                        if (wsc_tb) {
+                            if (stream)
+                                kw_item<FMT, true, true>(p, e, m0, mcount, nt * kOutN, k0w, k1w,
+                                                         store_rows, own, split);
+                            else
+                                kw_item<FMT, true>(p, e, m0, mcount, nt * kOutN, k0w, k1w,
+                                                   store_rows, own, split);
+                        } else if (stream) {
+                            kw_item<FMT, false, true>(p, e, m0, mcount, nt * kOutN, k0w, k1w,
+                                                      store_rows, own, split);
+                        } else {
                             kw_item<FMT, false>(p, e, m0, mcount, nt * kOutN, k0w, k1w,
                                                 store_rows, own, split);
+                        }
                         continue;
                     }
                 }
                 if constexpr (kWS) {
                     if (ws_ok) {
-                        routed_item<FMT, !TRANS, false, 1, OP, true>(
-                            p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own, w);
+                        if (stream)
+                            routed_item<FMT, !TRANS, false, 1, OP, true, true>(
+                                p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own, w);
+                        else
+                            routed_item<FMT, !TRANS, false, 1, OP, true>(
+                                p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own, w);
                         continue;
                     }
                 }
-                routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0, ks1,
-                                                       store_rows, own, w, split);
+                if (stream)
+                    routed_item<FMT, !TRANS, false, 1, OP, false, true>(
+                        p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, own, w, split);
+                else
+                    routed_item<FMT, !TRANS, false, 1, OP>(p, e, m0, mcount, nt * kOutN, ks0,
+                                                           ks1, store_rows, own, w, split);
             }
         }
     }

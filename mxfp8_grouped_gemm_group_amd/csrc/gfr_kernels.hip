@@ -879,11 +879,12 @@ static_assert(kCoopStagesKN * kSlotBytes <= kWavesPerBlock * kRingBytes &&
 
 // One 32-bit element k (uniform, 0..3; larger values read element 3) of w.
 // Cache policy of the weight loads of a wave item whose weights no other
-// item reads (NT): non-temporal.  A probe streaming 1 GB as 32 experts x 8192
-// rows x 4 KB in 128-byte pieces of 64 rows (the [K,N] wave items' pattern)
-// read 6.3 TB/s with the default policy and 6.9-7.0 TB/s with nt; where
-// weights are shared through L2 (cooperative units, the row tiles of one
-// expert) the default policy is kept.
+// item reads (NT): non-temporal, as the page's kernel marks each expert's
+// weight tile non-cacheable to spare L2 (§5.3).  A probe streaming 1 GB as 32
+// experts x 8192 rows x 4 KB in 128-byte pieces of 64 rows (the [K,N] wave
+// items' pattern) read 6.3 TB/s with the default policy and 6.9-7.0 TB/s
+// with nt; where weights are shared through L2 (cooperative units, the row
+// tiles of one expert) the default policy is kept.
 constexpr int kNonTemporal = 2;
 constexpr int kStreamMinBytes = 256 << 10;   // an item's weight bytes for nt loads
 

@@ -142,32 +142,6 @@ struct SatAddU32 {
     }
 };
 
-// Exclusive block-wide prefix sum: a shuffle scan within each wave, then the
-// wave totals through LDS (two barriers in all).
-template <class T>
-__device__ T block_exclusive_scan(T v, T *s_scan, T &total) {
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWaveSize - 1), wv = tid / kWaveSize;
-    T x = v;
-#pragma unroll
-    for (int off = 1; off < kWaveSize; off <<= 1) {
-        const T y = __shfl_up(x, off, kWaveSize);
-        if (lane >= off) x += y;
-    }
-    if (lane == kWaveSize - 1) s_scan[wv] = x;
-    __syncthreads();
-    T before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < kWavesPerBlock; ++i) {
-        const T t = s_scan[i];
-        before += i < wv ? t : T(0);
-        all += t;
-    }
-    total = all;
-    __syncthreads();   // s_scan may be reused after return
-    return before + x - v;
-}
-
 // ---------------------------------------------------------------------------
 // Work list (group_list -> expert ranges -> item prefix), built in LDS by
 // every workgroup.  group_list formats per the page's §4.3: type 0 = prefix
@@ -3014,25 +2988,36 @@ __global__ void det_count_kernel(FusedParams p, int *counts) {
     }
 }
 
+// One workgroup: the counts (at most M < 2^31 in all) in chunks of four per
+// thread, each chunk a 32-bit DPP block scan plus the carry of the chunks
+// before it.
 __global__ void det_scan_kernel(FusedParams p, const int *counts, int *offsets, int *cursor) {
-    __shared__ int64_t s_scan[kBlockThreads];
-    __shared__ int64_t s_carry;
-    if (threadIdx.x == 0) s_carry = 0;
-    __syncthreads();
-    for (int base = 0; base < p.batch; base += kBlockThreads) {
-        const int b = base + threadIdx.x;
-        const int64_t v = b < p.batch ? counts[b] : 0;
-        int64_t tot = 0;
-        const int64_t ex = block_exclusive_scan<int64_t>(v, s_scan, tot);
-        if (b < p.batch) {
-            offsets[b] = static_cast<int>(s_carry + ex);
-            cursor[b] = static_cast<int>(s_carry + ex);
+    __shared__ uint32_t s_scan[4];
+    constexpr int kPer = 4;                       // counts per thread and chunk
+    constexpr int kChunk = kBlockThreads * kPer;
+    uint32_t carry = 0;
+    for (int base = 0; base < p.batch; base += kChunk) {
+        const int b0 = base + threadIdx.x * kPer;
+        uint32_t c[kPer], sum = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            c[i] = b0 + i < p.batch ? static_cast<uint32_t>(counts[b0 + i]) : 0u;
+            sum += c[i];
         }
-        __syncthreads();
-        if (threadIdx.x == 0) s_carry += tot;
-        __syncthreads();
+        uint32_t v[1] = {sum}, tot[1];
+        block_scan_u32<1>(v, tot, s_scan, AddU32{});   // ends synchronised
+        uint32_t run = carry + v[0];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (b0 + i < p.batch) {
+                offsets[b0 + i] = static_cast<int>(run);
+                cursor[b0 + i] = static_cast<int>(run);
+            }
+            run += c[i];
+        }
+        carry += tot[0];
     }
-    if (threadIdx.x == 0) offsets[p.batch] = static_cast<int>(s_carry);
+    if (threadIdx.x == 0) offsets[p.batch] = static_cast<int>(carry);
 }
 
 __global__ void det_fill_kernel(FusedParams p, int *cursor, int *tokens) {

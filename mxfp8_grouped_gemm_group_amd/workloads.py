@@ -239,6 +239,8 @@ C5_PE = _reg(replace(C5, name="c5_pe", scale_per_expert=True, seed=1035))
 SMALL_T_FP4 = _reg(replace(SMALL_T, name="small_t_fp4", fp8="e2m1", K=768, seed=1041))
 SMALL_BIG_T_FP4 = _reg(replace(SMALL_BIG_T, name="small_big_t_fp4", fp8="e2m1", K=768,
                                seed=1042))
+SMALL_T_FP4_K512 = _reg(replace(SMALL_T, name="small_t_fp4_k512", fp8="e2m1", K=512,
+                                seed=1059))
 SMALL_T_FP4_K1280 = _reg(replace(SMALL_T, name="small_t_fp4_k1280", fp8="e2m1", K=1280,
                                  seed=1051))
 # ... K = 256 (one 256-K step per row: per-step scale loads) in cooperative
@@ -281,7 +283,8 @@ W4A8_P3 = _reg(Workload("w4a8_p3", batch=512, topk=8, M=4096, K=2048, N=7168, E=
 for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SMALL_HUGE_N,
               SMALL_COOP_T_K128, SMALL_SPLIT_N, SMALL_SPLIT_T, SMALL_TAIL_N, SMALL_TAIL_T,
               SMALL_HUGE_T, SMALL_MANY_N, SMALL_MANY_T, SMALL_T_K768,
-              SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_N_PE,
+              SMALL_BIG_T_K768, SMALL_T_K512, SMALL_T_K384, SMALL_T_FP4_K1280, SMALL_T_FP4_K512,
+              SMALL_N_PE,
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, SMALL_BIG_T_FP4_K256,
               SMALL_SPLIT_T_FP4, SMALL_TAIL_T_FP4, SMALL_MANY_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_SPLIT_N_FP4,

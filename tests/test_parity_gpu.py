@@ -136,7 +136,8 @@ def slack_for(inp, rows=None):
                                   "small_split_t_fp4", "small_split_t_fp4_exact",
                                   "small_tail_t_fp4", "small_tail_t_fp4_exact",
                                   "small_many_t_fp4", "small_many_t_fp4_exact",
-                                  "small_split_n_fp4", "small_split_n_fp4_exact"])
+                                  "small_split_n_fp4", "small_split_n_fp4_exact",
+                                  "small_t_fp4_k512", "small_t_fp4_k512_exact"])
 @pytest.mark.parametrize("split_k", [0, 1, 3])
 def test_small_full(name, split_k):
     w = WORKLOADS[name]

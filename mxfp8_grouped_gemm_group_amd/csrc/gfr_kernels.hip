@@ -546,13 +546,13 @@ constexpr int kBLoadsPerStep = kSlotBytes / (kWaveSize * 16);   // 8 x 1 KB
 // Scales are loaded as the aligned dword that holds them and the byte is
 // selected when the step is consumed: a byte load would be zero-extended where
 // the compiler chooses, which can force an early wait on the load.
-template <int AL, int RF, int SB, int SW>
+template <int AL, int RF, int SB>
 struct StepRegs {
     v4i a[RF][AL];       // x1 row bytes of fragment f: FP8 [K,N] bytes [16g, +16),
                          // [32 + 16g, +16) of the step's 64; [N,K] bytes 32q + 16g
                          // of the step's 128; FP4 [K,N] bytes [16g, +16) of 32
-    uint32_t sa[RF][SW]; // x1 scale bytes of the step
-    uint32_t sb[SB][SW]; // weight scale bytes of column group j
+    uint32_t sa[RF][1];  // x1 scale bytes of the step
+    uint32_t sb[SB][1];  // weight scale bytes of column group j
 };
 
 // Destination row and weight of the tile's 32 (or 64) rows, loaded when the
@@ -894,14 +894,16 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                             char *split = nullptr) {
     static_assert(RF == 1 || (COOP && RF == 2), "two row fragments only in cooperative units");
     // FP4 E2M1 (MFMA format 4): elements packed two per byte along the
-    // contiguous axis (x1 and [N, K] weights along K, [K, N] weights along N).
-    // An FP4 MFMA operand is 16 bytes per lane: lane (c, g) holds K
-    // [32g, 32g + 32) of its row / column, nibble i = K 32g + i (low nibble
-    // first) -- measured with one-hot operands against an FP8 operand of known
-    // layout.  FP4 [K, N] steps are 64 K x 256 columns (the slot keeps 64 rows
-    // of 128 bytes), eight MFMAs per step.
+    // contiguous axis (x1 along K, [K, N] weights along N).  An FP4 MFMA
+    // operand is 16 bytes per lane: lane (c, g) holds K [32g, 32g + 32) of
+    // its row / column, nibble i = K 32g + i (low nibble first) -- measured
+    // with one-hot operands against an FP8 operand of known layout.  FP4
+    // [K, N] steps are 64 K x 256 columns (the slot keeps 64 rows of 128
+    // bytes), eight MFMAs per step.  (MXFP4 [N, K] items are ck_unit's and
+    // cw_item's.)
     constexpr bool FP4 = FMT == 4;
     constexpr bool KN4 = FP4 && KN;
+    static_assert(!FP4 || KN, "MXFP4 here only with [K, N] weights");
     // FMT 8, the W4A8 variant: INT8 x1 and signed INT4 [K, N] weights packed
     // two per byte along N.  Its slot is FP8's (64 K rows of 128 bytes, here
     // 256 columns) and its operands come out of LDS the same way, as
@@ -1105,10 +1107,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // [N,K] weight column moves the same 128 bytes)
     constexpr int kStepA = KN ? (FP4 ? kStepK / 2 : kStepK) : kStepKNK;
     constexpr int kAL = KN ? (FP4 ? 1 : 2) : 4;      // x1 loads per step
-    // WS ([N, K], 4-slot ring; K >= 512 for FP8, >= 1024 for FP4): the x1
-    // and weight scales are loaded once per window of four steps, 16 bytes
-    // per x1 row and per weight column (FP8: the four steps' dwords; FP4: two
-    // loads, the four steps' qwords) instead of a gather per step: each load
+    // WS ([N, K], 4-slot ring; K >= 512): the x1 and weight scales are loaded
+    // once per window of four steps, 16 bytes per x1 row and per weight
+    // column (the four steps' dwords) instead of a gather per step: each load
     // instruction touches 32 rows, so this is 4x fewer scattered cache-line
     // accesses.  The window load goes first in the load
     // group of the window's first step (item-relative steps 4m, a multiple of
@@ -1124,25 +1125,23 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     static_assert(!WS || (!I8 && D == 4 && (!KN || (!FP4 && OP == 0 && COOP && RF == 2))),
                   "windowed scales: 4 slots; [K,N] only FP8 two-fragment cooperative units");
     constexpr bool kWSKN = WS && KN;
-    constexpr int kWL = FP4 ? 2 : 1;                 // 16-byte loads per row per window
     constexpr int kSA = I8 || WS ? 0 : 1;            // x1-scale loads per step and fragment
     constexpr int kSB = I8 || (WS && !KN) ? 0 : KN4 ? 8 : KN ? 4 : 2;   // weight-scale loads per step
-    constexpr int kXW = kWSKN ? RF : WS ? kWL * (RF + 2) : 0;   // loads per window
-    constexpr int kSW = FP4 && !KN ? 2 : 1;          // dwords per scale load
-    // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4 (FP8) or 8 (FP4)
-    constexpr int kBlk = KN ? 2 : (FP4 ? 8 : 4);
-    StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> regs[D];
+    constexpr int kXW = kWSKN ? RF : WS ? RF + 2 : 0;   // loads per window
+    // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4
+    constexpr int kBlk = KN ? 2 : 4;
+    StepRegs<kAL, RF, (kSB > 0 ? kSB : 1)> regs[D];
 
     // hf: SPLIT's tile of virtual step vs (0 gate, 1 up) = vs & 1, passed as
     // the unrolled ring index's parity so that it is a compile-time constant
     // (ks0 * 2 and D are even; for the clamped re-reads past the last step it
     // may differ, and those are never consumed)
     // WS: scale windows, [0] current, [1] next ([K,N]: x1 scales only, 8 bytes)
-    v4i wsa[2][kWSKN ? 1 : RF][kWL], wsb[2][2][kWL];
+    v4i wsa[2][kWSKN ? 1 : RF], wsb[2][2];
     v2i wsk[2][kWSKN ? RF : 1];
     int wdl[2] = {0, 0};   // WS: step shift of a window moved back from the row end
     // steps of a whole row; each takes kBlk scale bytes of it
-    const int k_row = K / (KN ? kStepK : FP4 ? 2 * kStepKNK : kStepKNK);
+    const int k_row = K / (KN ? kStepK : kStepKNK);
     auto wload = [&](int vs, int set) {   // the window starting at step vs
         const int start = vs < k_row - 4 ? vs : k_row - 4;
         wdl[set] = vs - start;
@@ -1155,23 +1154,11 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             return;
         }
 #pragma unroll
-        for (int q = 0; q < kWL; ++q) {
+        for (int f = 0; f < RF; ++f)
+            wsa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + kBlk * start, 0, 0);
 #pragma unroll
-            for (int f = 0; f < RF; ++f)
-                wsa[set][f][q] =
-                    __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + kBlk * start + 16 * q, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                wsb[set][j][q] =
-                    __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + kBlk * start + 16 * q, 0, 0);
-        }
-    };
-    // dword k (uniform) of a window: FP8 one per step, FP4 two per step
-    auto wpick = [&](const v4i (&w)[kWL], int k) {
-        if constexpr (kWL == 2)
-            return k < 4 ? pick(w[0], k) : pick(w[1], k - 4);
-        else
-            return pick(w[0], k);
+        for (int j = 0; j < 2; ++j)
+            wsb[set][j] = __builtin_amdgcn_raw_buffer_load_b128(rsb, vsb[j] + kBlk * start, 0, 0);
     };
 
     // The weight-tile loads of a step (into LDS slot `slot`).
@@ -1203,7 +1190,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         if constexpr (WS) {
             if (wstart) wload(vs, 1);
         }
-        StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
+        StepRegs<kAL, RF, (kSB > 0 ? kSB : 1)> &r = regs[slot];
         if constexpr (kXL) {
             static_assert(!kXL || RF * kAL == kXLoads, "as many x1 loads per step as in registers");
 #pragma unroll
@@ -1221,27 +1208,13 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // x1 scale bytes of the step: [K,N] (2 ks + g) & 3 of the dword at
         // (2 ks) & ~3; [N,K] the step's kBlk bytes at kBlk ks
 #pragma unroll
-        for (int f = 0; f < RF * kSA; ++f) {
-            if constexpr (kSW == 2) {
-                const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[f], kBlk * ks, 0);
-                r.sa[f][0] = v.x;
-                r.sa[f][1] = v.y;
-            } else {
-                r.sa[f][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f],
-                                                                  KN ? (2 * ks) & ~3 : kBlk * ks, 0);
-            }
-        }
+        for (int f = 0; f < RF * kSA; ++f)
+            r.sa[f][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa[f],
+                                                              KN ? (2 * ks) & ~3 : kBlk * ks, 0);
 #pragma unroll
-        for (int j = 0; j < kSB; ++j) {
-            if constexpr (kSW == 2) {
-                const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb[j], kBlk * ks, 0);
-                r.sb[j][0] = v.x;
-                r.sb[j][1] = v.y;
-            } else {
-                r.sb[j][0] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rsb, SPLIT ? vsb[4 * hf + j] : vsb[j], KN ? ks * 2 * N : kBlk * ks, 0);
-            }
-        }
+        for (int j = 0; j < kSB; ++j)
+            r.sb[j][0] = __builtin_amdgcn_raw_buffer_load_b32(
+                rsb, SPLIT ? vsb[4 * hf + j] : vsb[j], KN ? ks * 2 * N : kBlk * ks, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -1287,7 +1260,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     auto mma = [&](int slot, const BTile &b, const v4i (&ax)[4], bool live, int vs, int hf,
                    int wpos) {
         const int ks = SPLIT ? vs >> 1 : vs;
-        StepRegs<kAL, RF, (kSB > 0 ? kSB : 1), kSW> &r = regs[slot];
+        StepRegs<kAL, RF, (kSB > 0 ? kSB : 1)> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
         // multiply a zero operand
 #pragma unroll
@@ -1349,42 +1322,14 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                         acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
                     }
                 }
-            } else if constexpr (FP4) {
-                uint32_t sa2[2] = {r.sa[f][0], r.sa[f][1]};
-                uint32_t sb2[2][2] = {{r.sb[0][0], r.sb[0][1]}, {r.sb[1][0], r.sb[1][1]}};
-                if constexpr (WS) {
-                    const int k = 2 * (wpos + wdl[0]);   // the step's qword in the window
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        sa2[h] = wpick(wsa[0][f], k + h);
-                        sb2[0][h] = wpick(wsb[0][0], k + h);
-                        sb2[1][h] = wpick(wsb[0][1], k + h);
-                    }
-                }
-                // four 64-K sub-steps s, two 32-column groups j; operand =
-                // 16 bytes (chunk 2s + g of the lane's row / column); scale of
-                // 32-block 8 ks + 2 s + g = byte 2 s + g of the step's 8; odd
-                // sub-steps accumulate into acc[f][2 + j] (fewer back-to-back
-                // dependent MFMAs), summed before the epilogue
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const v4i z = {0, 0, 0, 0};
-                    const v8i a = on ? cat(r.a[f][s4], z) : v8i{};
-                    const int shf = 8 * (2 * (s4 & 1) + g);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[f][j + 2 * (s4 & 1)] =
-                            mfma<FMT, 0>(a, cat(b[2 * s4 + j], z), acc[f][j + 2 * (s4 & 1)],
-                                         sa2[s4 >> 1] >> shf, sb2[j][s4 >> 1] >> shf);
-                }
             } else {
                 // two 64-K halves s, two 32-column groups j; the scale of
                 // 32-block 4 ks + 2 s + g is byte 2 s + g of each scale dword
                 uint32_t sa = r.sa[f][0], sb[2] = {r.sb[0][0], r.sb[1][0]};
                 if constexpr (WS) {
-                    sa = wpick(wsa[0][f], wpos + wdl[0]);
-                    sb[0] = wpick(wsb[0][0], wpos + wdl[0]);
-                    sb[1] = wpick(wsb[0][1], wpos + wdl[0]);
+                    sa = pick(wsa[0][f], wpos + wdl[0]);
+                    sb[0] = pick(wsb[0][0], wpos + wdl[0]);
+                    sb[1] = pick(wsb[0][1], wpos + wdl[0]);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
@@ -1478,12 +1423,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                         for (int f = 0; f < RF; ++f) wsk[0][f] = wsk[1][f];
                     } else {
 #pragma unroll
-                        for (int q = 0; q < kWL; ++q) {
-#pragma unroll
-                            for (int f = 0; f < RF; ++f) wsa[0][f][q] = wsa[1][f][q];
-                            wsb[0][0][q] = wsb[1][0][q];
-                            wsb[0][1][q] = wsb[1][1][q];
-                        }
+                        for (int f = 0; f < RF; ++f) wsa[0][f] = wsa[1][f];
+                        wsb[0][0] = wsb[1][0];
+                        wsb[0][1] = wsb[1][1];
                     }
                     wdl[0] = wdl[1];
                 }
@@ -1493,13 +1435,6 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     }
     // Drain the trailing re-reads before the ring is reused.
     wait_vmcnt<0>();
-    if constexpr (FP4 && !KN) {
-#pragma unroll
-        for (int f = 0; f < RF; ++f) {
-            acc[f][0] += acc[f][2];
-            acc[f][1] += acc[f][3];
-        }
-    }
     if constexpr (OP == 1)
         epilogue_swiglu<SPLIT ? 8 : 2, RF, NA>(p, acc, m0, mcount, n0);
     else if constexpr (I8)
@@ -2611,10 +2546,10 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         *p.det_total = wl.routed_tokens;
 
     const bool store_rows = OP == 0 && p.wbuf != nullptr;
-    // [N, K]: windowed scale loads in the 4-slot-ring items (a window is four
-    // steps of a row's scale bytes: K >= 512 for FP8, >= 1024 for FP4)
+    // [N, K]: windowed scale loads in the 4-slot-ring items (the upstream
+    // step's; a window is four 128-K steps of a row's scale bytes: K >= 512)
     constexpr bool kWS = TRANS && FMT != 8;
-    const bool ws_ok = kWS && p.K >= 4 * (FMT == 4 ? 2 * kStepKNK : kStepKNK);
+    const bool ws_ok = kWS && p.K >= 4 * kStepKNK;
     // [K, N] FP8 finalize: windowed x1 scales in the two-fragment cooperative
     // units (their x1 bytes come through LDS, which leaves the registers)
     constexpr bool kWSC = kWS || (!TRANS && (FMT == 0 || FMT == 1) && OP == 0);

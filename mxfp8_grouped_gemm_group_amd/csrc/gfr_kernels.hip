@@ -2614,6 +2614,17 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         (blocks % 8 == 0) ? static_cast<int>(blockIdx.x % 8) * (blocks / 8) + blockIdx.x / 8
                           : blockIdx.x;
     const int waves = static_cast<int>(blocks) * kWavesPerBlock;
+    // One-fragment cooperative units (no snake deal) take ranks in chunks of
+    // 16 per XCD: ranks 16c .. 16c + 15 are blocks of XCD c mod 8.  Sixteen
+    // consecutive units (the row groups of a band over four column tiles)
+    // still share one XCD's L2, and when there are more units than blocks
+    // the blocks that also take a wave unit spread over the XCDs instead of
+    // filling the first ones (g1_llada 146 -> 134 µs, c4_fp4 -1 %).
+    const int coop_rank =
+        (blocks % 128 == 0)
+            ? ((static_cast<int>(blockIdx.x / 8) / 16) * 8 + static_cast<int>(blockIdx.x % 8)) * 16 +
+                  static_cast<int>(blockIdx.x / 8) % 16
+            : xcd_block;
 
     // The deal.  With two-fragment cooperative units present, units g = 0,
     // 1, ... (the cooperative units in the order of the work list, experts
@@ -2624,9 +2635,9 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // rows: c4 523 -> 501 µs, c5 2355 -> 2278).  Ranks are XCD-grouped
     // (consecutive ranks on one XCD, so consecutive cooperative units share
     // an L2).  Otherwise (one-fragment cooperative units, where the snake
-    // measured slower, or none) the cooperative units go round-robin over the
-    // XCD-grouped ranks and the wave units round-robin in plain block order
-    // (measured fastest for pure streaming).
+    // measured slower, or none) the cooperative units go round-robin over
+    // ranks in XCD chunks of 16 (coop_rank) and the wave units round-robin in
+    // plain block order (measured fastest for pure streaming).
     // A block alternates between its cooperative and its wave units (even
     // blocks start with a cooperative unit, odd ones with a wave unit):
     // cooperative units hardly use HBM (their weights are shared through L2)
@@ -2687,10 +2698,10 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         n_wave = rounds_below(seq_pos) - n_coop;
     } else {
         const int wave_pos = coop_units == 0 ? seq_pos : units - coop_units;
-        n_coop = coop_units > xcd_block ? (coop_units - xcd_block + blocks - 1) / blocks : 0;
+        n_coop = coop_units > coop_rank ? (coop_units - coop_rank + blocks - 1) / blocks : 0;
         n_wave = wave_pos > blockIdx.x ? (wave_pos - blockIdx.x + blocks - 1) / blocks : 0;
     }
-    auto coop_pos = [&](int i) { return snake ? g_of(i) : xcd_block + i * blocks; };
+    auto coop_pos = [&](int i) { return snake ? g_of(i) : coop_rank + i * blocks; };
     auto wave_pos_of = [&](int j) {
         return snake ? g_of(n_coop + j) : coop_units + blockIdx.x + j * blocks;
     };

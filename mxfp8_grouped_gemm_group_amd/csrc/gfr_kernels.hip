@@ -866,6 +866,12 @@ __device__ __forceinline__ uint32_t pick(const v4i &w, int k) {
     return static_cast<uint32_t>(k <= 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w);
 }
 
+// a compile-time int passed to generic lambdas
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 // Rotation of an [N, K] wave item's K order.  A step reads the same 128-byte
 // piece of 128 weight rows (columns); where a row is 4 KB long (MXFP4 K 8192)
 // every item in flight then hits the same in-row offset, the rows of
@@ -1492,9 +1498,10 @@ __device__ __forceinline__ void lds_issue_w8(uint32_t wa0, uint32_t wa1, v4i (&t
         : "memory");
 }
 
-template <int RF>
+template <int RF, int NT>
 __device__ __forceinline__ void lds_issue_ck(uint32_t wa0, uint32_t wa1, uint32_t xa0,
-                                             uint32_t xa1, v4i (&t)[8 + 2 * RF]) {
+                                             uint32_t xa1, v4i (&t)[NT]) {
+    static_assert(NT >= 8 + 2 * RF, "operand buffer holds the reads");
     lds_issue_w8(wa0, wa1, t);
     if constexpr (RF == 2)
         asm volatile(
@@ -1677,11 +1684,16 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
         __builtin_amdgcn_sched_barrier(0);
     };
     // operands of half s of the step in weight stage ws / x1 stage xs
-    auto read_half = [&](int ws, int xs, int s2, v4i (&t)[kNH]) {
-        const uint32_t wbase = lds_addr(wring + ws * kCkWSlot);
-        const uint32_t xbase = lds_addr(xring + xs * kXStage);
-        lds_issue_ck<RF>(wbase + o[2 * s2], wbase + o[2 * s2 + 1], xbase + o[2 * s2],
-                         xbase + o[2 * s2 + 1], t);
+    // LF: fragments of this wave with live rows (a constant of the loop
+    // instance); the others' reads and MFMAs are skipped
+    auto read_half = [&](int ws, int xs, int s2, v4i (&t)[kNH], auto lf_c) {
+        constexpr int LF = decltype(lf_c)::value;
+        if constexpr (LF > 0) {
+            const uint32_t wbase = lds_addr(wring + ws * kCkWSlot);
+            const uint32_t xbase = lds_addr(xring + xs * kXStage);
+            lds_issue_ck<LF>(wbase + o[2 * s2], wbase + o[2 * s2 + 1], xbase + o[2 * s2],
+                             xbase + o[2 * s2 + 1], t);
+        }
     };
     v4i hb[2][kNH];   // [0]: half 0 of a step, [1]: half 1
     // (x1 rows past the expert's last token are zero in LDS: the DMA reads
@@ -1692,7 +1704,8 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     // holding 16 bytes = K [64h + 32g, +32) of it (the chunk the FP8 read
     // gives as its 2h-th); the scale of 32-block 4 s + 2 h + g is byte 2 h + g
     // of the step's dword s.
-    auto mma_half = [&](const v4i (&t)[kNH], int s2, int set, int wpos) {
+    auto mma_half = [&](const v4i (&t)[kNH], int s2, int set, int wpos, auto lf_c) {
+        constexpr int LF = decltype(lf_c)::value;
         const int sw = kScW * (wpos + wdl[0]) + (FP4 ? s2 : 0);   // window dword
         uint32_t sa[RF], sb[4];
 #pragma unroll
@@ -1711,7 +1724,7 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
             for (int h = 0; h < 2; ++h) {
                 const int shf = 8 * (2 * h + g);
 #pragma unroll
-                for (int f = 0; f < RF; ++f) {
+                for (int f = 0; f < LF; ++f) {
                     const v8i a = cat(t[8 + 2 * f + h], z);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
@@ -1722,7 +1735,7 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
         } else {
             const int shf = 8 * (2 * s2 + g);
 #pragma unroll
-            for (int f = 0; f < RF; ++f) {
+            for (int f = 0; f < LF; ++f) {
                 const v8i a = cat(t[8 + 2 * f], t[8 + 2 * f + 1]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -1756,56 +1769,67 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
     static_assert(kWLd + 2 * kXLd < 64 && kWLd + kXLd + RF + 4 < 64, "vmcnt range");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_half(0, 0, 0, hb[0]);
-    lds_wait_all(hb[0]);
-    // Iteration i (half 0 of step i already in hb[0]; xs = x1 stage of step i):
-    //   read half 1; half 0's MFMAs; wait for the reads;
-    //   wait for step i + 1 (WS: everything but the x1 of step i + 2) and
-    //   barrier: every wave's share of step i + 1 is in and every wave has
-    //   read all of step i; read half 0 of step i + 1; refill: weights of step
-    //   i + 2 into step i's weight stage (WS: with the next window when step
-    //   i + 2 starts one), x1 of step i + DX into step i's x1 stage; half 1's
-    //   MFMAs; per-step scales of step i + 2 into the set just consumed; wait
-    //   for the reads.
-    int xs = 0;
-    for (int i0 = 0; i0 < n_steps; i0 += DW) {
+    // A wave without live rows in a fragment still moves its share of every
+    // step (the loads, waits and barriers are the block's) but reads and
+    // multiplies only its live fragments.
+    auto main_loop = [&](auto lf_c) {
+        read_half(0, 0, 0, hb[0], lf_c);
+        lds_wait_all(hb[0]);
+        // Iteration i (half 0 of step i already in hb[0]; xs = x1 stage of step i):
+        //   read half 1; half 0's MFMAs; wait for the reads;
+        //   wait for step i + 1 (WS: everything but the x1 of step i + 2) and
+        //   barrier: every wave's share of step i + 1 is in and every wave has
+        //   read all of step i; read half 0 of step i + 1; refill: weights of step
+        //   i + 2 into step i's weight stage (WS: with the next window when step
+        //   i + 2 starts one), x1 of step i + DX into step i's x1 stage; half 1's
+        //   MFMAs; per-step scales of step i + 2 into the set just consumed; wait
+        //   for the reads.
+        int xs = 0;
+        for (int i0 = 0; i0 < n_steps; i0 += DW) {
 #pragma unroll
-        for (int d = 0; d < DW; ++d) {
-            const int i = i0 + d;
-            const bool live = i < n_steps;
-            const int xn = xs + 1 == DX ? 0 : xs + 1;   // x1 stage of step i + 1
-            read_half(d, xs, 1, hb[1]);
-            if (live) mma_half(hb[0], 0, d, i & (kWin - 1));   // padding steps past the range: none
-            lds_wait_all(hb[1]);
-            if constexpr (WS)
-                wait_vmcnt<kXLd>();
-            else
-                wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            read_half((d + 1) % DW, xn, 0, hb[0]);
-            if constexpr (WS) {
-                if (((i + 2) & (kWin - 1)) == 0) wload(step_of(i + 2), 1);
-            }
-            issue_w(step_of(i + 2), d);
-            issue_x(step_of(i + DX), xs);
-            if (live) mma_half(hb[1], 1, d, i & (kWin - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (!WS) issue_scales(step_of(i + 2), d);
-            lds_wait_all(hb[0]);
-            if constexpr (WS) {
-                if ((i & (kWin - 1)) == kWin - 1) {   // the next window becomes current
-#pragma unroll
-                    for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) wb[0][j] = wb[1][j];
-                    wdl[0] = wdl[1];
+            for (int d = 0; d < DW; ++d) {
+                const int i = i0 + d;
+                const bool live = i < n_steps;
+                const int xn = xs + 1 == DX ? 0 : xs + 1;   // x1 stage of step i + 1
+                read_half(d, xs, 1, hb[1], lf_c);
+                if (live) mma_half(hb[0], 0, d, i & (kWin - 1), lf_c);   // padding steps: none
+                lds_wait_all(hb[1]);
+                if constexpr (WS)
+                    wait_vmcnt<kXLd>();
+                else
+                    wait_vmcnt<0>();
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                read_half((d + 1) % DW, xn, 0, hb[0], lf_c);
+                if constexpr (WS) {
+                    if (((i + 2) & (kWin - 1)) == 0) wload(step_of(i + 2), 1);
                 }
+                issue_w(step_of(i + 2), d);
+                issue_x(step_of(i + DX), xs);
+                if (live) mma_half(hb[1], 1, d, i & (kWin - 1), lf_c);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!WS) issue_scales(step_of(i + 2), d);
+                lds_wait_all(hb[0]);
+                if constexpr (WS) {
+                    if ((i & (kWin - 1)) == kWin - 1) {   // the next window becomes current
+#pragma unroll
+                        for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) wb[0][j] = wb[1][j];
+                        wdl[0] = wdl[1];
+                    }
+                }
+                xs = xn;
+                __builtin_amdgcn_sched_barrier(0);
             }
-            xs = xn;
-            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    if (mcount > (RF - 1) * kTileM)
+        main_loop(IntC<RF>{});
+    else if (RF == 2 && mcount > 0)
+        main_loop(IntC<1>{});
+    else
+        main_loop(IntC<0>{});
     wait_vmcnt<0>();   // the trailing re-reads, before the stages are reused
     epilogue<4, RF, 4>(p, acc, m0, n0, store_rows, rinfo);
 }
@@ -1951,7 +1975,11 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
         v8i b[4];
         v8i a[RF];
     };
-    auto read_half = [&](int ws, int xs, int s2, Half &t) {
+    // LF: fragments of this wave with live rows (a constant of the loop
+    // instance); the others' reads and MFMAs are skipped
+    auto read_half = [&](int ws, int xs, int s2, Half &t, auto lf_c) {
+        constexpr int LF = decltype(lf_c)::value;
+        if constexpr (LF == 0) return;
         char *wb = wring + ws * kCkWSlot + s2 * (kStepK * kTileN);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1964,7 +1992,7 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
         }
         char *xb = xring + xs * kXStage;
 #pragma unroll
-        for (int f = 0; f < RF; ++f) {
+        for (int f = 0; f < LF; ++f) {
             const v4i lo = *reinterpret_cast<const __attribute__((address_space(3))) v4i *>(
                 (lds_void_t *)(xb + f * 4096 + o[2 * s2]));
             const v4i hi = *reinterpret_cast<const __attribute__((address_space(3))) v4i *>(
@@ -1973,10 +2001,11 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
         }
     };
     Half hb[2];   // [0]: half 0 of a step, [1]: half 1
-    auto mma_half = [&](const Half &t, int s2, int set, int wpos) {
+    auto mma_half = [&](const Half &t, int s2, int set, int wpos, auto lf_c) {
+        constexpr int LF = decltype(lf_c)::value;
         const int shf = 8 * (2 * s2 + g);
 #pragma unroll
-        for (int f = 0; f < RF; ++f) {
+        for (int f = 0; f < LF; ++f) {
             uint32_t sa = 0;
             if constexpr (WS)
                 sa = pick(wa[0][f], wpos + wdl[0]);
@@ -2018,51 +2047,62 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
     __builtin_amdgcn_s_barrier();
     lds_reads_done();
     __builtin_amdgcn_sched_barrier(0);
-    read_half(0, 0, 0, hb[0]);
     // Iteration i (ck_unit's order): read half 1; half 0's MFMAs; wait for
     // step i + 1 and barrier; read half 0 of step i + 1; refill: weights of
     // step i + 2 into step i's weight stage (WS: with the next window when
     // step i + 2 starts one), x1 of step i + DX into step i's x1 stage; half
     // 1's MFMAs; step i + 2's scales into the register set just consumed.
-    int xs = 0;
-    for (int i0 = 0; i0 < n_steps; i0 += DW) {
+    // A wave without live rows in a fragment still moves its share of every
+    // step (the loads, waits and barriers are the block's) but reads and
+    // multiplies only its live fragments.
+    auto main_loop = [&](auto lf_c) {
+        read_half(0, 0, 0, hb[0], lf_c);
+        int xs = 0;
+        for (int i0 = 0; i0 < n_steps; i0 += DW) {
 #pragma unroll
-        for (int d = 0; d < DW; ++d) {
-            const int i = i0 + d;
-            const bool live = i < n_steps;
-            const int xn = xs + 1 == DX ? 0 : xs + 1;
-            read_half(d, xs, 1, hb[1]);
-            if (live) mma_half(hb[0], 0, d, i & 3);
-            // step i + 1's tile and x1 are in: pending may be the scales of
-            // step i + 1 (issued last) and, WS, the x1 of step i + 2
-            if constexpr (WS)
-                wait_vmcnt<kXLd + kSc>();
-            else
-                wait_vmcnt<kSc>();
-            lds_reads_done();   // this wave's reads of step i are done ...
-            __builtin_amdgcn_s_barrier();   // ... and every wave's: its stages may be refilled
-            lds_reads_done();
-            __builtin_amdgcn_sched_barrier(0);
-            read_half((d + 1) % DW, xn, 0, hb[0]);
-            if constexpr (WS) {
-                if (((i + 2) & 3) == 0) wload(step_of(i + 2), 1);
-            }
-            issue_w(step_of(i + 2), d);
-            issue_x(step_of(i + DX), xs);
-            if (live) mma_half(hb[1], 1, d, i & 3);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_sc(step_of(i + 2), d);
-            if constexpr (WS) {
-                if ((i & 3) == 3) {   // the next window becomes current
-#pragma unroll
-                    for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
-                    wdl[0] = wdl[1];
+            for (int d = 0; d < DW; ++d) {
+                const int i = i0 + d;
+                const bool live = i < n_steps;
+                const int xn = xs + 1 == DX ? 0 : xs + 1;
+                read_half(d, xs, 1, hb[1], lf_c);
+                if (live) mma_half(hb[0], 0, d, i & 3, lf_c);
+                // step i + 1's tile and x1 are in: pending may be the scales of
+                // step i + 1 (issued last) and, WS, the x1 of step i + 2
+                if constexpr (WS)
+                    wait_vmcnt<kXLd + kSc>();
+                else
+                    wait_vmcnt<kSc>();
+                lds_reads_done();   // this wave's reads of step i are done ...
+                __builtin_amdgcn_s_barrier();   // ... and every wave's: its stages may be refilled
+                lds_reads_done();
+                __builtin_amdgcn_sched_barrier(0);
+                read_half((d + 1) % DW, xn, 0, hb[0], lf_c);
+                if constexpr (WS) {
+                    if (((i + 2) & 3) == 0) wload(step_of(i + 2), 1);
                 }
+                issue_w(step_of(i + 2), d);
+                issue_x(step_of(i + DX), xs);
+                if (live) mma_half(hb[1], 1, d, i & 3, lf_c);
+                __builtin_amdgcn_sched_barrier(0);
+                issue_sc(step_of(i + 2), d);
+                if constexpr (WS) {
+                    if ((i & 3) == 3) {   // the next window becomes current
+#pragma unroll
+                        for (int f = 0; f < RF; ++f) wa[0][f] = wa[1][f];
+                        wdl[0] = wdl[1];
+                    }
+                }
+                xs = xn;
+                __builtin_amdgcn_sched_barrier(0);
             }
-            xs = xn;
-            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    if (mcount > (RF - 1) * kTileM)
+        main_loop(IntC<RF>{});
+    else if (RF == 2 && mcount > 0)
+        main_loop(IntC<1>{});
+    else
+        main_loop(IntC<0>{});
     wait_vmcnt<0>();   // the trailing re-reads, before the stages are reused
     epilogue<4, RF, 4>(p, acc, m0, n0, store_rows, rinfo);
 }

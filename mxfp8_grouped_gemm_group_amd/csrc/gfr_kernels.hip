@@ -162,7 +162,13 @@ struct WorkList {
 // Experts with at least this many tokens are processed by cooperative block
 // items: the four waves of a block share one weight-tile stream and each
 // applies it to its own 32 rows, so one streamed tile serves 128 rows.
+// Where the larger experts run two-fragment units (kinds with WIDE groups),
+// experts of 64-95 tokens stream faster as wave items of two or three row
+// tiles (c4 -1.8 %, c5 -0.8 %, c5_pe -1.1 %, g1_c2t -1.1 % against 64;
+// thresholds of 80, 112 and 128 were each slower on one of c4, c5_fp4 or c5);
+// with one-fragment units 64 stays (96: c4_fp4 +30 %, g1_llada +11 %).
 constexpr int kCoopMinRows = 64;
+constexpr int kCoopMinRowsWide = 96;
 constexpr int kCoopRows = kTileM * kWavesPerBlock;   // 128
 
 // Rows of one cooperative unit: experts with more than 128 rows use 256-row
@@ -189,6 +195,7 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
                                                 int n_tiles_coop, WorkList &wl,
                                                 int64_t *s_scan) {
     const int tid = threadIdx.x;
+    constexpr int kMinRows = WIDE ? kCoopMinRowsWide : kCoopMinRows;
     static_assert(kPerThread == 4, "one thread reads 4 consecutive group_list entries");
     // All loads are issued before any is used (one memory latency, not one per
     // entry); reads past the list (or of an absent list when M = 0) return 0.
@@ -242,9 +249,9 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
             wl.cnt[e] = cnt;
         }
         run += c[i];
-        const int64_t si = cnt >= kCoopMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
+        const int64_t si = cnt >= kMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
         const int gr = coop_group_rows<WIDE>(cnt);
-        const int64_t li = cnt >= kCoopMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
+        const int64_t li = cnt >= kMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
         items[i] = si | (li << 32);
         isum += items[i];
     }

@@ -843,9 +843,14 @@ __device__ __forceinline__ void epilogue_swiglu(const FusedParams &p, const v16f
 //     group); one s_barrier per step publishes the tile and retires the slot
 //     that is refilled next.
 // [K, N]: the slot is row-major [64 K rows][128 B] with the eight 16-byte
-//   chunks of row r XOR-swizzled by (r >> 1) & 3 (the transpose reads of a
-//   16-lane group then hit distinct banks); the operand comes out of LDS
-//   already K-contiguous per column (ds_read_b64_tr_b8).
+//   chunks of row r XOR-swizzled by 2 ((r >> 1) & 3); the operand comes out
+//   of LDS already K-contiguous per column (ds_read_b64_tr_b8).  A half wave
+//   of a transposing read (the 64 banks serve 32 lanes of 8 bytes at once)
+//   is two 16-lane groups reading logical chunks 2j and 2j + 1 of the same
+//   8 rows: with the even swizzle one group lands on even physical chunks and
+//   the other on odd ones, 64 distinct banks (with (r >> 1) & 3 both groups
+//   covered the same four chunks: two-way conflicts, 0.96 conflict cycles
+//   per conflict-free cycle in c3; p1_tc_b -3 %, c3 -0.8 %).
 // [N, K]: the slot is [128 cols][64 K bytes] with the four 16-byte chunks of
 //   a column XOR-swizzled by (col >> 1) & 3 so that 16-byte LDS reads of 32
 //   lanes do not collide on banks.
@@ -1049,17 +1054,17 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         // as for FP8 [K, N] below, in bytes: the tile's 128 byte columns are
         // weight columns [n0, n0 + 256)
         const int n0b = n0 / 2;
-        const int cb = n0b + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+        const int cb = n0b + 16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3)));
         vb[0] = (lane >> 3) * Nb + (cb < Nb ? cb : n0b);
         const int G = lane >> 4, sl = lane & 15, i = sl >> 1, h = sl & 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            tr_addr[j] = (16 * g + i) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((i >> 1) & 3)) + 8 * h;
+            tr_addr[j] = (16 * g + i) * kTileN + 16 * ((2 * j + (G & 1)) ^ (2 * ((i >> 1) & 3))) + 8 * h;
     } else if (KN) {
         // load u, lane l: K row r = 8u + l/8 (row offset in soffset); it fills
         // physical chunk l%8 of the slot row, which holds logical chunk
-        // (l%8) ^ ((r >> 1) & 3) = (l%8) ^ ((l >> 4) & 3)
-        const int chunk_col = wcol(16 * ((lane & 7) ^ ((lane >> 4) & 3)));
+        // (l%8) ^ 2 ((r >> 1) & 3) = (l%8) ^ 2 ((l >> 4) & 3)
+        const int chunk_col = wcol(16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3))));
         vb[0] = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
         if constexpr (SPLIT) {   // the up tile: same chunk, I columns further
             const int up_col = up0 + chunk_col;
@@ -1070,7 +1075,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         const int G = lane >> 4, sl = lane & 15, i = sl >> 1, h = sl & 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            tr_addr[j] = (16 * g + i) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((i >> 1) & 3)) + 8 * h;
+            tr_addr[j] = (16 * g + i) * kTileN + 16 * ((2 * j + (G & 1)) ^ (2 * ((i >> 1) & 3))) + 8 * h;
         // scale byte (ks, col, g) is byte 2 col + g of row ks of [K/64, N, 2];
         // the aligned dword holds columns col & ~1 and col | 1
 #pragma unroll
@@ -1847,7 +1852,7 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
 // two weight stages, two or three x1 stages, the x1 rows staged through LDS
 // as whole 128-byte lines -- with the [K, N] weight tile: a stage holds the
 // step's 128 K rows x 128 bytes as two 64-K halves of the [K, N] slot layout
-// (16-byte chunks of row r XOR-swizzled by (r >> 1) & 3), moved by 16
+// (16-byte chunks of row r XOR-swizzled by 2 ((r >> 1) & 3)), moved by 16
 // direct-to-LDS loads of 8 K rows (four per wave; every K row segment of the
 // tile is one 128-byte line), and read K-contiguous per column with
 // transposing reads.  Against the 64-K cooperative units each x1 line is
@@ -1885,8 +1890,8 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     // weight load u (u = 4w + uu): K row 8u + l/8 of the step (row offset in
     // the scalar offset); it fills physical chunk l%8 of its slot row, which
-    // holds logical chunk (l%8) ^ ((l >> 4) & 3); columns past N re-read n0
-    const int chunk_col = n0 + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+    // holds logical chunk (l%8) ^ 2 ((l >> 4) & 3); columns past N re-read n0
+    const int chunk_col = n0 + 16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3)));
     const int vw = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
     // x1 load v of 8 rows: ck_unit's
     int vx[kXLd];
@@ -1903,7 +1908,7 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
         const int G = lane >> 4, sl = lane & 15, ii = sl >> 1, h = sl & 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            tr[j] = (16 * g + ii) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((ii >> 1) & 3)) + 8 * h;
+            tr[j] = (16 * g + ii) * kTileN + 16 * ((2 * j + (G & 1)) ^ (2 * ((ii >> 1) & 3))) + 8 * h;
     }
     // scale rows: x1 row 32f + c (row 0 past the last token: its operand is
     // zero); weight scale dword of (64-K row, column pair of 32j + c)
@@ -2335,7 +2340,7 @@ __device__ __forceinline__ void cw_item(const FusedParams &p, int e, int m0, int
 // Wave item for FP8 [K, N] weights (finalize operator, experts below the
 // cooperative size): 32 tokens x 128 columns, K steps of 128, one wave.
 // A step's weight tile is 128 K rows x 128 B (16 KB: two 64-K halves of the
-// [K, N] slot layout, rows' 16-byte chunks XOR-swizzled by (r >> 1) & 3),
+// [K, N] slot layout, rows' 16-byte chunks XOR-swizzled by 2 ((r >> 1) & 3)),
 // moved by 16 direct-to-LDS loads of 8 rows x 128 B and read K-contiguous
 // with ds_read_b64_tr_b8 one 64-K half at a time; the x1 rows are gathered
 // into registers, each row's 128-byte line once per step (with 64-K steps
@@ -2369,9 +2374,9 @@ __device__ __forceinline__ void kw_item(const FusedParams &p, int e, int m0, int
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     // load u, lane l: K row 8u + l/8 of the step (row offset in the scalar
     // offset), physical chunk l%8 of the slot row holding logical chunk
-    // (l%8) ^ ((r >> 1) & 3) = (l%8) ^ ((l >> 4) & 3); columns past N re-read
+    // (l%8) ^ 2 ((r >> 1) & 3) = (l%8) ^ 2 ((l >> 4) & 3); columns past N re-read
     // column n0
-    const int chunk_col = n0 + 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+    const int chunk_col = n0 + 16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3)));
     const int vw = (lane >> 3) * N + (chunk_col < N ? chunk_col : n0);
     // transpose reads of a 64-K half (see lds_issue_kn): lane s of 16-lane
     // group G reads K row 16g + (s >> 1) (+ the read's offset), columns
@@ -2381,7 +2386,7 @@ __device__ __forceinline__ void kw_item(const FusedParams &p, int e, int m0, int
         const int G = lane >> 4, sl = lane & 15, ii = sl >> 1, h = sl & 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            tr[j] = (16 * g + ii) * kTileN + 16 * ((2 * j + (G & 1)) ^ ((ii >> 1) & 3)) + 8 * h;
+            tr[j] = (16 * g + ii) * kTileN + 16 * ((2 * j + (G & 1)) ^ (2 * ((ii >> 1) & 3))) + 8 * h;
     }
     // x1: lane (c, g) gathers row c's bytes 32q + 16g of the step (rows past
     // the last token read as zero); scales of row c (row 0 past it)

@@ -4,11 +4,14 @@ A seeded random sample alone can miss a class of work unit.  The rows chosen
 here are the union of
   * ``n_random`` seeded random rows, the first and last row, and the rows on
     both sides of each edge of the shared-expert range;
-  * for every expert large enough for the kernels' cooperative units
-    (>= 64 tokens), one token in every 128-row group of its range, at an
-    offset that moves through the group from one group to the next (so the
-    four waves and both 32-row fragments of a wave are hit across groups),
-    plus the expert's last token (its last, usually partial, group);
+  * for every expert of at least 64 tokens (the smallest expert with
+    cooperative units: 64 where a wave holds one 32-row fragment, 96 where it
+    holds two; the 64-95 token experts of the latter kinds run as wave items
+    of two or three row tiles, which the same rows cover), one token in every
+    128-row group of its range, at an offset that moves through the group
+    from one group to the next (so the four waves and both 32-row fragments
+    of a wave are hit across groups), plus the expert's last token (its last,
+    usually partial, group);
   * the last token of ``n_small`` seeded experts below that size (the ragged
     tail of a 32-row wave item),
 each mapped to the output row it is scattered to.  Every selected row is then
@@ -18,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-COOP_MIN_ROWS = 64   # tokens from which an expert gets cooperative units
+COOP_MIN_ROWS = 64   # smallest expert given per-group rows (see above)
 GROUP_STEP = 128     # rows per cooperative group (256-row groups are two of them)
 
 

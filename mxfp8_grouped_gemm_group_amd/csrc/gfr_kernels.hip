@@ -500,37 +500,6 @@ __device__ __forceinline__ void lds_wait(v4i (&t)[8]) {
                  : "memory");
 }
 
-// x1 operands of one [K, N] step of a two-fragment cooperative unit staged in
-// LDS: 16-byte reads at a0 (K half 0) and a1 (K half 1) of fragment 0, and
-// 2048 bytes further (fragment 1), issued without waiting.
-__device__ __forceinline__ void lds_issue_x(uint32_t a0, uint32_t a1, v4i (&t)[4]) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %4 offset:2048\n\t"
-        "ds_read_b128 %3, %5 offset:2048"
-        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
-        : "v"(a0), "v"(a1)
-        : "memory");
-}
-
-// ... one fragment: the reads at a0 and a1 only (t[2], t[3] untouched).
-__device__ __forceinline__ void lds_issue_x1(uint32_t a0, uint32_t a1, v4i (&t)[4]) {
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3"
-        : "=&v"(t[0]), "=&v"(t[1])
-        : "v"(a0), "v"(a1)
-        : "memory");
-}
-
-__device__ __forceinline__ void lds_wait(v4i (&t)[4]) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
-                 :
-                 : "memory");
-}
-
 // D += A * B with per-lane E8M0 scales; OPSEL_B picks the byte of sb.
 template <int FMT, int OPSEL_B>
 __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f acc, uint32_t sa, uint32_t sb) {
@@ -988,36 +957,6 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     const rsrc_t rb = make_rsrc(p.x2 + e * wbytes, wbytes);
     const rsrc_t rsb = make_rsrc(p.scale + e * p.scale_e_stride, static_cast<int64_t>(KS) * N);
     const int u0 = COOP ? w * kTileLoads : 0;   // first tile load this wave issues
-    // FP8 [K, N] two-fragment cooperative units (finalize operator): the
-    // wave's 64 x1 rows of a step (64 bytes each) go global -> LDS like the
-    // weights, four direct-to-LDS loads of 16 rows each (whole 64-byte row
-    // segments, instead of register gathers that touch 32 rows per
-    // instruction), into a per-wave ring after the block's weight ring; the
-    // 16-byte chunks of row r are XOR-swizzled by (r >> 1) & 3 and the
-    // operands come out with ds_read_b128, one step ahead, like the weights.
-    // One-fragment units (32 rows per wave, 8-slot weight ring) do the same
-    // with 2 KB slots.  (FP8 [N, K] units of the finalize operator are
-    // ck_unit / cw_item below.)
-    constexpr bool kXL = KN && COOP && !FP4 && !I8 && OP == 0;
-    constexpr int kXLoads = 2 * RF;                       // 16-row x1 loads per step
-    constexpr int kXSlotBytes = RF * kTileM * kStepK;     // 32 or 64 rows x 64 bytes
-    char *const xring = ring + D * kSlotBytes + w * D * kXSlotBytes;
-    static_assert(!kXL || D * kSlotBytes + kWavesPerBlock * D * kXSlotBytes <=
-                              kWavesPerBlock * kRingBytes,
-                  "x1 rings fit the block's LDS ring area");
-    int vx[4] = {0, 0, 0, 0};   // lane offsets of the x1 loads (row 16u + lane/4)
-    uint32_t xa[2] = {0, 0};    // slot-relative operand addresses, K halves 0 and 1
-    if constexpr (kXL) {
-#pragma unroll
-        for (int u = 0; u < kXLoads; ++u) {
-            const int r = 16 * u + (lane >> 2);
-            vx[u] = r * Kb + 16 * ((lane & 3) ^ ((r >> 1) & 3));
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            xa[q] = c * 64 + 16 * ((2 * q + g) ^ ((c >> 1) & 3));
-    }
-
     // Weight-tile load offsets (lane part) and weight-scale offsets.  Columns
     // past N (last partial n-tile) re-read column n0; their results are never
     // written.
@@ -1135,17 +1074,10 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // after the window's last step; a window that would run past the row's
     // end starts earlier (still 16 bytes inside the row) and the steps' dword
     // index is shifted by the difference.
-    // FP8 [K, N] two-fragment cooperative units with x1 in LDS (kXL): only
-    // the x1 scales are windowed -- one 8-byte load per row holds the four
-    // steps' two bytes each (a per-step dword gather touched 32 rows for 2
-    // bytes each); the weight scales are contiguous per step and stay
-    // per-step loads.
-    static_assert(!WS || (!I8 && D == 4 && (!KN || (!FP4 && OP == 0 && COOP && RF == 2))),
-                  "windowed scales: 4 slots; [K,N] only FP8 two-fragment cooperative units");
-    constexpr bool kWSKN = WS && KN;
+    static_assert(!WS || (!I8 && !KN && D == 4), "windowed scales: [N, K], 4 slots");
     constexpr int kSA = I8 || WS ? 0 : 1;            // x1-scale loads per step and fragment
     constexpr int kSB = I8 || (WS && !KN) ? 0 : KN4 ? 8 : KN ? 4 : 2;   // weight-scale loads per step
-    constexpr int kXW = kWSKN ? RF : WS ? RF + 2 : 0;   // loads per window
+    constexpr int kXW = WS ? RF + 2 : 0;   // loads per window
     // 32-element scale blocks per step and row: [K,N] 2, [N,K] 4
     constexpr int kBlk = KN ? 2 : 4;
     StepRegs<kAL, RF, (kSB > 0 ? kSB : 1)> regs[D];
@@ -1154,23 +1086,14 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // the unrolled ring index's parity so that it is a compile-time constant
     // (ks0 * 2 and D are even; for the clamped re-reads past the last step it
     // may differ, and those are never consumed)
-    // WS: scale windows, [0] current, [1] next ([K,N]: x1 scales only, 8 bytes)
-    v4i wsa[2][kWSKN ? 1 : RF], wsb[2][2];
-    v2i wsk[2][kWSKN ? RF : 1];
+    // WS: scale windows, [0] current, [1] next
+    v4i wsa[2][RF], wsb[2][2];
     int wdl[2] = {0, 0};   // WS: step shift of a window moved back from the row end
     // steps of a whole row; each takes kBlk scale bytes of it
     const int k_row = K / (KN ? kStepK : kStepKNK);
     auto wload = [&](int vs, int set) {   // the window starting at step vs
         const int start = vs < k_row - 4 ? vs : k_row - 4;
         wdl[set] = vs - start;
-        if constexpr (kWSKN) {
-            // x1 scale bytes 2 start .. 2 start + 7 of each row (K is a
-            // multiple of 128, so k_row and start are even: dword aligned)
-#pragma unroll
-            for (int f = 0; f < RF; ++f)
-                wsk[set][f] = __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[f] + kBlk * start, 0, 0);
-            return;
-        }
 #pragma unroll
         for (int f = 0; f < RF; ++f)
             wsa[set][f] = __builtin_amdgcn_raw_buffer_load_b128(rsa, vsa[f] + kBlk * start, 0, 0);
@@ -1209,20 +1132,11 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             if (wstart) wload(vs, 1);
         }
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1)> &r = regs[slot];
-        if constexpr (kXL) {
-            static_assert(!kXL || RF * kAL == kXLoads, "as many x1 loads per step as in registers");
 #pragma unroll
-            for (int u = 0; u < kXLoads; ++u) {
-                lds_void_t *dst = (lds_void_t *)(xring + slot * kXSlotBytes + u * 1024);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vx[u], k0, 0, 0);
-            }
-        } else {
+        for (int f = 0; f < RF; ++f)
 #pragma unroll
-            for (int f = 0; f < RF; ++f)
-#pragma unroll
-                for (int q = 0; q < kAL; ++q)
-                    r.a[f][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[f], k0 + 32 * q, 0);
-        }
+            for (int q = 0; q < kAL; ++q)
+                r.a[f][q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[f], k0 + 32 * q, 0);
         // x1 scale bytes of the step: [K,N] (2 ks + g) & 3 of the dword at
         // (2 ks) & ~3; [N,K] the step's kBlk bytes at kBlk ks
 #pragma unroll
@@ -1239,14 +1153,6 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     // B operands of one step in registers, double-buffered across steps.
     using BTile = std::conditional_t<KN, v2i[16], v4i[8]>;
     BTile bt[2];
-    v4i at[2][4];   // kXL: x1 operands of a step (fragment f, K half q at 2 f + q)
-    auto read_a = [&](int slot, v4i (&a)[4]) {
-        const uint32_t base = lds_addr(xring + slot * kXSlotBytes);
-        if constexpr (RF == 2)
-            lds_issue_x(base + xa[0], base + xa[1], a);
-        else
-            lds_issue_x1(base + xa[0], base + xa[1], a);
-    };
     // [N,K] reads: 64-K half s, 16-byte half h of the lane's 32 operand bytes
     // = logical chunk 4s + 2h + g of column 32j + c (column c's slot row at
     // 128 c, group j 4 KB further)
@@ -1275,8 +1181,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
         }
     };
 
-    auto mma = [&](int slot, const BTile &b, const v4i (&ax)[4], bool live, int vs, int hf,
-                   int wpos) {
+    auto mma = [&](int slot, const BTile &b, bool live, int vs, int hf, int wpos) {
         const int ks = SPLIT ? vs >> 1 : vs;
         StepRegs<kAL, RF, (kSB > 0 ? kSB : 1)> &r = regs[slot];
         // padding rows and padding steps (re-reads past the last K step)
@@ -1315,17 +1220,9 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
                     acc[f][j] = mfma<FMT, 0>(a, bj, acc[f][j], sa, r.sb[j][0] >> sb_shift);
                 }
             } else if constexpr (KN) {
-                v8i a = on ? cat(r.a[f][0], r.a[f][1]) : v8i{};
-                if constexpr (kXL) a = on ? cat(ax[2 * f], ax[2 * f + 1]) : v8i{};
-                // byte (2 ks + g) & 3 of the x1 scale dword; windowed: byte
-                // 2 (j & 1) + g of the window's dword j >> 1, j the step's
-                // index in the window
-                uint32_t sa = r.sa[f][0] >> (8 * (2 * (ks & 1) + g));
-                if constexpr (kWSKN) {
-                    const int jw = wpos + wdl[0];
-                    sa = static_cast<uint32_t>(jw < 2 ? wsk[0][f].x : wsk[0][f].y) >>
-                         (8 * (2 * (jw & 1) + g));
-                }
+                const v8i a = on ? cat(r.a[f][0], r.a[f][1]) : v8i{};
+                // byte (2 ks + g) & 3 of the x1 scale dword
+                const uint32_t sa = r.sa[f][0] >> (8 * (2 * (ks & 1) + g));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v8i bj = {b[4 * j].x,     b[4 * j].y,     b[4 * j + 1].x, b[4 * j + 1].y,
@@ -1406,9 +1303,7 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
     if (COOP) __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_b(0, bt[0]);
-    if constexpr (kXL) read_a(0, at[0]);
     lds_wait(bt[0]);
-    if constexpr (kXL) lds_wait(at[0]);
     for (int i0 = 0; i0 < n_steps; i0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -1420,7 +1315,6 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             if (COOP) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             read_b((d + 1) % D, bt[(d + 1) & 1]);
-            if constexpr (kXL) read_a((d + 1) % D, at[(d + 1) & 1]);
             // [N, K]: slot d was read into registers last iteration (and, in
             // a cooperative unit, by every wave: the barrier above), so its
             // refill goes out before this step's MFMAs, which would otherwise
@@ -1428,23 +1322,17 @@ __device__ __forceinline__ void routed_item(const FusedParams &p, int e, int m0,
             // step i + D follow the MFMAs that consume register set d.
             // [K, N] measured faster with the whole group after the MFMAs.
             if constexpr (kTileFirst) issue_tile(step_of(i + D), d, d & 1);
-            mma(d, bt[d & 1], at[d & 1], i < n_steps, step_of(i), d & 1, d);
+            mma(d, bt[d & 1], i < n_steps, step_of(i), d & 1, d);
             __builtin_amdgcn_sched_barrier(0);
             issue_regs(step_of(i + D), d, d & 1, d == 0);
             if constexpr (!kTileFirst) issue_tile(step_of(i + D), d, d & 1);
             lds_wait(bt[(d + 1) & 1]);
-            if constexpr (kXL) lds_wait(at[(d + 1) & 1]);
             if constexpr (WS) {
                 if (d == 3) {   // the next window becomes current
-                    if constexpr (kWSKN) {
 #pragma unroll
-                        for (int f = 0; f < RF; ++f) wsk[0][f] = wsk[1][f];
-                    } else {
-#pragma unroll
-                        for (int f = 0; f < RF; ++f) wsa[0][f] = wsa[1][f];
-                        wsb[0][0] = wsb[1][0];
-                        wsb[0][1] = wsb[1][1];
-                    }
+                    for (int f = 0; f < RF; ++f) wsa[0][f] = wsa[1][f];
+                    wsb[0][0] = wsb[1][0];
+                    wsb[0][1] = wsb[1][1];
                     wdl[0] = wdl[1];
                 }
             }
@@ -2602,10 +2490,6 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // step's; a window is four 128-K steps of a row's scale bytes: K >= 512)
     constexpr bool kWS = TRANS && FMT != 8;
     const bool ws_ok = kWS && p.K >= 4 * kStepKNK;
-    // [K, N] FP8 finalize: windowed x1 scales in the two-fragment cooperative
-    // units (their x1 bytes come through LDS, which leaves the registers)
-    constexpr bool kWSC = kWS || (!TRANS && (FMT == 0 || FMT == 1) && OP == 0);
-    const bool wsc_ok = kWS ? ws_ok : kWSC && p.K >= 4 * kStepK;
     // K elements per step: 64 ([K,N]), 128 ([N,K] FP8), 256 ([N,K] FP4): one
     // step always moves 8 KB of the weight tile
     const int k_steps = p.K / (!TRANS ? kStepK : FMT == 4 ? 2 * kStepKNK : kStepKNK);
@@ -2839,8 +2723,8 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
                 }
             } else {
                 if (kWide && gr > kCoopRows) {
-                    if constexpr (kWSC) {
-                        if (wsc_ok) {
+                    if constexpr (kWS) {
+                        if (ws_ok) {
                             routed_item<FMT, !TRANS, true, 2, OP, true>(
                                 p, e, m0, mcount, nt * kOutN, ks0, ks1, store_rows, s_ring, w);
                             continue;

@@ -853,6 +853,16 @@ struct IntC {
     static constexpr int value = V;
 };
 
+// An empty use of a loaded register: the load stays, and the compiler waits
+// for it here.  The cooperative units' explicit vmcnt waits count every load
+// a step issues, so a load whose result a loop instance never reads (the
+// scales of a fragment without live rows) must not be dropped: the waits
+// would then let that many of the step's later tile loads pass unfinished.
+template <class T>
+__device__ __forceinline__ void keep_loaded(const T &v) {
+    asm volatile("" ::"v"(v));
+}
+
 // Rotation of an [N, K] wave item's K order.  A step reads the same 128-byte
 // piece of 128 weight rows (columns); where a row is 4 KB long (MXFP4 K 8192)
 // every item in flight then hits the same in-row offset, the rows of
@@ -1618,6 +1628,24 @@ __device__ __forceinline__ void ck_unit(const FusedParams &p, int e, int m0, int
             sb[j] = sb_r[set][j][FP4 ? s2 : 0];
             if constexpr (WS) sb[j] = pick(wb[0][j], sw);
         }
+        // the scales of fragments without live rows, consumed where their
+        // MFMAs would be (keep_loaded)
+#pragma unroll
+        for (int f = LF; f < RF; ++f) {
+            if constexpr (WS)
+                keep_loaded(wa[0][f]);
+            else
+                keep_loaded(sa_r[set][f][FP4 ? s2 : 0]);
+        }
+        if constexpr (LF == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (WS)
+                    keep_loaded(wb[0][j]);
+                else
+                    keep_loaded(sb_r[set][j][FP4 ? s2 : 0]);
+            }
+        }
         if constexpr (FP4) {
             const v4i z = {0, 0, 0, 0};
 #pragma unroll
@@ -1904,6 +1932,19 @@ __device__ __forceinline__ void kc_unit(const FusedParams &p, int e, int m0, int
     auto mma_half = [&](const Half &t, int s2, int set, int wpos, auto lf_c) {
         constexpr int LF = decltype(lf_c)::value;
         const int shf = 8 * (2 * s2 + g);
+        // the scales of fragments without live rows, consumed where their
+        // MFMAs would be (keep_loaded)
+#pragma unroll
+        for (int f = LF; f < RF; ++f) {
+            if constexpr (WS)
+                keep_loaded(wa[0][f]);
+            else
+                keep_loaded(sa_r[set][f]);
+        }
+        if constexpr (LF == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) keep_loaded(sb_r[set][s2][j]);
+        }
 #pragma unroll
         for (int f = 0; f < LF; ++f) {
             uint32_t sa = 0;

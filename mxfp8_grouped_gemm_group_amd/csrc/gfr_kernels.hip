@@ -150,13 +150,15 @@ struct SatAddU32 {
 struct WorkList {
     int *start;   // [E]   first token of expert e
     int *cnt;     // [E]   tokens of expert e
-    int *spref;   // [E+1] prefix of per-expert wave items (one K split)
+    int *spref;   // [n_we+1] prefix of wave items (one K split), experts in `wperm` order
+    int *wperm;   // [n_we]  experts with wave items, in the order their items are dealt
     int *lpref;   // [n_ce+1] prefix of cooperative block items, experts in `perm` order
     int *perm;    // [n_ce]  cooperative experts, most rows per cooperative group first
     int routed_tokens;  // sum of counts
     int sitems;         // spref[E]
     int litems;         // lpref[n_ce]
     int n_ce;           // experts with cooperative units
+    int n_we;           // experts with wave items
 };
 
 // Experts with at least this many tokens are processed by cooperative block
@@ -233,11 +235,18 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
     block_scan_u32<1>(tok, tok_total, s32, SatAddU32{cap});
     const int64_t total_tokens = tok_total[0];
     int64_t run = tok[0];
-    // Both item counts: wave items low, block items high (each total stays
-    // below 2^31: the host bounds (M/32 + E) * ceil(N/128)).
-    int64_t isum = 0;
+    // Item counts (each total stays below 2^31: the host bounds
+    // (M/32 + E) * ceil(N/128)).  Wave items go in classes by the expert's
+    // row tiles -- one, two, three or more -- dealt in that order: a unit of
+    // four wave items of a one-row-tile expert streams four weight tiles, of
+    // a two-row-tile expert two (its waves pair up on a tile), so the costly
+    // units come first and the cheap ones fill the end of the launch (the
+    // snake deal then balances like a longest-first schedule).  Within a
+    // class the experts keep their index order.
     int64_t items[kPerThread];
-    int ccnt[kPerThread];
+    int ccnt[kPerThread], wcls[kPerThread];
+    // scan values: class items 0..2, class experts (0 | 1 << 16, 2), block items
+    uint32_t iv[6] = {0, 0, 0, 0, 0, 0}, it[6];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
@@ -249,33 +258,52 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
             wl.cnt[e] = cnt;
         }
         run += c[i];
-        const int64_t si = cnt >= kMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
+        const int mt = (cnt + kTileM - 1) / kTileM;
+        const int64_t si = cnt >= kMinRows ? 0 : static_cast<int64_t>(mt) * n_tiles;
         const int gr = coop_group_rows<WIDE>(cnt);
         const int64_t li = cnt >= kMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
         items[i] = si | (li << 32);
-        isum += items[i];
+        wcls[i] = si > 0 ? (mt < 3 ? mt - 1 : 2) : -1;
+        if (wcls[i] >= 0) {
+            iv[wcls[i]] += static_cast<uint32_t>(si);
+            if (wcls[i] < 2) iv[3] += 1u << (16 * wcls[i]);
+            else iv[4] += 1u;
+        }
+        iv[5] += static_cast<uint32_t>(li);
     }
-    uint32_t iv[2] = {static_cast<uint32_t>(isum), static_cast<uint32_t>(isum >> 32)}, it[2];
-    block_scan_u32<2>(iv, it, s32, AddU32{});
-    const int64_t total_items = static_cast<int64_t>(it[0]) | (static_cast<int64_t>(it[1]) << 32);
-    int64_t ipre = static_cast<int64_t>(iv[0]) | (static_cast<int64_t>(iv[1]) << 32);
+    block_scan_u32<6>(iv, it, s32, AddU32{});
+    const uint32_t t_items[3] = {it[0], it[1], it[2]};
+    const uint32_t t_exp[3] = {it[3] & 0xffff, it[3] >> 16, it[4]};
+    const uint32_t off_items[3] = {0, t_items[0], t_items[0] + t_items[1]};
+    const uint32_t off_exp[3] = {0, t_exp[0], t_exp[0] + t_exp[1]};
+    uint32_t run_items[3] = {iv[0], iv[1], iv[2]};
+    uint32_t run_exp[3] = {iv[3] & 0xffff, iv[3] >> 16, iv[4]};
+    uint32_t lrun = iv[5];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
-        if (e < p.E) {
-            wl.spref[e] = static_cast<int>(ipre & 0xffffffff);
-            wl.lpref[e] = static_cast<int>(ipre >> 32);
+        const int k = wcls[i];
+        if (k >= 0) {
+            const int rank = static_cast<int>(off_exp[k] + run_exp[k]);
+            wl.spref[rank] = static_cast<int>(off_items[k] + run_items[k]);
+            wl.wperm[rank] = e;
+            run_items[k] += static_cast<uint32_t>(items[i] & 0xffffffff);
+            run_exp[k] += 1;
         }
-        ipre += items[i];
+        if (e < p.E) wl.lpref[e] = static_cast<int>(lrun);
+        lrun += static_cast<uint32_t>(items[i] >> 32);
     }
+    const int n_we = static_cast<int>(t_exp[0] + t_exp[1] + t_exp[2]);
+    const uint32_t sitems = t_items[0] + t_items[1] + t_items[2];
     if (tid == 0) {
-        wl.spref[p.E] = static_cast<int>(total_items & 0xffffffff);
-        wl.lpref[p.E] = static_cast<int>(total_items >> 32);
+        wl.spref[n_we] = static_cast<int>(sitems);
+        wl.lpref[p.E] = static_cast<int>(it[5]);
     }
     wl.routed_tokens = static_cast<int>(total_tokens < p.M ? total_tokens : p.M);
-    wl.sitems = static_cast<int>(total_items & 0xffffffff);
-    wl.litems = static_cast<int>(total_items >> 32);
+    wl.sitems = static_cast<int>(sitems);
+    wl.litems = static_cast<int>(it[5]);
     wl.n_ce = 0;
+    wl.n_we = n_we;
     if (bad && blockIdx.x == 0) flag(p.status, GFR_DEV_BAD_GROUP_LIST);
     __syncthreads();
     if (wl.litems == 0) return;
@@ -2501,6 +2529,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     __shared__ int s_start[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_spref[kMaxExperts + 1];
+    __shared__ int s_wperm[kMaxExperts];
     __shared__ int s_lpref[kMaxExperts + 1];
     __shared__ __attribute__((aligned(16))) int s_perm[kMaxExperts];
     __shared__ int64_t s_scan[kBlockThreads];
@@ -2518,7 +2547,7 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     const int n_tiles = ((OP == 0 ? p.N : p.I) + kOutN - 1) / kOutN;
     constexpr int kOutNC = kOutN;                   // output columns per cooperative unit
     const int n_tiles_c = n_tiles;
-    WorkList wl{s_start, s_cnt, s_spref, s_lpref, s_perm, 0, 0, 0, 0};
+    WorkList wl{s_start, s_cnt, s_spref, s_wperm, s_lpref, s_perm, 0, 0, 0, 0, 0};
     // two-fragment cooperative groups except where a fragment has 8
     // accumulators (MXFP4 and W4A8 [K, N], the upstream step with [K, N])
     constexpr bool kWide = FMT != 8 && !(OP == 1 && !TRANS) && (FMT != 4 || TRANS);
@@ -2782,10 +2811,11 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int it = (u - coop_units) * kWavesPerBlock + w;
             if (it >= wave_items) continue;
             const int q = static_cast<int>(it / S);
-            const int e = __builtin_amdgcn_readfirstlane(find_expert(s_spref, p.E, q));
+            const int rk = __builtin_amdgcn_readfirstlane(find_expert(s_spref, wl.n_we, q));
+            const int e = __builtin_amdgcn_readfirstlane(s_wperm[rk]);
             const int e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
             const int e_start = __builtin_amdgcn_readfirstlane(s_start[e]);
-            const int e_pref = __builtin_amdgcn_readfirstlane(s_spref[e]);
+            const int e_pref = __builtin_amdgcn_readfirstlane(s_spref[rk]);
             const int mt_count = (e_cnt + kTileM - 1) / kTileM;
             const int local = it - static_cast<int>(e_pref) * S;
             // items of an expert: row tiles fastest, then K ranges, then

@@ -2649,7 +2649,10 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // cooperative units hardly use HBM (their weights are shared through L2)
     // and wave units stream it, so mixing them keeps HBM busy while the
     // cooperative work proceeds (c5 2412 -> 2369 µs, c5_fp4 1732 -> 1619,
-    // c4 516 -> 506 against all cooperative units first).
+    // c4 516 -> 506 against all cooperative units first).  Block parity is
+    // XCD parity, so at a given time an XCD runs mostly one kind; starting
+    // half of each XCD's blocks with each kind (parity of blockIdx / 8 or
+    // / 16) measured slower: c5 +1.4-3.5 %, c4 +1.5-2.5 %.
     //
     // A last round with at most half as many units as blocks would leave the
     // other blocks idle for a whole unit (c4: 896 units, 3.5 per block, so

@@ -200,12 +200,14 @@ def test_large_shapes_coverage_rows(name):
     assert_parity(got[torch.as_tensor(rows, device=DEV)], ref, mag, exact=w.exact, what=name)
 
 
-@pytest.mark.parametrize("name", ["c5", "c5_exact", "small_n", "small_t", "small_big_n",
+@pytest.mark.parametrize("name", ["c5", "c5_exact", "c4", "c4_exact", "small_n", "small_t", "small_big_n",
                                   "small_big_t_exact", "small_t_fp4", "small_big_n_fp4",
                                   "small_big_t_k768", "small_huge_t", "small_huge_n_exact"])
 def test_deterministic_mode(name):
     """Deterministic mode: bitwise repeatable, within tolerance of the oracle
-    (bit-exact on integer data)."""
+    (bit-exact on integer data).  c4 holds a cooperative expert whose last row
+    group has 9 rows (waves without live rows in every step): a missed wait
+    there showed as results that changed from launch to launch."""
     w = WORKLOADS[name]
     print(f"case {name} deterministic", flush=True)
     inp = make_inputs(w, DEV)

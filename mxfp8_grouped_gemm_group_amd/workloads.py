@@ -271,6 +271,16 @@ C4_FP4 = _reg(replace(C4, name="c4_fp4", fp8="e2m1", seed=1050))
 # The A2/A3 W4A8 variant ([P3] A2/A3 notes: INT8 x1 with k 2048, INT4 x2 with
 # n 7168, e up to 256): small ragged cases and the page's shape with a
 # skewed routing of 4096 tokens (batch 512, topk 8).
+# The largest expert count the library takes (1024), Zipf-routed: cooperative
+# experts beside hundreds of one- to three-row-tile experts and empty ones,
+# four group_list entries per work-list thread all in use.
+SMALL_MAX_E_N = _reg(Workload("small_max_e_n", batch=600, M=3000, K=256, N=256, E=1024,
+                              fp8="e4m3fn", groups=("zipf", 1.2), group_list_type=1,
+                              exp_range=(-4, 4), row_index="perm", seed=1064))
+SMALL_MAX_E_T = _reg(Workload("small_max_e_t", batch=600, M=3000, K=512, N=256, E=1024,
+                              fp8="e5m2", transpose_x2=True, groups=("zipf", 1.1),
+                              group_list_type=0, exp_range=(-4, 4), row_index="perm",
+                              out_init="normal", seed=1065))
 W4A8_SMALL = _reg(replace(SMALL_N, name="w4a8_small", fp8="w4a8", seed=1061))
 W4A8_SMALL_BIG = _reg(replace(SMALL_BIG_N, name="w4a8_small_big", fp8="w4a8", K=640,
                               w4a8_offset=False, seed=1062))
@@ -288,7 +298,8 @@ for _base in (C1, C2, C3, C4, C5, SMALL_N, SMALL_T, SMALL_BIG_N, SMALL_BIG_T, SM
               SMALL_BIG_T_PE, SMALL_T_FP4, SMALL_BIG_T_FP4, SMALL_BIG_T_FP4_K256,
               SMALL_SPLIT_T_FP4, SMALL_TAIL_T_FP4, SMALL_MANY_T_FP4, C3_FP4T, SMALL_N_FP4,
               SMALL_SPLIT_N_FP4,
-              SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3):
+              SMALL_BIG_N_FP4, C3_FP4, W4A8_SMALL, W4A8_SMALL_BIG, W4A8_P3, SMALL_MAX_E_N,
+              SMALL_MAX_E_T):
     _reg(replace(_base, name=_base.name + "_exact", exact=True, seed=_base.seed + 100,
                  logit="exact" if _base.logit != "none" else "none"))
 

@@ -2657,11 +2657,12 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     // A last round with at most half as many units as blocks would leave the
     // other blocks idle for a whole unit (c4: 896 units, 3.5 per block, so
     // half the blocks ran a fourth one).  In atomic finalize mode each of its
-    // units is cut into T K ranges instead (T = blocks / units left, at least
-    // eight K steps each) and the pieces fill the round; a piece adds its
-    // partial sums like any K split.  The deal is over positions: positions
-    // below R * blocks (R full rounds) are units, position R * blocks + q is
-    // piece q % T of unit R * blocks + q / T.
+    // units is cut into K ranges instead (tT = blocks / units left, or tT + 1
+    // for the last ones so that every rank gets a piece; at least eight K
+    // steps each) and the pieces fill the round; a piece adds its partial
+    // sums like any K split.  The deal is over positions: positions below
+    // R * blocks (R full rounds) are units, the next ones the pieces of the
+    // last round's units in order (unit_of).
     const bool snake = kWide && coop_units > 0;
     const bool tail_ok = OP == 0 && !store_rows && !bsplit;
     auto tail_factor = [&](int n) -> int {   // pieces per unit of n's last round
@@ -2676,15 +2677,29 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
     const int seq_n = snake ? units : coop_units == 0 ? units : 0;
     const int tT = seq_n > 0 ? tail_factor(seq_n) : 1;
     const int seq_full = seq_n / blocks * blocks;
-    const int seq_pos = tT > 1 ? seq_full + (seq_n - seq_full) * tT : seq_n;
-    // position of the split sequence -> unit and piece (T = tT past seq_full)
-    auto unit_of = [&](int g, int &piece) -> int {
+    // The cut round's pieces fill every rank: its last t_x units get one
+    // piece more (tT + 1) where a piece still has eight K steps (c4: 104
+    // units, 56 in halves and 48 in thirds, none of 256 ranks idle; -2.8 %
+    // against halves only, which left 48 ranks without a fourth unit)
+    const int t_left = seq_n - seq_full;
+    const int t_x = (tT > 1 && tT + 1 <= (k_steps / S) / 8) ? blocks - t_left * tT : 0;
+    const int t_n1 = (t_left - t_x) * tT;   // positions of the units cut in tT
+    const int seq_pos = tT > 1 ? seq_full + t_n1 + t_x * (tT + 1) : seq_n;
+    // position of the split sequence -> unit, piece and pieces of that unit
+    auto unit_of = [&](int g, int &piece, int &T) -> int {
+        T = tT;
         if (g < seq_full || tT == 1) {
             piece = 0;
             return g;
         }
-        piece = static_cast<int>((g - seq_full) % tT);
-        return seq_full + (g - seq_full) / tT;
+        const int q = g - seq_full;
+        if (q < t_n1) {
+            piece = q % tT;
+            return seq_full + q / tT;
+        }
+        T = tT + 1;
+        piece = (q - t_n1) % T;
+        return seq_full + (t_left - t_x) + (q - t_n1) / T;
     };
     auto g_of = [&](int k) {
         return k * blocks + ((k & 1) ? blocks - 1 - xcd_block : xcd_block);
@@ -2700,9 +2715,11 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
             const int kq = X / blocks;
             return kq + (g_of(kq) < X ? 1 : 0);
         };
-        const int g_coop = coop_units <= seq_full || tT == 1
-                               ? coop_units
-                               : seq_full + (coop_units - seq_full) * tT;
+        const int g_coop =
+            coop_units <= seq_full || tT == 1 ? coop_units
+            : coop_units - seq_full < t_left - t_x
+                ? seq_full + (coop_units - seq_full) * tT
+                : seq_full + t_n1 + (coop_units - seq_full - (t_left - t_x)) * (tT + 1);
         n_coop = rounds_below(g_coop < seq_pos ? g_coop : seq_pos);
         n_wave = rounds_below(seq_pos) - n_coop;
     } else {
@@ -2719,15 +2736,15 @@ __device__ __forceinline__ void run_units(const FusedParams &p) {
         const bool take_coop = i_wave >= n_wave ||
                                (i_coop < n_coop && ((uu + blockIdx.x) & 1) == 0);
         const int g = take_coop ? coop_pos(i_coop++) : wave_pos_of(i_wave++);
-        int piece = 0;
-        const int u = unit_of(g, piece);
+        int piece = 0, pT = 1;
+        const int u = unit_of(g, piece, pT);
         // K range of a last-round piece inside its unit's range
         auto narrow = [&](int &a, int &b) {
             if (tT > 1 && g >= seq_full) {
                 const int span = b - a;
                 const int a0 = a;
-                a = a0 + span * piece / tT;
-                b = a0 + span * (piece + 1) / tT;
+                a = a0 + span * piece / pT;
+                b = a0 + span * (piece + 1) / pT;
             }
         };
         __syncthreads();   // the previous unit's waves are done with the LDS

@@ -235,18 +235,13 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
     block_scan_u32<1>(tok, tok_total, s32, SatAddU32{cap});
     const int64_t total_tokens = tok_total[0];
     int64_t run = tok[0];
-    // Item counts (each total stays below 2^31: the host bounds
-    // (M/32 + E) * ceil(N/128)).  Wave items go in classes by the expert's
-    // row tiles -- one, two, three or more -- dealt in that order: a unit of
-    // four wave items of a one-row-tile expert streams four weight tiles, of
-    // a two-row-tile expert two (its waves pair up on a tile), so the costly
-    // units come first and the cheap ones fill the end of the launch (the
-    // snake deal then balances like a longest-first schedule).  Within a
-    // class the experts keep their index order.
+    // Both item counts: wave items low, block items high (each total stays
+    // below 2^31: the host bounds (M/32 + E) * ceil(N/128)).  Wave items in
+    // expert order here; with cooperative units of two fragments they are
+    // reordered below.
+    int64_t isum = 0;
     int64_t items[kPerThread];
-    int ccnt[kPerThread], wcls[kPerThread];
-    // scan values: class items 0..2, class experts (0 | 1 << 16, 2), block items
-    uint32_t iv[6] = {0, 0, 0, 0, 0, 0}, it[6];
+    int ccnt[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
@@ -258,52 +253,35 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
             wl.cnt[e] = cnt;
         }
         run += c[i];
-        const int mt = (cnt + kTileM - 1) / kTileM;
-        const int64_t si = cnt >= kMinRows ? 0 : static_cast<int64_t>(mt) * n_tiles;
+        const int64_t si = cnt >= kMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
         const int gr = coop_group_rows<WIDE>(cnt);
         const int64_t li = cnt >= kMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
         items[i] = si | (li << 32);
-        wcls[i] = si > 0 ? (mt < 3 ? mt - 1 : 2) : -1;
-        if (wcls[i] >= 0) {
-            iv[wcls[i]] += static_cast<uint32_t>(si);
-            if (wcls[i] < 2) iv[3] += 1u << (16 * wcls[i]);
-            else iv[4] += 1u;
-        }
-        iv[5] += static_cast<uint32_t>(li);
+        isum += items[i];
     }
-    block_scan_u32<6>(iv, it, s32, AddU32{});
-    const uint32_t t_items[3] = {it[0], it[1], it[2]};
-    const uint32_t t_exp[3] = {it[3] & 0xffff, it[3] >> 16, it[4]};
-    const uint32_t off_items[3] = {0, t_items[0], t_items[0] + t_items[1]};
-    const uint32_t off_exp[3] = {0, t_exp[0], t_exp[0] + t_exp[1]};
-    uint32_t run_items[3] = {iv[0], iv[1], iv[2]};
-    uint32_t run_exp[3] = {iv[3] & 0xffff, iv[3] >> 16, iv[4]};
-    uint32_t lrun = iv[5];
+    uint32_t iv[2] = {static_cast<uint32_t>(isum), static_cast<uint32_t>(isum >> 32)}, it[2];
+    block_scan_u32<2>(iv, it, s32, AddU32{});
+    const int64_t total_items = static_cast<int64_t>(it[0]) | (static_cast<int64_t>(it[1]) << 32);
+    int64_t ipre = static_cast<int64_t>(iv[0]) | (static_cast<int64_t>(iv[1]) << 32);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
-        const int k = wcls[i];
-        if (k >= 0) {
-            const int rank = static_cast<int>(off_exp[k] + run_exp[k]);
-            wl.spref[rank] = static_cast<int>(off_items[k] + run_items[k]);
-            wl.wperm[rank] = e;
-            run_items[k] += static_cast<uint32_t>(items[i] & 0xffffffff);
-            run_exp[k] += 1;
+        if (e < p.E) {
+            wl.spref[e] = static_cast<int>(ipre & 0xffffffff);
+            wl.wperm[e] = e;
+            wl.lpref[e] = static_cast<int>(ipre >> 32);
         }
-        if (e < p.E) wl.lpref[e] = static_cast<int>(lrun);
-        lrun += static_cast<uint32_t>(items[i] >> 32);
+        ipre += items[i];
     }
-    const int n_we = static_cast<int>(t_exp[0] + t_exp[1] + t_exp[2]);
-    const uint32_t sitems = t_items[0] + t_items[1] + t_items[2];
     if (tid == 0) {
-        wl.spref[n_we] = static_cast<int>(sitems);
-        wl.lpref[p.E] = static_cast<int>(it[5]);
+        wl.spref[p.E] = static_cast<int>(total_items & 0xffffffff);
+        wl.lpref[p.E] = static_cast<int>(total_items >> 32);
     }
     wl.routed_tokens = static_cast<int>(total_tokens < p.M ? total_tokens : p.M);
-    wl.sitems = static_cast<int>(sitems);
-    wl.litems = static_cast<int>(it[5]);
+    wl.sitems = static_cast<int>(total_items & 0xffffffff);
+    wl.litems = static_cast<int>(total_items >> 32);
     wl.n_ce = 0;
-    wl.n_we = n_we;
+    wl.n_we = p.E;
     if (bad && blockIdx.x == 0) flag(p.status, GFR_DEV_BAD_GROUP_LIST);
     __syncthreads();
     if (wl.litems == 0) return;
@@ -320,6 +298,50 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         return;
     }
 
+    // Beside two-fragment cooperative units (the snake deal) wave items go in
+    // classes by the expert's row tiles -- one, two, three or more -- dealt
+    // in that order: a unit of four wave items of a one-row-tile expert
+    // streams four weight tiles, of a two-row-tile expert two (its waves pair
+    // up on a tile), so the costly units come first and the cheap ones fill
+    // the end of the launch, like a longest-first schedule (c5 -1.9 %, c5_pe
+    // -2.1 %, c4 -1.3 %).  Within a class the experts keep their index
+    // order.  (It costs about a microsecond of start-up, so shapes without
+    // cooperative units keep the expert order: c1 +2.5 % with the classes.)
+    {
+        int wcls[kPerThread];
+        // scan values: class items 0..2, class experts (0 | 1 << 16, 2)
+        uint32_t cv[5] = {0, 0, 0, 0, 0}, ct[5];
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const uint32_t si = static_cast<uint32_t>(items[i] & 0xffffffff);
+            const int mt = (ccnt[i] + kTileM - 1) / kTileM;
+            wcls[i] = si > 0 ? (mt < 3 ? mt - 1 : 2) : -1;
+            cv[0] += wcls[i] == 0 ? si : 0u;
+            cv[1] += wcls[i] == 1 ? si : 0u;
+            cv[2] += wcls[i] == 2 ? si : 0u;
+            cv[3] += wcls[i] == 0 ? 1u : wcls[i] == 1 ? 1u << 16 : 0u;
+            cv[4] += wcls[i] == 2 ? 1u : 0u;
+        }
+        block_scan_u32<5>(cv, ct, s32, AddU32{});   // also orders the writes above before these
+        const uint32_t n0 = ct[3] & 0xffff, n1 = ct[3] >> 16;
+        uint32_t ri[3] = {cv[0], ct[0] + cv[1], ct[0] + ct[1] + cv[2]};   // item offsets
+        uint32_t re[3] = {cv[3] & 0xffff, n0 + (cv[3] >> 16), n0 + n1 + cv[4]};   // ranks
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int k = wcls[i];
+            if (k < 0) continue;
+            const uint32_t rank = k == 0 ? re[0] : k == 1 ? re[1] : re[2];
+            const uint32_t off = k == 0 ? ri[0] : k == 1 ? ri[1] : ri[2];
+            wl.spref[rank] = static_cast<int>(off);
+            wl.wperm[rank] = tid * kPerThread + i;
+            const uint32_t si = static_cast<uint32_t>(items[i] & 0xffffffff);
+            if (k == 0) { ri[0] += si; re[0] += 1; }
+            else if (k == 1) { ri[1] += si; re[1] += 1; }
+            else { ri[2] += si; re[2] += 1; }
+        }
+        wl.n_we = static_cast<int>(n0 + n1 + ct[4]);
+        if (tid == 0) wl.spref[wl.n_we] = static_cast<int>(ct[0] + ct[1] + ct[2]);
+    }
     // Cooperative experts in the order their units are dealt: more rows per
     // cooperative group first (a unit's time grows with its live rows: their
     // x1 loads), ties by expert index.  The cooperative experts are first

@@ -131,6 +131,42 @@ __device__ __forceinline__ void block_scan_u32(uint32_t (&v)[NV], uint32_t (&tot
     __syncthreads();   // s may be reused after return
 }
 
+// As block_scan_u32, with an operator that also takes the value's index n.
+template <int NV, class F>
+__device__ __forceinline__ void block_scan_u32_by(uint32_t (&v)[NV], uint32_t (&total)[NV],
+                                                  uint32_t *s, F op) {
+    const int lane = threadIdx.x & (kWaveSize - 1), wv = threadIdx.x / kWaveSize;
+    uint32_t ex[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        const uint32_t x = wave_incl_scan(v[n], [&](uint32_t a, uint32_t b) { return op(n, a, b); });
+        if (lane == kWaveSize - 1) s[wv * NV + n] = x;
+        ex[n] = dpp_u32<0x138, 0xf, 0xf, true>(x);   // wave_shr:1: lane l - 1's, lane 0 0
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            const uint32_t t = s[i * NV + n];
+            if (i < wv) before = op(n, before, t);
+            all = op(n, all, t);
+        }
+        total[n] = all;
+        v[n] = op(n, before, ex[n]);
+    }
+    __syncthreads();   // s may be reused after return
+}
+
+// value 0 saturating at cap, the others plain sums
+struct TokItemsOp {
+    uint32_t cap;
+    __device__ uint32_t operator()(int n, uint32_t a, uint32_t b) const {
+        return n == 0 ? (a >= cap - b ? cap : a + b) : a + b;
+    }
+};
+
 struct AddU32 {
     __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
 };
@@ -228,20 +264,40 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
         c[i] = static_cast<int>(v);
         csum += c[i];
     }
-    // With invalid lists the raw sum can exceed M many times over: the scan
-    // saturates at M + 1 (every prefix above M is treated alike below).
+    // Both item counts of an expert: wave items low, block items high (each
+    // total stays below 2^31: the host bounds (M/32 + E) * ceil(N/128)).
+    // Wave items in expert order here; with cooperative units of two
+    // fragments they are reordered below.
+    auto item_counts = [&](int cnt) -> int64_t {
+        const int64_t si = cnt >= kMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
+        const int gr = coop_group_rows<WIDE>(cnt);
+        const int64_t li = cnt >= kMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
+        return si | (li << 32);
+    };
+    // One scan for the tokens and both item counts of the counts as read.
+    // The token scan saturates at M + 1 (with invalid lists the raw sum can
+    // exceed M many times over; every prefix above M is treated alike).  For
+    // a valid list (at most M tokens) no count is clamped and the item
+    // prefixes stand; an invalid one is clamped against the token prefix and
+    // its items scanned again.  (One scan less than tokens, then items: c1
+    // -1.4 %, c1_fp4 -1.2 %.)
     const uint32_t cap = static_cast<uint32_t>(p.M) + 1u;
-    uint32_t tok[1] = {static_cast<uint32_t>(csum < cap ? csum : cap)}, tok_total[1];
-    block_scan_u32<1>(tok, tok_total, s32, SatAddU32{cap});
-    const int64_t total_tokens = tok_total[0];
-    int64_t run = tok[0];
-    // Both item counts: wave items low, block items high (each total stays
-    // below 2^31: the host bounds (M/32 + E) * ceil(N/128)).  Wave items in
-    // expert order here; with cooperative units of two fragments they are
-    // reordered below.
-    int64_t isum = 0;
     int64_t items[kPerThread];
+    int64_t isum = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        items[i] = item_counts(c[i]);
+        isum += items[i];
+    }
+    uint32_t v3[3] = {static_cast<uint32_t>(csum < cap ? csum : cap),
+                      static_cast<uint32_t>(isum), static_cast<uint32_t>(isum >> 32)}, t3[3];
+    block_scan_u32_by<3>(v3, t3, s32, TokItemsOp{cap});
+    const int64_t total_tokens = t3[0];
+    int64_t run = v3[0];
     int ccnt[kPerThread];
+    int64_t total_items = static_cast<int64_t>(t3[1]) | (static_cast<int64_t>(t3[2]) << 32);
+    int64_t ipre = static_cast<int64_t>(v3[1]) | (static_cast<int64_t>(v3[2]) << 32);
+    const bool clamp = total_tokens > p.M;   // block-uniform
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
@@ -253,16 +309,19 @@ __device__ __forceinline__ void build_work_list(const FusedParams &p, int n_tile
             wl.cnt[e] = cnt;
         }
         run += c[i];
-        const int64_t si = cnt >= kMinRows ? 0 : ((cnt + kTileM - 1) / kTileM) * n_tiles;
-        const int gr = coop_group_rows<WIDE>(cnt);
-        const int64_t li = cnt >= kMinRows ? ((cnt + gr - 1) / gr) * n_tiles_coop : 0;
-        items[i] = si | (li << 32);
-        isum += items[i];
     }
-    uint32_t iv[2] = {static_cast<uint32_t>(isum), static_cast<uint32_t>(isum >> 32)}, it[2];
-    block_scan_u32<2>(iv, it, s32, AddU32{});
-    const int64_t total_items = static_cast<int64_t>(it[0]) | (static_cast<int64_t>(it[1]) << 32);
-    int64_t ipre = static_cast<int64_t>(iv[0]) | (static_cast<int64_t>(iv[1]) << 32);
+    if (clamp) {
+        isum = 0;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            items[i] = item_counts(ccnt[i]);
+            isum += items[i];
+        }
+        uint32_t iv[2] = {static_cast<uint32_t>(isum), static_cast<uint32_t>(isum >> 32)}, it[2];
+        block_scan_u32<2>(iv, it, s32, AddU32{});
+        total_items = static_cast<int64_t>(it[0]) | (static_cast<int64_t>(it[1]) << 32);
+        ipre = static_cast<int64_t>(iv[0]) | (static_cast<int64_t>(iv[1]) << 32);
+    }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int e = tid * kPerThread + i;
